@@ -1,0 +1,377 @@
+/*
+ * CPU oracle for the quantized MoE grouped-GEMM path.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product library calls, links or
+ * includes this file; only the tests, the smoke check and the bench's CPU
+ * baseline do.  It shares no code with the HIP library.
+ *
+ * What it computes (plain definitions, double precision, no blocking):
+ *
+ *  route    Orbit page, 时刻细节 "Active-expert-chunked dequantization": every
+ *           token activates only the experts its router selects.  Per token:
+ *           order experts by (logit descending, expert id ascending), keep the
+ *           first k; softmax over all E logits in double; renormalise the k
+ *           kept probabilities so they sum to 1.
+ *  permute  Same passage: the selected experts are grouped before the grouped
+ *           GEMM.  Pairs p = t*k + j are listed expert by expert (ascending
+ *           id), ascending p inside an expert (a stable counting sort).
+ *  decode   "超大规模开放权重模型技术解析", 三 微缩放量化的原理: 4-bit elements in
+ *           groups of 32 sharing one scale.  MXFP4: E2M1 value table times
+ *           2^(e8m0 - 127) (code 255 is NaN); INT4: two's-complement nibble
+ *           times its BF16 scale.  Both products are formed in fp32, where
+ *           they are exact unless they overflow.
+ *  project  y[pair][n] = sum over k ascending of x[t][k] * W_e[n][k], double.
+ *  ffn      h = W_gu,e x (rows [0,I) gate, [I,2I) up); a = silu(gate) * up;
+ *           o = W_down,e a; y[t] = sum over j ascending of g[t,j] * o[t,j].
+ *  dx       Orbit page, 时刻细节: the backward for a frozen base forms no weight
+ *           gradient.  dO = g * dY[t]; dA = W_down^T dO; dH = [dA * up *
+ *           silu'(gate) | dA * silu(gate)]; dXp = W_gu^T dH; dX[t] = sum over
+ *           j ascending of dXp[t,j].  Gates are constants.
+ *
+ * Weight layout: packed [E][N][K/2] (element k in byte k>>1, low nibble for
+ * even k), scales [E][N][K/32] (u8 E8M0 for MXFP4, u16 BF16 bits for INT4).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { FMT_MXFP4 = 1, FMT_INT4 = 2 };
+
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+/* ------------------------------------------------------------- scalars */
+
+static float bf16_to_float(uint16_t h) {
+  uint32_t u = (uint32_t)h << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return f;
+}
+
+/* Round-to-nearest-even fp32 -> BF16 bits; NaN stays NaN (quiet). */
+static uint16_t float_to_bf16(float f) {
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  if (isnan(f)) return (uint16_t)((u >> 16) | 0x40u);
+  uint32_t rounding = 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)((u + rounding) >> 16);
+}
+
+void oracle_bf16_view(const float* w, int64_t n, uint16_t* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = float_to_bf16(w[i]);
+}
+
+void oracle_bf16_to_f64(const uint16_t* h, int64_t n, double* out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = (double)bf16_to_float(h[i]);
+}
+
+/* E2M1 values by code: sign bit 3, then the eight magnitudes. */
+static const float kE2M1[16] = {0.0f,  0.5f,  1.0f,  1.5f,  2.0f,  3.0f,  4.0f,  6.0f,
+                                -0.0f, -0.5f, -1.0f, -1.5f, -2.0f, -3.0f, -4.0f, -6.0f};
+
+static float e8m0_value(uint8_t code) {
+  if (code == 255) return NAN;
+  return ldexpf(1.0f, (int)code - 127);
+}
+
+static float decode_one(int fmt, uint8_t nib, const void* scales, int64_t sidx) {
+  if (fmt == FMT_MXFP4) return kE2M1[nib] * e8m0_value(((const uint8_t*)scales)[sidx]);
+  int q = (int)(nib & 0xF);
+  if (q >= 8) q -= 16;
+  return (float)q * bf16_to_float(((const uint16_t*)scales)[sidx]);
+}
+
+/* Decode one expert's [N][K] weights to fp32. */
+int oracle_decode(int fmt, const uint8_t* packed, const void* scales, int64_t N, int64_t K,
+                  float* w) {
+  if ((fmt != FMT_MXFP4 && fmt != FMT_INT4) || K % 32) return 1;
+#pragma omp parallel for schedule(static)
+  for (int64_t n = 0; n < N; ++n) {
+    for (int64_t k = 0; k < K; ++k) {
+      const uint8_t byte = packed[n * (K / 2) + k / 2];
+      const uint8_t nib = (k & 1) ? (byte >> 4) : (byte & 0xF);
+      w[n * K + k] = decode_one(fmt, nib, scales, n * (K / 32) + k / 32);
+    }
+  }
+  return 0;
+}
+
+static int64_t scale_bytes(int fmt) { return fmt == FMT_MXFP4 ? 1 : 2; }
+
+static void expert_ptrs(int fmt, const uint8_t* packed, const void* scales, int64_t N, int64_t K,
+                        int e, const uint8_t** pe, const void** se) {
+  *pe = packed + (int64_t)e * N * (K / 2);
+  *se = (const uint8_t*)scales + (int64_t)e * N * (K / 32) * scale_bytes(fmt);
+}
+
+/* --------------------------------------------------------------- route */
+
+int oracle_route(const float* logits, int T, int E, int k, int32_t* ids, double* gates) {
+  if (T < 0 || E <= 0 || k <= 0 || k > E) return 1;
+  for (int64_t i = 0; i < (int64_t)T * E; ++i)
+    if (!isfinite(logits[i])) return 2;
+  int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+  for (int t = 0; t < T; ++t) {
+    const float* l = logits + (int64_t)t * E;
+    char* taken = (char*)calloc((size_t)E, 1);
+    double* p = (double*)malloc(sizeof(double) * (size_t)E);
+    if (!taken || !p) {
+      bad = 1;
+      free(taken);
+      free(p);
+      continue;
+    }
+    for (int j = 0; j < k; ++j) {
+      int best = -1;
+      for (int e = 0; e < E; ++e) {
+        if (taken[e]) continue;
+        /* strictly greater logit wins; equal logits keep the lower id */
+        if (best < 0 || l[e] > l[best]) best = e;
+      }
+      taken[best] = 1;
+      ids[(int64_t)t * k + j] = best;
+    }
+    double m = -INFINITY;
+    for (int e = 0; e < E; ++e) m = fmax(m, (double)l[e]);
+    double z = 0.0;
+    for (int e = 0; e < E; ++e) {
+      p[e] = exp((double)l[e] - m);
+      z += p[e];
+    }
+    double s = 0.0;
+    for (int j = 0; j < k; ++j) s += p[ids[(int64_t)t * k + j]] / z;
+    for (int j = 0; j < k; ++j) gates[(int64_t)t * k + j] = (p[ids[(int64_t)t * k + j]] / z) / s;
+    free(taken);
+    free(p);
+  }
+  return bad ? 3 : 0;
+}
+
+/* ------------------------------------------------------------- permute */
+
+int oracle_permute(const int32_t* ids, int T, int k, int E, int32_t* counts, int32_t* offsets,
+                   int32_t* perm, int32_t* inv_perm, int32_t* active, int32_t* n_active) {
+  const int64_t P = (int64_t)T * k;
+  for (int64_t p = 0; p < P; ++p)
+    if (ids[p] < 0 || ids[p] >= E) return 1;
+  for (int e = 0; e < E; ++e) counts[e] = 0;
+  for (int64_t p = 0; p < P; ++p) counts[ids[p]]++;
+  offsets[0] = 0;
+  for (int e = 0; e < E; ++e) offsets[e + 1] = offsets[e] + counts[e];
+  int64_t pos = 0;
+  for (int e = 0; e < E; ++e)
+    for (int64_t p = 0; p < P; ++p)
+      if (ids[p] == e) perm[pos++] = (int32_t)p;
+  for (int64_t i = 0; i < P; ++i) inv_perm[perm[i]] = (int32_t)i;
+  int a = 0;
+  for (int e = 0; e < E; ++e)
+    if (counts[e] > 0) active[a++] = e;
+  for (int i = a; i < E; ++i) active[i] = -1;
+  *n_active = a;
+  return 0;
+}
+
+/* ---------------------------------------------------------- projection */
+
+static double dot_f64(const double* a, const float* b, int64_t n) {
+  double s = 0.0;
+  for (int64_t i = 0; i < n; ++i) s += a[i] * (double)b[i];
+  return s;
+}
+
+/* y[i][n] = sum_k x[tok[i]][k] * W_{exp[i]}[n][k] for npairs pairs.
+ * x is BF16 [T][K]; weights [E][N][K] in fmt; y is double [npairs][N]. */
+int oracle_project(int fmt, const uint8_t* packed, const void* scales, int E, int64_t N,
+                   int64_t K, const uint16_t* x, int64_t npairs, const int32_t* tok,
+                   const int32_t* expert, double* y) {
+  float* w = (float*)malloc(sizeof(float) * (size_t)(N * K));
+  double* xr = (double*)malloc(sizeof(double) * (size_t)K);
+  if (!w || !xr) {
+    free(w);
+    free(xr);
+    return 3;
+  }
+  for (int e = 0; e < E; ++e) {
+    int used = 0;
+    for (int64_t i = 0; i < npairs && !used; ++i) used = expert[i] == e;
+    if (!used) continue;
+    const uint8_t* pe;
+    const void* se;
+    expert_ptrs(fmt, packed, scales, N, K, e, &pe, &se);
+    if (oracle_decode(fmt, pe, se, N, K, w)) {
+      free(w);
+      free(xr);
+      return 1;
+    }
+    for (int64_t i = 0; i < npairs; ++i) {
+      if (expert[i] != e) continue;
+      oracle_bf16_to_f64(x + (int64_t)tok[i] * K, K, xr);
+#pragma omp parallel for schedule(static)
+      for (int64_t n = 0; n < N; ++n) y[i * N + n] = dot_f64(xr, w + n * K, K);
+    }
+  }
+  free(w);
+  free(xr);
+  return 0;
+}
+
+/* ----------------------------------------------------------------- FFN */
+
+static double sigmoid(double z) { return 1.0 / (1.0 + exp(-z)); }
+double oracle_silu(double z) { return z * sigmoid(z); }
+double oracle_silu_grad(double z) {
+  const double s = sigmoid(z);
+  return s * (1.0 + z * (1.0 - s));
+}
+
+/* Shared driver: for every selected token and each of its k slots, decode the
+ * slot's expert (once per expert) and evaluate the per-pair quantities.
+ * mode 0: forward  -> o[slot][d] (and h[slot][2I] if h != NULL)
+ * mode 1: backward -> dxp[slot][d] (and dA[slot][I] if da != NULL) */
+static int ffn_pairs(int mode, int fmt, const uint8_t* gu_p, const void* gu_s,
+                     const uint8_t* dn_p, const void* dn_s, int E, int64_t d, int64_t I,
+                     const uint16_t* x, const uint16_t* dy, int k, const int32_t* ids,
+                     const double* gates, int64_t ntok, const int32_t* toks, double* out,
+                     double* h_out, double* da_out) {
+  const int64_t N2 = 2 * I;
+  float* wgu = (float*)malloc(sizeof(float) * (size_t)(N2 * d));
+  float* wdn = (float*)malloc(sizeof(float) * (size_t)(d * I));
+  double* xr = (double*)malloc(sizeof(double) * (size_t)d);
+  double* h = (double*)malloc(sizeof(double) * (size_t)N2);
+  double* a = (double*)malloc(sizeof(double) * (size_t)N2);
+  int rc = 0;
+  if (!wgu || !wdn || !xr || !h || !a) rc = 3;
+  for (int e = 0; e < E && !rc; ++e) {
+    int used = 0;
+    for (int64_t s = 0; s < ntok * k && !used; ++s)
+      used = ids[(int64_t)toks[s / k] * k + s % k] == e;
+    if (!used) continue;
+    const uint8_t* pe;
+    const void* se;
+    expert_ptrs(fmt, gu_p, gu_s, N2, d, e, &pe, &se);
+    rc |= oracle_decode(fmt, pe, se, N2, d, wgu);
+    expert_ptrs(fmt, dn_p, dn_s, d, I, e, &pe, &se);
+    rc |= oracle_decode(fmt, pe, se, d, I, wdn);
+    if (rc) break;
+    for (int64_t s = 0; s < ntok * k; ++s) {
+      const int64_t t = toks[s / k];
+      const int64_t j = s % k;
+      if (ids[t * k + j] != e) continue;
+      oracle_bf16_to_f64(x + t * d, d, xr);
+      /* h = W_gu x */
+#pragma omp parallel for schedule(static)
+      for (int64_t r = 0; r < N2; ++r) h[r] = dot_f64(xr, wgu + r * d, d);
+      if (h_out) memcpy(h_out + s * N2, h, sizeof(double) * (size_t)N2);
+      double* o = out + s * d;
+      if (mode == 0) {
+        for (int64_t i = 0; i < I; ++i) a[i] = oracle_silu(h[i]) * h[I + i];
+        /* o = W_down a */
+#pragma omp parallel for schedule(static)
+        for (int64_t n = 0; n < d; ++n) {
+          double acc = 0.0;
+          for (int64_t i = 0; i < I; ++i) acc += (double)wdn[n * I + i] * a[i];
+          o[n] = acc;
+        }
+      } else {
+        const double g = gates[t * k + j];
+        double* dO = (double*)malloc(sizeof(double) * (size_t)d);
+        double* dA = (double*)malloc(sizeof(double) * (size_t)I);
+        if (!dO || !dA) {
+          free(dO);
+          free(dA);
+          rc = 3;
+          break;
+        }
+        for (int64_t n = 0; n < d; ++n) dO[n] = g * (double)bf16_to_float(dy[t * d + n]);
+        /* dA = W_down^T dO */
+#pragma omp parallel for schedule(static)
+        for (int64_t i = 0; i < I; ++i) {
+          double acc = 0.0;
+          for (int64_t n = 0; n < d; ++n) acc += dO[n] * (double)wdn[n * I + i];
+          dA[i] = acc;
+        }
+        if (da_out) memcpy(da_out + s * I, dA, sizeof(double) * (size_t)I);
+        /* dH = [dA * up * silu'(gate) | dA * silu(gate)] */
+        for (int64_t i = 0; i < I; ++i) {
+          a[i] = dA[i] * h[I + i] * oracle_silu_grad(h[i]);
+          a[I + i] = dA[i] * oracle_silu(h[i]);
+        }
+        /* dXp = W_gu^T dH */
+#pragma omp parallel for schedule(static)
+        for (int64_t c = 0; c < d; ++c) {
+          double acc = 0.0;
+          for (int64_t r = 0; r < N2; ++r) acc += a[r] * (double)wgu[r * d + c];
+          o[c] = acc;
+        }
+        free(dO);
+        free(dA);
+      }
+    }
+  }
+  free(wgu);
+  free(wdn);
+  free(xr);
+  free(h);
+  free(a);
+  return rc;
+}
+
+/* y[s][n] for the selected tokens toks[0..ntok): sum over j ascending of
+ * g[t,j] * o[t,j][n].  h_out (nullable) receives h per (token, slot):
+ * [ntok*k][2I]. */
+int oracle_ffn(int fmt, const uint8_t* gu_p, const void* gu_s, const uint8_t* dn_p,
+               const void* dn_s, int E, int64_t d, int64_t I, const uint16_t* x, int k,
+               const int32_t* ids, const double* gates, int64_t ntok, const int32_t* toks,
+               double* y, double* h_out) {
+  double* o = (double*)malloc(sizeof(double) * (size_t)(ntok * k * d));
+  if (!o) return 3;
+  int rc = ffn_pairs(0, fmt, gu_p, gu_s, dn_p, dn_s, E, d, I, x, NULL, k, ids, gates, ntok, toks,
+                     o, h_out, NULL);
+  if (!rc) {
+    for (int64_t s = 0; s < ntok; ++s) {
+      const int64_t t = toks[s];
+      for (int64_t n = 0; n < d; ++n) {
+        double acc = 0.0;
+        for (int j = 0; j < k; ++j) acc += gates[t * k + j] * o[(s * k + j) * d + n];
+        y[s * d + n] = acc;
+      }
+    }
+  }
+  free(o);
+  return rc;
+}
+
+/* dX[s][c] for the selected tokens: sum over j ascending of dXp[t,j][c].
+ * da_out (nullable) receives dA per (token, slot): [ntok*k][I]. */
+int oracle_dx(int fmt, const uint8_t* gu_p, const void* gu_s, const uint8_t* dn_p,
+              const void* dn_s, int E, int64_t d, int64_t I, const uint16_t* x,
+              const uint16_t* dy, int k, const int32_t* ids, const double* gates, int64_t ntok,
+              const int32_t* toks, double* dx, double* da_out) {
+  double* dxp = (double*)malloc(sizeof(double) * (size_t)(ntok * k * d));
+  if (!dxp) return 3;
+  int rc = ffn_pairs(1, fmt, gu_p, gu_s, dn_p, dn_s, E, d, I, x, dy, k, ids, gates, ntok, toks,
+                     dxp, NULL, da_out);
+  if (!rc) {
+    for (int64_t s = 0; s < ntok; ++s) {
+      for (int64_t c = 0; c < d; ++c) {
+        double acc = 0.0;
+        for (int j = 0; j < k; ++j) acc += dxp[(s * k + j) * d + c];
+        dx[s * d + c] = acc;
+      }
+    }
+  }
+  free(dxp);
+  return rc;
+}
