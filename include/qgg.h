@@ -1,0 +1,178 @@
+/*
+ * qgg.h -- C-ABI of the MI355X (gfx950) quantized MoE grouped-GEMM library.
+ *
+ * The path (Orbit page, section 时刻细节, "Active-expert-chunked
+ * dequantization"): every token activates only the experts its router picks;
+ * the picked experts are grouped into fixed-size chunks, each chunk's 4-bit
+ * weights are dequantized to BF16 only while the chunk is being computed, the
+ * expert projections run as one grouped matrix multiplication, and the
+ * high-precision copy is released before the next chunk.  The base stays
+ * frozen in its low-precision format (same page, 单节点 Kimi-K2.6 驱散: INT4;
+ * 单节点 DeepSeek V4 Flash 驱散: FP4).  The backward computes no gradient for the
+ * frozen base (时刻细节, bypass-base-weight-grad GEMM backward).
+ *
+ * Weight formats (page "超大规模开放权重模型技术解析", 三 微缩放量化的原理:
+ * groups of 32 elements share one scale):
+ *   QGG_FMT_MXFP4  E2M1 nibbles, one E8M0 exponent byte per 32 elements along K
+ *   QGG_FMT_INT4   two's-complement nibbles, one BF16 scale per 32 along K
+ *
+ * Conventions for every call
+ *  - Pointers are DEVICE memory owned by the caller unless marked "host".
+ *    The library never allocates device memory: scratch and intermediates
+ *    come from the caller's `workspace`, sized by qgg_workspace_bytes().
+ *  - BF16 tensors are passed as uint16_t bit patterns.  Row-major throughout.
+ *  - Calls are asynchronous on `stream` (a hipStream_t; 0 = null stream).
+ *    Exception: variant QGG_CHUNKED reads the active-expert count and the
+ *    per-chunk tile table back to the host once per call and waits for it.
+ *  - Argument errors are detected on the host before any launch and returned
+ *    as a status; nothing aborts.  Data errors found on the device (a
+ *    non-finite router logit, an expert id outside [0, E)) set *err_flag to a
+ *    nonzero value when err_flag is not NULL; the caller zeroes it first.
+ *  - Limits: 1 <= k <= 32, k <= E <= 1024, T*k < 2^31, K % 128 == 0,
+ *    N % 64 == 0 (inter % 64 == 0 for the FFN calls).
+ *  - Pair index p = t*k + j names token t's j-th routed expert.  "Sorted
+ *    order" lists pairs expert by expert (ascending id), ascending p inside an
+ *    expert; row i of a sorted tensor belongs to pair perm[i].
+ */
+#ifndef QGG_H_
+#define QGG_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* qgg_stream_t; /* same type as hipStream_t */
+typedef int qgg_status;
+
+#define QGG_OK 0
+#define QGG_ERR_INVALID_ARG 1
+#define QGG_ERR_UNSUPPORTED 2
+#define QGG_ERR_WORKSPACE_TOO_SMALL 3
+#define QGG_ERR_HIP 4
+
+#define QGG_FMT_MXFP4 1
+#define QGG_FMT_INT4 2
+
+/* variant: CHUNKED dequantizes one chunk of active experts into BF16 scratch
+ * and runs a BF16 grouped GEMM over it (the pages' formulation); FUSED decodes
+ * nibbles and scales in registers and feeds BF16 MFMA directly (no scratch). */
+#define QGG_CHUNKED 0
+#define QGG_FUSED 1
+
+/* dequant_grouped_gemm flags */
+#define QGG_A_SORTED 0        /* a is [P][K] already in sorted order          */
+#define QGG_A_TOKENS 1        /* a is [T][K]; sorted row i reads a[perm[i]/k] */
+#define QGG_TRANSPOSE_W 2     /* y = a . W (reduce over N; a is [.][N], y [P][K]) */
+#define QGG_DEQUANT_ONLY 4    /* CHUNKED only: write the first chunk's BF16
+                                 weights [chunk][N][K] to the start of the
+                                 workspace and stop (a test hook)            */
+
+/* workspace queries */
+#define QGG_CALL_PERMUTE 1
+#define QGG_CALL_GEMM 2
+#define QGG_CALL_FFN_FWD 3
+#define QGG_CALL_DX_BWD 4
+
+/* A frozen 4-bit weight tensor of E experts, each [N][K] (out x in).
+ * packed: [E][N][K/2] bytes; element k of a row is byte k>>1, low nibble for
+ *         even k.  scales: [E][N][K/32], uint8 E8M0 codes (value 2^(c-127),
+ *         255 = NaN) for MXFP4, uint16 BF16 bits for INT4.  Host struct,
+ *         device pointers, read only. */
+typedef struct {
+  int32_t fmt;
+  int32_t E, N, K;
+  const uint8_t* packed;
+  const void* scales;
+} qgg_qweight;
+
+/* Routing permutation, all device arrays written by expert_permute.
+ * counts[E]      pairs routed to each expert
+ * offsets[E+1]   exclusive prefix sum of counts
+ * perm[P]        sorted row -> pair index
+ * inv_perm[P]    pair index -> sorted row
+ * active[E]      ids of experts with counts > 0, ascending; rest are -1
+ * n_active[1]    number of active experts */
+typedef struct {
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* perm;
+  int32_t* inv_perm;
+  int32_t* active;
+  int32_t* n_active;
+} qgg_perm;
+
+/* moe_route -- per token, top-k experts of fp32 router logits [T][E] under the
+ * key (logit descending, expert id ascending), with gates = softmax over all E
+ * renormalised over the k kept experts (equivalently, softmax over the kept
+ * logits).  Orbit page, 时刻细节: tokens activate only router-selected experts.
+ * Outputs topk_ids [T][k] int32 (slot order = key order) and topk_gates
+ * [T][k] fp32 summing to 1 per token.  A non-finite logit sets *err_flag. */
+qgg_status moe_route(const float* logits, int T, int E, int k, int32_t* topk_ids,
+                     float* topk_gates, int32_t* err_flag, qgg_stream_t stream);
+
+/* expert_permute -- group the T*k (token, expert) pairs by expert: a stable
+ * counting sort built from wavefront prefix sums (same passage: the selected
+ * experts are grouped into batches before the grouped GEMM).  Fills every
+ * array of *p (a host struct of device pointers).  If x and x_perm are both
+ * non-NULL it also gathers x_perm[i][:] = x[perm[i]/k][:] (BF16, d columns).
+ * Expert ids outside [0, E) set *err_flag and are dropped from the sort.
+ * workspace: qgg_workspace_bytes(QGG_CALL_PERMUTE, ...) bytes. */
+qgg_status expert_permute(const int32_t* topk_ids, int T, int k, int E, const qgg_perm* p,
+                          const uint16_t* x, int d, uint16_t* x_perm, int32_t* err_flag,
+                          void* workspace, size_t ws_bytes, qgg_stream_t stream);
+
+/* dequant_grouped_gemm -- one grouped projection over the routed rows:
+ * y[i][:] = a_row(i) . W_e^T for every sorted row i of expert e (fp32
+ * accumulate, BF16 out), y is [P][N] in sorted order.  With QGG_TRANSPOSE_W
+ * the product is a_row(i) . W_e (a is [.][N], y is [P][K]).  variant and
+ * chunk (experts per chunk, 0 = all active) as above; chunking never changes
+ * the result.  p must come from expert_permute on the same routing. */
+qgg_status dequant_grouped_gemm(const qgg_qweight* w, const uint16_t* a, int flags,
+                                const qgg_perm* p, int T, int k, int variant, int chunk,
+                                void* workspace, size_t ws_bytes, uint16_t* y,
+                                qgg_stream_t stream);
+
+/* moe_ffn_fwd -- the SwiGLU expert FFN for a routed batch: route, permute,
+ * h = x . W_gu^T (rows [0,inter) of W_gu are gate, [inter, 2*inter) up),
+ * a = silu(gate) * up, o = a . W_down^T, y[t] = sum_j g[t,j] * o[pair(t,j)]
+ * (fp32 sum in ascending j).  w_gate_up: N = 2*inter, K = d; w_down: N = d,
+ * K = inter.  Writes topk_ids/topk_gates [T][k], the arrays of *p, y [T][d];
+ * if h_save is not NULL also h [P][2*inter] BF16 in sorted order (needed by
+ * moe_dx_bwd). */
+qgg_status moe_ffn_fwd(const qgg_qweight* w_gate_up, const qgg_qweight* w_down,
+                       const uint16_t* x, const float* logits, int T, int d, int E, int k,
+                       int inter, int variant, int chunk, int32_t* topk_ids, float* topk_gates,
+                       const qgg_perm* p, uint16_t* h_save, int32_t* err_flag, void* workspace,
+                       size_t ws_bytes, uint16_t* y, qgg_stream_t stream);
+
+/* moe_dx_bwd -- input gradient of moe_ffn_fwd with the base frozen: no
+ * weight gradient and no gate gradient (gates are constants).
+ * dA = (g * dY[t]) . W_down, dH = [dA * up * silu'(gate) | dA * silu(gate)]
+ * using h_saved from the forward, dXp = dH . W_gu, dx[t] = sum_j dXp[pair(t,j)]
+ * (fp32 sum in ascending j).  dy, dx [T][d] BF16; topk_gates [T][k]. */
+qgg_status moe_dx_bwd(const qgg_qweight* w_gate_up, const qgg_qweight* w_down,
+                      const uint16_t* dy, const float* topk_gates, const qgg_perm* p,
+                      const uint16_t* h_saved, int T, int d, int E, int k, int inter, int variant,
+                      int chunk, void* workspace, size_t ws_bytes, uint16_t* dx,
+                      qgg_stream_t stream);
+
+/* Workspace bytes a call needs.  N_or_inter is N for QGG_CALL_GEMM (with K =
+ * d) and inter for the FFN calls.  *scratch_bytes (nullable) receives the part
+ * that holds dequantized BF16 weights (0 for QGG_FUSED): chunk * max(N*K) * 2. */
+size_t qgg_workspace_bytes(int call, int T, int d, int E, int k, int N_or_inter, int variant,
+                           int chunk, size_t* scratch_bytes);
+
+/* Human-readable name of a status code (static storage). */
+const char* qgg_status_string(qgg_status s);
+
+/* Library version string (static storage). */
+const char* qgg_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QGG_H_ */

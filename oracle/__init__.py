@@ -51,6 +51,7 @@ def _L():
         lib.oracle_bf16_view.argtypes = [P, i64, P]
         lib.oracle_bf16_to_f64.argtypes = [P, i64, P]
         lib.oracle_project.argtypes = [i32, P, P, i32, i64, i64, P, i64, P, P, P]
+        lib.oracle_project_t.argtypes = [i32, P, P, i32, i64, i64, P, i64, P, P]
         lib.oracle_ffn.argtypes = [i32, P, P, P, P, i32, i64, i64, P, i32, P, P, i64, P, P, P]
         lib.oracle_dx.argtypes = [i32, P, P, P, P, i32, i64, i64, P, P, i32, P, P, i64, P, P, P]
         lib.oracle_silu.argtypes = [ctypes.c_double]
@@ -134,6 +135,17 @@ def project(fmt, packed, scales, x, tok, expert) -> np.ndarray:
     y = np.zeros((tok.size, N), np.float64)
     _check(_L().oracle_project(fmt, _p(packed), _p(scales), E, N, 2 * K2, _p(x), tok.size,
                                _p(tok), _p(expert), _p(y)), "project")
+    return y
+
+
+def project_t(fmt, packed, scales, a, expert) -> np.ndarray:
+    """double y [npairs][K] = a[i] . W_{expert[i]} (a is BF16 [npairs][N])."""
+    E, N, K2 = packed.shape
+    a = np.ascontiguousarray(a, np.uint16)
+    expert = np.ascontiguousarray(expert, np.int32)
+    y = np.zeros((expert.size, 2 * K2), np.float64)
+    _check(_L().oracle_project_t(fmt, _p(packed), _p(scales), E, N, 2 * K2, _p(a), expert.size,
+                                 _p(expert), _p(y)), "project_t")
     return y
 
 

@@ -20,7 +20,8 @@
  *           2^(e8m0 - 127) (code 255 is NaN); INT4: two's-complement nibble
  *           times its BF16 scale.  Both products are formed in fp32, where
  *           they are exact unless they overflow.
- *  project  y[pair][n] = sum over k ascending of x[t][k] * W_e[n][k], double.
+ *  project  y[pair][n] = sum over k ascending of x[t][k] * W_e[n][k], double;
+ *           the transposed form sums over W's rows: y[i][c] = sum_n a[i][n] W_e[n][c].
  *  ffn      h = W_gu,e x (rows [0,I) gate, [I,2I) up); a = silu(gate) * up;
  *           o = W_down,e a; y[t] = sum over j ascending of g[t,j] * o[t,j].
  *  dx       Orbit page, 时刻细节: the backward for a frozen base forms no weight
@@ -224,6 +225,47 @@ int oracle_project(int fmt, const uint8_t* packed, const void* scales, int E, in
   }
   free(w);
   free(xr);
+  return 0;
+}
+
+/* Transposed access, as the input-gradient backward reads the frozen base:
+ * y[i][c] = sum over n ascending of a[i][n] * W_{expert[i]}[n][c].  a is BF16
+ * [npairs][N] (one row per pair), y is double [npairs][K]. */
+int oracle_project_t(int fmt, const uint8_t* packed, const void* scales, int E, int64_t N,
+                     int64_t K, const uint16_t* a, int64_t npairs, const int32_t* expert,
+                     double* y) {
+  float* w = (float*)malloc(sizeof(float) * (size_t)(N * K));
+  double* ar = (double*)malloc(sizeof(double) * (size_t)N);
+  if (!w || !ar) {
+    free(w);
+    free(ar);
+    return 3;
+  }
+  for (int e = 0; e < E; ++e) {
+    int used = 0;
+    for (int64_t i = 0; i < npairs && !used; ++i) used = expert[i] == e;
+    if (!used) continue;
+    const uint8_t* pe;
+    const void* se;
+    expert_ptrs(fmt, packed, scales, N, K, e, &pe, &se);
+    if (oracle_decode(fmt, pe, se, N, K, w)) {
+      free(w);
+      free(ar);
+      return 1;
+    }
+    for (int64_t i = 0; i < npairs; ++i) {
+      if (expert[i] != e) continue;
+      oracle_bf16_to_f64(a + i * N, N, ar);
+#pragma omp parallel for schedule(static)
+      for (int64_t c = 0; c < K; ++c) {
+        double acc = 0.0;
+        for (int64_t n = 0; n < N; ++n) acc += ar[n] * (double)w[n * K + c];
+        y[i * K + c] = acc;
+      }
+    }
+  }
+  free(w);
+  free(ar);
   return 0;
 }
 

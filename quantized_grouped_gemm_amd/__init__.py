@@ -1,0 +1,268 @@
+"""Python binding of ``libqgg.so``, the gfx950 quantized MoE grouped-GEMM library.
+
+Argument marshalling only: every step of the path runs in the library's HIP
+kernels, which this module reaches through ctypes with raw device pointers and
+the current HIP stream.  PyTorch supplies device memory and streams.  If the
+library is not built, every call raises; there is no fallback.
+
+Names follow the C-ABI in ``include/qgg.h``: ``moe_route``, ``expert_permute``,
+``dequant_grouped_gemm``, ``moe_ffn_fwd``, ``moe_dx_bwd``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+from . import accounting  # noqa: F401  (host-side byte/FLOP accounting)
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqgg.so")
+
+FMT_MXFP4 = 1
+FMT_INT4 = 2
+CHUNKED = 0
+FUSED = 1
+A_SORTED = 0
+A_TOKENS = 1
+TRANSPOSE_W = 2
+DEQUANT_ONLY = 4
+CALL_PERMUTE = 1
+CALL_GEMM = 2
+CALL_FFN_FWD = 3
+CALL_DX_BWD = 4
+
+STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too small", 4: "HIP error"}
+
+# Every symbol include/qgg.h declares.
+EXPORTS = ("moe_route", "expert_permute", "dequant_grouped_gemm", "moe_ffn_fwd", "moe_dx_bwd",
+           "qgg_workspace_bytes", "qgg_status_string", "qgg_version")
+
+_lib = None
+
+
+class QggError(RuntimeError):
+    pass
+
+
+class _QWeight(ctypes.Structure):
+    _fields_ = [("fmt", ctypes.c_int32), ("E", ctypes.c_int32), ("N", ctypes.c_int32),
+                ("K", ctypes.c_int32), ("packed", ctypes.c_void_p), ("scales", ctypes.c_void_p)]
+
+
+class _Perm(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("counts", "offsets", "perm", "inv_perm", "active", "n_active")]
+
+
+def lib():
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise QggError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m quantized_grouped_gemm_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, i32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+        L.moe_route.argtypes = [P, i32, i32, i32, P, P, P, P]
+        L.expert_permute.argtypes = [P, i32, i32, i32, ctypes.POINTER(_Perm), P, i32, P, P, P, sz, P]
+        L.dequant_grouped_gemm.argtypes = [ctypes.POINTER(_QWeight), P, i32, ctypes.POINTER(_Perm),
+                                           i32, i32, i32, i32, P, sz, P, P]
+        L.moe_ffn_fwd.argtypes = [ctypes.POINTER(_QWeight), ctypes.POINTER(_QWeight), P, P, i32,
+                                  i32, i32, i32, i32, i32, i32, P, P, ctypes.POINTER(_Perm), P, P,
+                                  P, sz, P, P]
+        L.moe_dx_bwd.argtypes = [ctypes.POINTER(_QWeight), ctypes.POINTER(_QWeight), P, P,
+                                 ctypes.POINTER(_Perm), P, i32, i32, i32, i32, i32, i32, i32, P,
+                                 sz, P, P]
+        L.qgg_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32,
+                                          ctypes.POINTER(ctypes.c_size_t)]
+        L.qgg_workspace_bytes.restype = ctypes.c_size_t
+        L.qgg_status_string.argtypes = [i32]
+        L.qgg_status_string.restype = ctypes.c_char_p
+        L.qgg_version.restype = ctypes.c_char_p
+        for f in ("moe_route", "expert_permute", "dequant_grouped_gemm", "moe_ffn_fwd",
+                  "moe_dx_bwd"):
+            getattr(L, f).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        raise QggError(f"{what}: {lib().qgg_status_string(rc).decode()} ({rc})")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+@dataclass
+class QWeight:
+    """Frozen 4-bit expert weights on the device: packed [E][N][K/2] uint8 and
+    scales [E][N][K/32] (uint8 E8M0 for MXFP4, BF16 bits for INT4)."""
+    fmt: int
+    packed: "object"
+    scales: "object"
+
+    @property
+    def E(self):
+        return self.packed.shape[0]
+
+    @property
+    def N(self):
+        return self.packed.shape[1]
+
+    @property
+    def K(self):
+        return self.packed.shape[2] * 2
+
+    def c(self):
+        return _QWeight(self.fmt, self.E, self.N, self.K, self.packed.data_ptr(),
+                        self.scales.data_ptr())
+
+
+@dataclass
+class Perm:
+    """Routing permutation (device int32 tensors), see ``qgg_perm``."""
+    counts: "object"
+    offsets: "object"
+    perm: "object"
+    inv_perm: "object"
+    active: "object"
+    n_active: "object"
+
+    @staticmethod
+    def empty(P: int, E: int, device):
+        import torch
+        z = lambda n: torch.empty(max(n, 1), dtype=torch.int32, device=device)  # noqa: E731
+        return Perm(z(E), z(E + 1), z(P), z(P), z(E), z(1))
+
+    def c(self):
+        return _Perm(*(t.data_ptr() for t in (self.counts, self.offsets, self.perm,
+                                               self.inv_perm, self.active, self.n_active)))
+
+
+def workspace_bytes(call: int, T: int, d: int, E: int, k: int, n_or_inter: int, variant: int,
+                    chunk: int):
+    """(total workspace bytes, dequant scratch bytes) for a call."""
+    s = ctypes.c_size_t(0)
+    total = lib().qgg_workspace_bytes(call, T, d, E, k, n_or_inter, variant, chunk,
+                                      ctypes.byref(s))
+    return int(total), int(s.value)
+
+
+class Workspace:
+    """A reusable device byte buffer that grows on demand."""
+
+    def __init__(self):
+        self.buf = None
+
+    def get(self, nbytes: int, device):
+        import torch
+        if self.buf is None or self.buf.numel() < nbytes or self.buf.device != device:
+            self.buf = None
+            self.buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+        return self.buf
+
+
+_default_ws = Workspace()
+
+
+def moe_route(logits, k: int, err_flag=None):
+    """(topk_ids int32 [T,k], topk_gates fp32 [T,k]) for fp32 logits [T,E]."""
+    import torch
+    T, E = logits.shape
+    ids = torch.empty((T, k), dtype=torch.int32, device=logits.device)
+    gates = torch.empty((T, k), dtype=torch.float32, device=logits.device)
+    _check(lib().moe_route(_ptr(logits), T, E, k, _ptr(ids), _ptr(gates), _ptr(err_flag),
+                           _stream()), "moe_route")
+    return ids, gates
+
+
+def expert_permute(topk_ids, E: int, x=None, err_flag=None, ws: Workspace | None = None):
+    """Perm for int32 ids [T,k]; with x [T,d] BF16 also returns x_perm [P,d]."""
+    import torch
+    T, k = topk_ids.shape
+    dev = topk_ids.device
+    p = Perm.empty(T * k, E, dev)
+    x_perm = None
+    d = 0
+    if x is not None:
+        d = x.shape[1]
+        x_perm = torch.empty((T * k, d), dtype=x.dtype, device=dev)
+    nb, _ = workspace_bytes(CALL_PERMUTE, T, 128, E, k, 64, FUSED, 0)
+    buf = (ws or _default_ws).get(nb, dev)
+    pc = p.c()
+    _check(lib().expert_permute(_ptr(topk_ids), T, k, E, ctypes.byref(pc), _ptr(x), d,
+                                _ptr(x_perm), _ptr(err_flag), _ptr(buf), buf.numel(), _stream()),
+           "expert_permute")
+    return p, x_perm
+
+
+def dequant_grouped_gemm(w: QWeight, a, perm: Perm, T: int, k: int, variant: int = FUSED,
+                         chunk: int = 0, flags: int = A_TOKENS, ws: Workspace | None = None,
+                         out=None):
+    """y [P, N] (or [P, K] with TRANSPOSE_W) in sorted order, BF16."""
+    import torch
+    dev = w.packed.device
+    P = T * k
+    trans = bool(flags & TRANSPOSE_W)
+    ncols = w.K if trans else w.N
+    if flags & DEQUANT_ONLY:
+        y = None
+    else:
+        y = out if out is not None else torch.empty((P, ncols), dtype=torch.bfloat16, device=dev)
+    nb, _ = workspace_bytes(CALL_GEMM, T, w.K, w.E, k, w.N, variant, chunk)
+    buf = (ws or _default_ws).get(nb, dev)
+    wc, pc = w.c(), perm.c()
+    _check(lib().dequant_grouped_gemm(ctypes.byref(wc), _ptr(a), flags, ctypes.byref(pc), T, k,
+                                      variant, chunk, _ptr(buf), buf.numel(), _ptr(y), _stream()),
+           "dequant_grouped_gemm")
+    return y if y is not None else buf
+
+
+def moe_ffn_fwd(w_gate_up: QWeight, w_down: QWeight, x, logits, k: int, variant: int = FUSED,
+                chunk: int = 0, save_h: bool = False, err_flag=None, ws: Workspace | None = None):
+    """dict(y [T,d], topk_ids, topk_gates, perm, h [P,2I] or None)."""
+    import torch
+    T, d = x.shape
+    E = w_gate_up.E
+    inter = w_gate_up.N // 2
+    dev = x.device
+    P = T * k
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    gates = torch.empty((T, k), dtype=torch.float32, device=dev)
+    p = Perm.empty(P, E, dev)
+    h = torch.empty((P, 2 * inter), dtype=torch.bfloat16, device=dev) if save_h else None
+    y = torch.empty((T, d), dtype=torch.bfloat16, device=dev)
+    nb, _ = workspace_bytes(CALL_FFN_FWD, T, d, E, k, inter, variant, chunk)
+    buf = (ws or _default_ws).get(nb, dev)
+    g, dn, pc = w_gate_up.c(), w_down.c(), p.c()
+    _check(lib().moe_ffn_fwd(ctypes.byref(g), ctypes.byref(dn), _ptr(x), _ptr(logits), T, d, E, k,
+                             inter, variant, chunk, _ptr(ids), _ptr(gates), ctypes.byref(pc),
+                             _ptr(h), _ptr(err_flag), _ptr(buf), buf.numel(), _ptr(y), _stream()),
+           "moe_ffn_fwd")
+    return dict(y=y, topk_ids=ids, topk_gates=gates, perm=p, h=h)
+
+
+def moe_dx_bwd(w_gate_up: QWeight, w_down: QWeight, dy, topk_gates, perm: Perm, h_saved, k: int,
+               variant: int = FUSED, chunk: int = 0, ws: Workspace | None = None):
+    """dx [T,d] BF16: the input gradient through the frozen base."""
+    import torch
+    T, d = dy.shape
+    E = w_gate_up.E
+    inter = w_gate_up.N // 2
+    dev = dy.device
+    dx = torch.empty((T, d), dtype=torch.bfloat16, device=dev)
+    nb, _ = workspace_bytes(CALL_DX_BWD, T, d, E, k, inter, variant, chunk)
+    buf = (ws or _default_ws).get(nb, dev)
+    g, dn, pc = w_gate_up.c(), w_down.c(), perm.c()
+    _check(lib().moe_dx_bwd(ctypes.byref(g), ctypes.byref(dn), _ptr(dy), _ptr(topk_gates),
+                            ctypes.byref(pc), _ptr(h_saved), T, d, E, k, inter, variant, chunk,
+                            _ptr(buf), buf.numel(), _ptr(dx), _stream()), "moe_dx_bwd")
+    return dx

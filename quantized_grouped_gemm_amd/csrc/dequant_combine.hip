@@ -1,0 +1,125 @@
+// Chunk dequantization (the chunked variant's scratch fill) and the
+// gate-weighted combine / scatter-sum back to token order.
+//
+// Orbit page, section 时刻细节 ("Active-expert-chunked dequantization"): a
+// chunk of router-selected experts is dequantized temporarily and the
+// high-precision copy is released after the grouped GEMM; here "release" is
+// the next chunk overwriting the same scratch in stream order.  Group-32
+// decoding: "超大规模开放权重模型技术解析", 三 微缩放量化的原理.
+#include "qgg_device.hpp"
+#include "qgg_internal.hpp"
+
+namespace qgg {
+
+namespace {
+
+// fp32 value of each E2M1 code (sign bit 3).
+__constant__ float kE2M1Val[16] = {0.0f,  0.5f,  1.0f,  1.5f,  2.0f,  3.0f,  4.0f,  6.0f,
+                                   -0.0f, -0.5f, -1.0f, -1.5f, -2.0f, -3.0f, -4.0f, -6.0f};
+
+// One thread per 32-element group: 16 packed bytes + 1 scale -> 64 bytes of
+// BF16.  The product code value x scale is formed in fp32 (exact unless it
+// overflows) and rounded to BF16 to nearest even; an E8M0 code of 255 (NaN)
+// yields the quiet NaN 0x7FC0 for the whole group.
+template <int FMT>
+__global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ packed,
+                                                 const void* __restrict__ scales, int N, int K,
+                                                 const int32_t* __restrict__ active,
+                                                 const int32_t* __restrict__ n_active, int first,
+                                                 int count, uint16_t* __restrict__ dst) {
+  const int64_t groups_per_expert = (int64_t)N * (K / 32);
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int slot = (int)(gid / groups_per_expert);
+  if (slot >= count) return;
+  const int a = first + slot;
+  if (a >= *n_active) return;
+  const int64_t e = active[a];
+  const int64_t gi = gid % groups_per_expert;  // n * (K/32) + group
+  const u32x4_t w = reinterpret_cast<const u32x4_t*>(packed + e * groups_per_expert * 16)[gi];
+  uint32_t out[16];
+  if constexpr (FMT == 1) {
+    const uint32_t code = static_cast<const uint8_t*>(scales)[e * groups_per_expert + gi];
+    const float s = e8m0_to_f32(code);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t byte = (w[i >> 2] >> (8 * (i & 3))) & 0xFFu;
+      uint32_t lo = f32_to_bf16_rne(kE2M1Val[byte & 15] * s);
+      uint32_t hi = f32_to_bf16_rne(kE2M1Val[byte >> 4] * s);
+      if (code == 255) lo = hi = 0x7FC0u;
+      out[i] = lo | (hi << 16);
+    }
+  } else {
+    const float s = bf16_to_f32(static_cast<const uint16_t*>(scales)[e * groups_per_expert + gi]);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const uint32_t byte = (w[i >> 2] >> (8 * (i & 3))) & 0xFFu;
+      const int q0 = (int)(byte & 15u) - ((byte & 8u) ? 16 : 0);
+      const int q1 = (int)(byte >> 4) - ((byte & 128u) ? 16 : 0);
+      out[i] = f32_to_bf16_rne((float)q0 * s) | (f32_to_bf16_rne((float)q1 * s) << 16);
+    }
+  }
+  u32x4_t* o = reinterpret_cast<u32x4_t*>(dst + ((int64_t)slot * groups_per_expert + gi) * 32);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    u32x4_t v = {out[4 * i], out[4 * i + 1], out[4 * i + 2], out[4 * i + 3]};
+    o[i] = v;
+  }
+}
+
+// out[t][:] = sum over j ascending of w_j * rows[inv_perm[t*k+j]][:], fp32
+// accumulation, BF16 out.  One workgroup per token, 8 columns per thread step.
+__global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ rows, int d,
+                                                 const int32_t* __restrict__ inv_perm,
+                                                 const float* __restrict__ gates, int k,
+                                                 uint16_t* __restrict__ out) {
+  const int64_t t = blockIdx.x;
+  int32_t src[32];
+  float w[32];
+  for (int j = 0; j < k; ++j) {
+    src[j] = inv_perm[t * k + j];
+    w[j] = gates ? gates[t * k + j] : 1.0f;
+  }
+  for (int c = threadIdx.x; c < d / 8; c += blockDim.x) {
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+    for (int j = 0; j < k; ++j) {
+      if (src[j] < 0) continue;
+      const u32x4_t v = reinterpret_cast<const u32x4_t*>(rows + (int64_t)src[j] * d)[c];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[2 * i] = __builtin_fmaf(w[j], bf16_to_f32(v[i] & 0xFFFFu), acc[2 * i]);
+        acc[2 * i + 1] = __builtin_fmaf(w[j], bf16_to_f32(v[i] >> 16), acc[2 * i + 1]);
+      }
+    }
+    u32x4_t o = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                 pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])};
+    reinterpret_cast<u32x4_t*>(out + t * d)[c] = o;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_dequant(int fmt, const uint8_t* packed, const void* scales, int N, int K,
+                          const int32_t* active, const int32_t* n_active, int first, int count,
+                          uint16_t* dst, hipStream_t s) {
+  const int64_t groups = (int64_t)count * N * (K / 32);
+  if (groups <= 0) return hipSuccess;
+  const dim3 grid((unsigned)((groups + 255) / 256));
+  if (fmt == 1)
+    hipLaunchKernelGGL(k_dequant<1>, grid, dim3(256), 0, s, packed, scales, N, K, active,
+                       n_active, first, count, dst);
+  else
+    hipLaunchKernelGGL(k_dequant<2>, grid, dim3(256), 0, s, packed, scales, N, K, active,
+                       n_active, first, count, dst);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const uint16_t* rows, int d, const int32_t* inv_perm,
+                          const float* gates, int T, int k, uint16_t* out, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_combine, dim3(T), dim3(256), 0, s, rows, d, inv_perm, gates, k, out);
+  return hipGetLastError();
+}
+
+}  // namespace qgg

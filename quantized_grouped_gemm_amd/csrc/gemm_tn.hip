@@ -1,0 +1,303 @@
+// Grouped GEMM y = a . W_e over the routed rows of each expert (reduction over
+// W's rows), the transposed access that the input-gradient backward needs.
+//
+// Orbit page, section 时刻细节: the backward through the frozen base forms
+// only the input gradient (bypass-base-weight-grad GEMM backward), so the
+// weights are read transposed: dA = dO . W_down and dXp = dH . W_gate_up,
+// with the group-32 scales running along W's K index (the output columns
+// here), not along the reduction.
+//
+// Work decomposition: as the forward kernel (persistent grid, XCD-contiguous
+// item ranges, 4 wavefronts x 64 output columns, v_mfma_f32_32x32x16_bf16),
+// but both operands are staged through double-buffered LDS, 32 reduction
+// rows per stage.  Each stage's weight tile (32 W rows x 256 columns) is
+// loaded once per workgroup with each thread taking two adjacent rows and 16
+// columns; the decoded values are paired row-wise with v_perm_b32 and written
+// column-major, so a B operand (8 consecutive reduction rows of one column) is
+// one 16-byte LDS read.  The SwiGLU-backward epilogue applies the gate and the
+// SwiGLU derivative from the saved forward activations.
+#include "qgg_device.hpp"
+#include "qgg_internal.hpp"
+
+namespace qgg {
+
+namespace {
+
+constexpr int kKR = 32;               // reduction rows per stage
+constexpr int kRowBT = kKR * 2 + 16;  // padded LDS bytes per row (A) / column (B)
+// B columns get an extra 64 bytes every 16 columns so that the 64 lanes of a
+// wavefront writing (row pair, column) words hit 64 distinct banks.
+constexpr int kBsBytes = 256 * kRowBT + 16 * 64;
+__device__ __forceinline__ int bcol(int c) { return c * kRowBT + (c >> 4) * 64; }
+
+__device__ __forceinline__ uint16_t bf16_hw_t(float v) {
+  return __builtin_bit_cast(uint16_t, (__bf16)v);
+}
+
+template <int SRC>
+struct BStage {
+  // two W rows, 16 columns each
+  uint32_t p[SRC == kSrcBF16 ? 16 : 4];
+  float s0, s1;
+};
+
+template <int SRC>
+__device__ __forceinline__ void load_bt(const GemmArgs& g, int64_t slot_or_expert, int r,
+                                        int c, bool ok, BStage<SRC>& b) {
+  // rows r, r+1 of W (reduction index), columns c..c+15 (W's K index)
+  if (!ok) {
+#pragma unroll
+    for (int i = 0; i < (SRC == kSrcBF16 ? 16 : 4); ++i) b.p[i] = 0;
+    b.s0 = b.s1 = 0.f;
+    return;
+  }
+  if constexpr (SRC == kSrcBF16) {
+    const uint16_t* w0 = g.wbf16 + (slot_or_expert * g.N + r) * (int64_t)g.K + c;
+    const u32x4_t* a0 = reinterpret_cast<const u32x4_t*>(w0);
+    const u32x4_t* a1 = reinterpret_cast<const u32x4_t*>(w0 + g.K);
+    const u32x4_t x0 = a0[0], x1 = a0[1], y0 = a1[0], y1 = a1[1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      b.p[i] = x0[i];
+      b.p[4 + i] = x1[i];
+      b.p[8 + i] = y0[i];
+      b.p[12 + i] = y1[i];
+    }
+  } else {
+    const int64_t rowbytes = g.K / 2;
+    const uint8_t* w0 = g.packed + (slot_or_expert * g.N + r) * rowbytes + c / 2;
+    const uint2 x = *reinterpret_cast<const uint2*>(w0);
+    const uint2 y = *reinterpret_cast<const uint2*>(w0 + rowbytes);
+    b.p[0] = x.x;
+    b.p[1] = x.y;
+    b.p[2] = y.x;
+    b.p[3] = y.y;
+    const int64_t si = (slot_or_expert * g.N + r) * (int64_t)(g.K / 32) + c / 32;
+    if constexpr (SRC == kSrcMXFP4) {
+      const uint8_t* sp = static_cast<const uint8_t*>(g.scales);
+      b.s0 = e8m0_to_f32(sp[si]);
+      b.s1 = e8m0_to_f32(sp[si + g.K / 32]);
+    } else {
+      const uint16_t* sp = static_cast<const uint16_t*>(g.scales);
+      b.s0 = bf16_to_f32(sp[si]);
+      b.s1 = bf16_to_f32(sp[si + g.K / 32]);
+    }
+  }
+}
+
+// Decode both rows to BF16 pairs, interleave row-wise per column and store
+// column-major: Bs[col][r..r+1].
+template <int SRC>
+__device__ __forceinline__ void store_bt(const BStage<SRC>& b, uint8_t* Bs, int cl, int rp) {
+  uint32_t r0[8], r1[8];
+  if constexpr (SRC == kSrcBF16) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      r0[i] = b.p[i];
+      r1[i] = b.p[8 + i];
+    }
+  } else if constexpr (SRC == kSrcMXFP4) {
+    dq8_mxfp4(b.p[0], b.s0, r0);
+    dq8_mxfp4(b.p[1], b.s0, r0 + 4);
+    dq8_mxfp4(b.p[2], b.s1, r1);
+    dq8_mxfp4(b.p[3], b.s1, r1 + 4);
+  } else {
+    const float n0 = -8.0f * b.s0, n1 = -8.0f * b.s1;
+    dq8_int4(b.p[0], b.s0, n0, r0);
+    dq8_int4(b.p[1], b.s0, n0, r0 + 4);
+    dq8_int4(b.p[2], b.s1, n1, r1);
+    dq8_int4(b.p[3], b.s1, n1, r1 + 4);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    // column 2i: low halves; column 2i+1: high halves
+    const uint32_t lo = __builtin_amdgcn_perm(r1[i], r0[i], 0x05040100u);
+    const uint32_t hi = __builtin_amdgcn_perm(r1[i], r0[i], 0x07060302u);
+    *reinterpret_cast<uint32_t*>(Bs + bcol(cl + 2 * i) + rp * 4) = lo;
+    *reinterpret_cast<uint32_t*>(Bs + bcol(cl + 2 * i + 1) + rp * 4) = hi;
+  }
+}
+
+template <int SRC, int MB, int EPI, int AMODE>
+__global__ __launch_bounds__(256, MB == 4 ? 1 : 2) void k_gemm_tn(GemmArgs g) {
+  constexpr int MT = 32 * MB;
+  constexpr int ACH = MT * 4;                    // 16-byte A chunks per stage
+  constexpr int NCH = (ACH + 255) / 256;
+  __shared__ __attribute__((aligned(16))) uint8_t As[2][MT * kRowBT];
+  __shared__ __attribute__((aligned(16))) uint8_t Bs[2][kBsBytes];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int col = lane & 31;
+  const int half = lane >> 5;
+  const int t_begin = g.range[0];
+  const int t_end = g.range[1];
+  const int n_tiles_n = (g.K + 255) / 256;      // output columns = W's K index
+  const int items = (t_end - t_begin) * n_tiles_n;
+  const int per_xcd = gridDim.x >> 3;
+  const int xcd = blockIdx.x & 7;
+  const int span = (items + 7) >> 3;
+  const int q_end = min(items, (xcd + 1) * span);
+  const int nstages = g.N / kKR;
+  // B loader role: rows 2*rp, 2*rp+1 of the stage, columns 16*bq .. +15
+  const int rp = tid & 15;
+  const int bq = tid >> 4;
+
+  for (int q = xcd * span + (blockIdx.x >> 3); q < q_end; q += per_xcd) {
+    const int4 tile = g.tiles[t_begin + q / n_tiles_n];
+    const int c0 = (q % n_tiles_n) * 256;
+    const int row0 = tile.y, nrows = tile.z;
+    const int64_t wsel = SRC == kSrcBF16 ? (int64_t)(tile.w - g.bf16_slot_base) : tile.x;
+
+    const uint16_t* asrc[NCH];
+    int adst[NCH];
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int c = tid + 256 * i;
+      const int r = c >> 2;
+      const int cc = c & 3;
+      const int rr = (c < ACH && r < nrows) ? r : 0;
+      int64_t srow;
+      if constexpr (AMODE == kATokens) srow = g.perm[row0 + rr] / g.topk;
+      else srow = row0 + rr;
+      asrc[i] = g.a + srow * g.lda + cc * 8;
+      adst[i] = c < ACH ? r * kRowBT + cc * 16 : -1;
+    }
+    const bool bok = c0 + 16 * bq < g.K;
+    const int wbase = c0 + wave * 64;
+    const bool active = wbase < g.K;
+
+    f32x16_t acc[MB][2];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[mb][nb][i] = 0.f;
+
+    BStage<SRC> bst;
+    u32x4_t areg[NCH];
+    load_bt<SRC>(g, wsel, 2 * rp, c0 + 16 * bq, bok, bst);
+#pragma unroll
+    for (int i = 0; i < NCH; ++i)
+      if (adst[i] >= 0) areg[i] = *reinterpret_cast<const u32x4_t*>(asrc[i]);
+    store_bt<SRC>(bst, Bs[0], 16 * bq, rp);
+#pragma unroll
+    for (int i = 0; i < NCH; ++i)
+      if (adst[i] >= 0) *reinterpret_cast<u32x4_t*>(&As[0][adst[i]]) = areg[i];
+    __syncthreads();
+
+    for (int st = 0; st < nstages; ++st) {
+      const int buf = st & 1;
+      if (st + 1 < nstages) {
+        load_bt<SRC>(g, wsel, (st + 1) * kKR + 2 * rp, c0 + 16 * bq, bok, bst);
+#pragma unroll
+        for (int i = 0; i < NCH; ++i)
+          if (adst[i] >= 0)
+            areg[i] = *reinterpret_cast<const u32x4_t*>(asrc[i] + (st + 1) * kKR);
+      }
+      if (active) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const bf16x8_t b0 = *reinterpret_cast<const bf16x8_t*>(
+              &Bs[buf][bcol(wave * 64 + col) + (16 * s + 8 * half) * 2]);
+          const bf16x8_t b1 = *reinterpret_cast<const bf16x8_t*>(
+              &Bs[buf][bcol(wave * 64 + 32 + col) + (16 * s + 8 * half) * 2]);
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) {
+            if (mb * 32 < nrows) {
+              const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(
+                  &As[buf][(mb * 32 + col) * kRowBT + (16 * s + 8 * half) * 2]);
+              acc[mb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b0, acc[mb][0], 0, 0, 0);
+              acc[mb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b1, acc[mb][1], 0, 0, 0);
+            }
+          }
+        }
+      }
+      if (st + 1 < nstages) {
+        store_bt<SRC>(bst, Bs[buf ^ 1], 16 * bq, rp);
+#pragma unroll
+        for (int i = 0; i < NCH; ++i)
+          if (adst[i] >= 0) *reinterpret_cast<u32x4_t*>(&As[buf ^ 1][adst[i]]) = areg[i];
+      }
+      __syncthreads();
+    }
+
+    if (!active) continue;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      if (mb * 32 >= nrows) continue;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int r = mb * 32 + 8 * i + 4 * half + j;
+          if (r >= nrows) continue;
+          const int64_t orow = row0 + r;
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb) {
+            const int c = wbase + nb * 32 + col;
+            const float v = acc[mb][nb][i * 4 + j];
+            if constexpr (EPI == kEpiSwiGLUBwd) {
+              // v = (dY . W_down)[c]; dA = g * v; h_saved holds [gate | up]
+              const float gate = g.gates[g.perm[orow]];
+              const float da = gate * v;
+              const int64_t hb = orow * 2 * (int64_t)g.inter;
+              const float hg = bf16_to_f32(g.h[hb + c]);
+              const float hu = bf16_to_f32(g.h[hb + g.inter + c]);
+              const float sg = 1.0f / (1.0f + __expf(-hg));
+              const float dsilu = sg * (1.0f + hg * (1.0f - sg));
+              g.y[orow * g.ldy + c] = bf16_hw_t(da * hu * dsilu);
+              g.y[orow * g.ldy + g.inter + c] = bf16_hw_t(da * hg * sg);
+            } else {
+              g.y[orow * g.ldy + c] = bf16_hw_t(v);
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int SRC, int MB, int EPI, int AMODE>
+hipError_t launch_tn_t(const GemmArgs& g, hipStream_t s) {
+  const int n_tiles_n = (g.K + 255) / 256;
+  const int64_t bound = (int64_t)g.max_tiles * n_tiles_n;
+  if (bound <= 0) return hipSuccess;
+  int64_t grid = std::min<int64_t>(bound, (int64_t)num_cus() * (MB == 4 ? 1 : 2));
+  grid = (grid + 7) / 8 * 8;
+  hipLaunchKernelGGL((k_gemm_tn<SRC, MB, EPI, AMODE>), dim3((unsigned)grid), dim3(256), 0, s, g);
+  return hipGetLastError();
+}
+
+template <int SRC, int MB>
+hipError_t launch_tn_e(const GemmArgs& g, hipStream_t s) {
+  if (g.epi == kEpiSwiGLUBwd) {
+    return g.amode == kATokens ? launch_tn_t<SRC, MB, kEpiSwiGLUBwd, kATokens>(g, s)
+                               : launch_tn_t<SRC, MB, kEpiSwiGLUBwd, kASorted>(g, s);
+  }
+  return g.amode == kATokens ? launch_tn_t<SRC, MB, kEpiStore, kATokens>(g, s)
+                             : launch_tn_t<SRC, MB, kEpiStore, kASorted>(g, s);
+}
+
+template <int SRC>
+hipError_t launch_tn_m(const GemmArgs& g, int MB, hipStream_t s) {
+  switch (MB) {
+    case 1: return launch_tn_e<SRC, 1>(g, s);
+    case 2: return launch_tn_e<SRC, 2>(g, s);
+    default: return launch_tn_e<SRC, 4>(g, s);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gemm_tn(const GemmArgs& g, int MB, hipStream_t s) {
+  switch (g.src) {
+    case kSrcBF16: return launch_tn_m<kSrcBF16>(g, MB, s);
+    case kSrcMXFP4: return launch_tn_m<kSrcMXFP4>(g, MB, s);
+    default: return launch_tn_m<kSrcINT4>(g, MB, s);
+  }
+}
+
+}  // namespace qgg

@@ -1,0 +1,448 @@
+// C-ABI entry points: argument validation, workspace layout, chunk loop and
+// kernel orchestration.  No device allocation happens here: every buffer is
+// the caller's.
+#include <hip/hip_runtime.h>
+
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "../../include/qgg.h"
+#include "qgg_internal.hpp"
+
+namespace qgg {
+
+int num_cus() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Bump allocator over the caller's workspace.
+struct Carver {
+  char* base;
+  size_t off = 0;
+  explicit Carver(void* b) : base(static_cast<char*>(b)) {}
+  template <class T>
+  T* take(size_t bytes) {
+    T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+    off += align_up(bytes);
+    return p;
+  }
+};
+
+// Rows per M-tile, from the mean rows per expert (P / E) rounded up to a
+// power-of-two number of 32-row MFMA blocks, at most 4.
+int choose_mb(int64_t P, int E) {
+  const int64_t mean = E > 0 ? (P + E - 1) / E : P;
+  const int64_t blocks = (mean + 31) / 32;
+  if (blocks <= 1) return 1;
+  if (blocks <= 2) return 2;
+  return 4;
+}
+
+int64_t tile_capacity(int64_t P, int E, int MT) { return (P + MT - 1) / MT + E + 1; }
+
+struct Plan {
+  int4* tiles = nullptr;
+  int32_t* chunk_first = nullptr;
+  int mb = 1;
+  int64_t cap = 0;
+};
+
+void carve_plan(Carver& cv, int64_t P, int E, Plan& pl) {
+  pl.mb = choose_mb(P, E);
+  pl.cap = tile_capacity(P, E, 32 * pl.mb);
+  pl.tiles = cv.take<int4>(sizeof(int4) * pl.cap);
+  pl.chunk_first = cv.take<int32_t>(sizeof(int32_t) * (E + 2));
+}
+
+bool valid_fmt(int f) { return f == QGG_FMT_MXFP4 || f == QGG_FMT_INT4; }
+
+bool valid_weight(const qgg_qweight* w, int E, int N, int K) {
+  return w && valid_fmt(w->fmt) && w->E == E && w->N == N && w->K == K && w->packed &&
+         w->scales;
+}
+
+bool valid_perm(const qgg_perm* p) {
+  return p && p->counts && p->offsets && p->perm && p->inv_perm && p->active && p->n_active;
+}
+
+bool valid_route_dims(int T, int E, int k) {
+  return T >= 0 && E >= 1 && E <= 1024 && k >= 1 && k <= 32 && k <= E &&
+         (int64_t)T * k < (int64_t)1 << 31;
+}
+
+PermPtrs to_ptrs(const qgg_perm* p) {
+  return PermPtrs{p->counts, p->offsets, p->perm, p->inv_perm, p->active, p->n_active};
+}
+
+#define QGG_HIP(expr)                          \
+  do {                                         \
+    if ((expr) != hipSuccess) return QGG_ERR_HIP; \
+  } while (0)
+
+int src_of(int fmt) { return fmt == QGG_FMT_MXFP4 ? kSrcMXFP4 : kSrcINT4; }
+
+GemmArgs base_args(const qgg_qweight* w, const Plan& pl) {
+  GemmArgs g;
+  std::memset(&g, 0, sizeof g);
+  g.src = src_of(w->fmt);
+  g.packed = w->packed;
+  g.scales = w->scales;
+  g.N = w->N;
+  g.K = w->K;
+  g.tiles = pl.tiles;
+  g.range = pl.chunk_first;
+  g.max_tiles = (int)pl.cap;
+  g.mt_rows = 32 * pl.mb;
+  return g;
+}
+
+// Host copy of n_active and the chunk table, read once per chunked call.
+qgg_status read_chunks(const Plan& pl, const int32_t* n_active_dev, int E, int C,
+                       hipStream_t s, int* n_active, std::vector<int32_t>& first) {
+  QGG_HIP(hipMemcpyAsync(n_active, n_active_dev, sizeof(int32_t), hipMemcpyDeviceToHost, s));
+  first.assign(E + 2, 0);
+  QGG_HIP(hipMemcpyAsync(first.data(), pl.chunk_first, sizeof(int32_t) * (E + 2),
+                         hipMemcpyDeviceToHost, s));
+  QGG_HIP(hipStreamSynchronize(s));
+  (void)C;
+  return QGG_OK;
+}
+
+}  // namespace
+}  // namespace qgg
+
+using namespace qgg;
+
+extern "C" {
+
+const char* qgg_status_string(qgg_status s) {
+  switch (s) {
+    case QGG_OK: return "ok";
+    case QGG_ERR_INVALID_ARG: return "invalid argument";
+    case QGG_ERR_UNSUPPORTED: return "unsupported shape or option";
+    case QGG_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case QGG_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* qgg_version(void) { return "qgg 0.1 gfx950"; }
+
+// Workspace layout per call (each piece 256-byte aligned, in this order):
+//  PERMUTE  segment counts
+//  GEMM     plan (tiles, chunk table) | BF16 chunk scratch (CHUNKED)
+//  FFN_FWD  segment counts | plan | a [P][inter] | o [P][d] | scratch
+//  DX_BWD   plan | dH [P][2*inter] | dXp [P][d] | scratch
+size_t qgg_workspace_bytes(int call, int T, int d, int E, int k, int N_or_inter, int variant,
+                           int chunk, size_t* scratch_bytes) {
+  if (scratch_bytes) *scratch_bytes = 0;
+  if (!valid_route_dims(T, E, k) || d <= 0 || N_or_inter <= 0 || chunk < 0) return 0;
+  const int64_t P = (int64_t)T * k;
+  const int64_t C = chunk > 0 ? std::min<int64_t>(chunk, E) : std::min<int64_t>(E, std::max<int64_t>(P, 1));
+  Carver cv(nullptr);
+  Plan pl;
+  size_t scratch = 0;
+  switch (call) {
+    case QGG_CALL_PERMUTE:
+      cv.take<char>(permute_ws_bytes(P, E));
+      break;
+    case QGG_CALL_GEMM:
+      carve_plan(cv, P, E, pl);
+      if (variant == QGG_CHUNKED) scratch = (size_t)C * N_or_inter * d * 2;
+      cv.take<char>(scratch);
+      break;
+    case QGG_CALL_FFN_FWD: {
+      const int64_t I = N_or_inter;
+      cv.take<char>(permute_ws_bytes(P, E));
+      carve_plan(cv, P, E, pl);
+      cv.take<char>((size_t)P * I * 2);
+      cv.take<char>((size_t)P * d * 2);
+      if (variant == QGG_CHUNKED) scratch = (size_t)C * 2 * I * d * 2;
+      cv.take<char>(scratch);
+      break;
+    }
+    case QGG_CALL_DX_BWD: {
+      const int64_t I = N_or_inter;
+      carve_plan(cv, P, E, pl);
+      cv.take<char>((size_t)P * 2 * I * 2);
+      cv.take<char>((size_t)P * d * 2);
+      if (variant == QGG_CHUNKED) scratch = (size_t)C * 2 * I * d * 2;
+      cv.take<char>(scratch);
+      break;
+    }
+    default:
+      return 0;
+  }
+  if (scratch_bytes) *scratch_bytes = scratch;
+  return std::max<size_t>(cv.off, kAlign);
+}
+
+qgg_status moe_route(const float* logits, int T, int E, int k, int32_t* topk_ids,
+                     float* topk_gates, int32_t* err_flag, qgg_stream_t stream) {
+  if (!valid_route_dims(T, E, k)) return QGG_ERR_INVALID_ARG;
+  if (T > 0 && (!logits || !topk_ids || !topk_gates)) return QGG_ERR_INVALID_ARG;
+  QGG_HIP(launch_route(logits, T, E, k, topk_ids, topk_gates, err_flag, stream));
+  return QGG_OK;
+}
+
+qgg_status expert_permute(const int32_t* topk_ids, int T, int k, int E, const qgg_perm* p,
+                          const uint16_t* x, int d, uint16_t* x_perm, int32_t* err_flag,
+                          void* workspace, size_t ws_bytes, qgg_stream_t stream) {
+  if (!valid_route_dims(T, E, k) || !valid_perm(p)) return QGG_ERR_INVALID_ARG;
+  if (T > 0 && !topk_ids) return QGG_ERR_INVALID_ARG;
+  const bool gather = x != nullptr && x_perm != nullptr;
+  if (gather && (d <= 0 || d % 8)) return QGG_ERR_INVALID_ARG;
+  const int64_t P = (int64_t)T * k;
+  const size_t need = qgg_workspace_bytes(QGG_CALL_PERMUTE, T, 8, E, k, 1, QGG_FUSED, 0, nullptr);
+  if (!workspace || ws_bytes < need) return QGG_ERR_WORKSPACE_TOO_SMALL;
+  const PermPtrs pp = to_ptrs(p);
+  QGG_HIP(launch_permute(topk_ids, P, E, pp, err_flag, workspace, stream));
+  if (gather) QGG_HIP(launch_gather(x, d, pp, E, k, P, x_perm, stream));
+  return QGG_OK;
+}
+
+qgg_status dequant_grouped_gemm(const qgg_qweight* w, const uint16_t* a, int flags,
+                                const qgg_perm* p, int T, int k, int variant, int chunk,
+                                void* workspace, size_t ws_bytes, uint16_t* y,
+                                qgg_stream_t stream) {
+  if (!w || !valid_perm(p) || !valid_fmt(w->fmt)) return QGG_ERR_INVALID_ARG;
+  const int E = w->E, N = w->N, K = w->K;
+  if (!valid_route_dims(T, E, k) || N <= 0 || K <= 0 || chunk < 0) return QGG_ERR_INVALID_ARG;
+  if (!w->packed || !w->scales) return QGG_ERR_INVALID_ARG;
+  if (variant != QGG_CHUNKED && variant != QGG_FUSED) return QGG_ERR_INVALID_ARG;
+  if (flags & ~(QGG_A_TOKENS | QGG_TRANSPOSE_W | QGG_DEQUANT_ONLY)) return QGG_ERR_INVALID_ARG;
+  if (K % 128 || N % 64) return QGG_ERR_UNSUPPORTED;
+  const bool trans = flags & QGG_TRANSPOSE_W;
+  const bool dq_only = flags & QGG_DEQUANT_ONLY;
+  if (dq_only && variant != QGG_CHUNKED) return QGG_ERR_INVALID_ARG;
+  if (!dq_only && (!a || !y) && T > 0) return QGG_ERR_INVALID_ARG;
+  const int64_t P = (int64_t)T * k;
+  size_t scratch = 0;
+  const size_t need = qgg_workspace_bytes(QGG_CALL_GEMM, T, K, E, k, N, variant, chunk, &scratch);
+  if (!workspace || ws_bytes < need) return QGG_ERR_WORKSPACE_TOO_SMALL;
+  const int C = chunk > 0 ? std::min(chunk, E) : (int)std::min<int64_t>(E, std::max<int64_t>(P, 1));
+  Carver cv(workspace);
+  Plan pl;
+  carve_plan(cv, P, E, pl);
+  uint16_t* sbuf = cv.take<uint16_t>(scratch);
+
+  if (dq_only) {
+    QGG_HIP(launch_dequant(w->fmt, w->packed, w->scales, N, K, p->active, p->n_active, 0, C,
+                           static_cast<uint16_t*>(workspace), stream));
+    return QGG_OK;
+  }
+  if (P == 0) return QGG_OK;
+  const PermPtrs pp = to_ptrs(p);
+  QGG_HIP(launch_tile_plan(pp, 32 * pl.mb, variant == QGG_CHUNKED ? C : 0, pl.tiles,
+                           pl.chunk_first, stream));
+  GemmArgs g = base_args(w, pl);
+  g.a = a;
+  g.lda = trans ? N : K;
+  g.amode = (flags & QGG_A_TOKENS) ? kATokens : kASorted;
+  g.perm = p->perm;
+  g.topk = k;
+  g.y = y;
+  g.ldy = trans ? K : N;
+  g.epi = kEpiStore;
+  if (variant == QGG_FUSED) {
+    QGG_HIP(trans ? launch_gemm_tn(g, pl.mb, stream) : launch_gemm_nt(g, pl.mb, stream));
+    return QGG_OK;
+  }
+  int n_act = 0;
+  std::vector<int32_t> first;
+  qgg_status st = read_chunks(pl, p->n_active, E, C, stream, &n_act, first);
+  if (st != QGG_OK) return st;
+  const int nch = (n_act + C - 1) / C;
+  g.src = kSrcBF16;
+  g.wbf16 = sbuf;
+  for (int c = 0; c < nch; ++c) {
+    QGG_HIP(launch_dequant(w->fmt, w->packed, w->scales, N, K, p->active, p->n_active, c * C, C,
+                           sbuf, stream));
+    g.range = pl.chunk_first + c;
+    g.max_tiles = first[c + 1] - first[c];
+    g.bf16_slot_base = c * C;
+    QGG_HIP(trans ? launch_gemm_tn(g, pl.mb, stream) : launch_gemm_nt(g, pl.mb, stream));
+  }
+  return QGG_OK;
+}
+
+qgg_status moe_ffn_fwd(const qgg_qweight* w_gate_up, const qgg_qweight* w_down,
+                       const uint16_t* x, const float* logits, int T, int d, int E, int k,
+                       int inter, int variant, int chunk, int32_t* topk_ids, float* topk_gates,
+                       const qgg_perm* p, uint16_t* h_save, int32_t* err_flag, void* workspace,
+                       size_t ws_bytes, uint16_t* y, qgg_stream_t stream) {
+  if (!valid_route_dims(T, E, k) || d <= 0 || inter <= 0 || chunk < 0) return QGG_ERR_INVALID_ARG;
+  if (!valid_weight(w_gate_up, E, 2 * inter, d) || !valid_weight(w_down, E, d, inter))
+    return QGG_ERR_INVALID_ARG;
+  if (w_gate_up->fmt != w_down->fmt) return QGG_ERR_INVALID_ARG;
+  if (variant != QGG_CHUNKED && variant != QGG_FUSED) return QGG_ERR_INVALID_ARG;
+  if (!valid_perm(p)) return QGG_ERR_INVALID_ARG;
+  if (T > 0 && (!x || !logits || !topk_ids || !topk_gates || !y)) return QGG_ERR_INVALID_ARG;
+  if (d % 128 || inter % 128) return QGG_ERR_UNSUPPORTED;
+  const int64_t P = (int64_t)T * k;
+  size_t scratch = 0;
+  const size_t need =
+      qgg_workspace_bytes(QGG_CALL_FFN_FWD, T, d, E, k, inter, variant, chunk, &scratch);
+  if (!workspace || ws_bytes < need) return QGG_ERR_WORKSPACE_TOO_SMALL;
+  const int C = chunk > 0 ? std::min(chunk, E) : (int)std::min<int64_t>(E, std::max<int64_t>(P, 1));
+  Carver cv(workspace);
+  void* pws = cv.take<char>(permute_ws_bytes(P, E));
+  Plan pl;
+  carve_plan(cv, P, E, pl);
+  uint16_t* abuf = cv.take<uint16_t>((size_t)P * inter * 2);
+  uint16_t* obuf = cv.take<uint16_t>((size_t)P * d * 2);
+  uint16_t* sbuf = cv.take<uint16_t>(scratch);
+  const PermPtrs pp = to_ptrs(p);
+
+  QGG_HIP(launch_route(logits, T, E, k, topk_ids, topk_gates, err_flag, stream));
+  QGG_HIP(launch_permute(topk_ids, P, E, pp, err_flag, pws, stream));
+  if (P == 0) return QGG_OK;
+  QGG_HIP(launch_tile_plan(pp, 32 * pl.mb, variant == QGG_CHUNKED ? C : 0, pl.tiles,
+                           pl.chunk_first, stream));
+
+  GemmArgs gu = base_args(w_gate_up, pl);
+  gu.a = x;
+  gu.lda = d;
+  gu.amode = kATokens;
+  gu.perm = p->perm;
+  gu.topk = k;
+  gu.y = abuf;
+  gu.ldy = inter;
+  gu.epi = kEpiSwiGLU;
+  gu.inter = inter;
+  gu.h = h_save;
+  GemmArgs dn = base_args(w_down, pl);
+  dn.a = abuf;
+  dn.lda = inter;
+  dn.amode = kASorted;
+  dn.perm = p->perm;
+  dn.topk = k;
+  dn.y = obuf;
+  dn.ldy = d;
+  dn.epi = kEpiStore;
+
+  if (variant == QGG_FUSED) {
+    QGG_HIP(launch_gemm_nt(gu, pl.mb, stream));
+    QGG_HIP(launch_gemm_nt(dn, pl.mb, stream));
+  } else {
+    int n_act = 0;
+    std::vector<int32_t> first;
+    qgg_status st = read_chunks(pl, p->n_active, E, C, stream, &n_act, first);
+    if (st != QGG_OK) return st;
+    const int nch = (n_act + C - 1) / C;
+    gu.src = dn.src = kSrcBF16;
+    gu.wbf16 = dn.wbf16 = sbuf;
+    for (int c = 0; c < nch; ++c) {
+      gu.range = dn.range = pl.chunk_first + c;
+      gu.max_tiles = dn.max_tiles = first[c + 1] - first[c];
+      gu.bf16_slot_base = dn.bf16_slot_base = c * C;
+      QGG_HIP(launch_dequant(w_gate_up->fmt, w_gate_up->packed, w_gate_up->scales, 2 * inter, d,
+                             p->active, p->n_active, c * C, C, sbuf, stream));
+      QGG_HIP(launch_gemm_nt(gu, pl.mb, stream));
+      QGG_HIP(launch_dequant(w_down->fmt, w_down->packed, w_down->scales, d, inter, p->active,
+                             p->n_active, c * C, C, sbuf, stream));
+      QGG_HIP(launch_gemm_nt(dn, pl.mb, stream));
+    }
+  }
+  QGG_HIP(launch_combine(obuf, d, p->inv_perm, topk_gates, T, k, y, stream));
+  return QGG_OK;
+}
+
+qgg_status moe_dx_bwd(const qgg_qweight* w_gate_up, const qgg_qweight* w_down,
+                      const uint16_t* dy, const float* topk_gates, const qgg_perm* p,
+                      const uint16_t* h_saved, int T, int d, int E, int k, int inter, int variant,
+                      int chunk, void* workspace, size_t ws_bytes, uint16_t* dx,
+                      qgg_stream_t stream) {
+  if (!valid_route_dims(T, E, k) || d <= 0 || inter <= 0 || chunk < 0) return QGG_ERR_INVALID_ARG;
+  if (!valid_weight(w_gate_up, E, 2 * inter, d) || !valid_weight(w_down, E, d, inter))
+    return QGG_ERR_INVALID_ARG;
+  if (w_gate_up->fmt != w_down->fmt) return QGG_ERR_INVALID_ARG;
+  if (variant != QGG_CHUNKED && variant != QGG_FUSED) return QGG_ERR_INVALID_ARG;
+  if (!valid_perm(p)) return QGG_ERR_INVALID_ARG;
+  if (T > 0 && (!dy || !topk_gates || !h_saved || !dx)) return QGG_ERR_INVALID_ARG;
+  if (d % 256 || inter % 256) return QGG_ERR_UNSUPPORTED;
+  const int64_t P = (int64_t)T * k;
+  size_t scratch = 0;
+  const size_t need =
+      qgg_workspace_bytes(QGG_CALL_DX_BWD, T, d, E, k, inter, variant, chunk, &scratch);
+  if (!workspace || ws_bytes < need) return QGG_ERR_WORKSPACE_TOO_SMALL;
+  if (P == 0) return QGG_OK;
+  const int C = chunk > 0 ? std::min(chunk, E) : (int)std::min<int64_t>(E, std::max<int64_t>(P, 1));
+  Carver cv(workspace);
+  Plan pl;
+  carve_plan(cv, P, E, pl);
+  uint16_t* dh = cv.take<uint16_t>((size_t)P * 2 * inter * 2);
+  uint16_t* dxp = cv.take<uint16_t>((size_t)P * d * 2);
+  uint16_t* sbuf = cv.take<uint16_t>(scratch);
+  const PermPtrs pp = to_ptrs(p);
+  QGG_HIP(launch_tile_plan(pp, 32 * pl.mb, variant == QGG_CHUNKED ? C : 0, pl.tiles,
+                           pl.chunk_first, stream));
+
+  // dA = (g dY) . W_down, then dH from the SwiGLU derivative (fused epilogue)
+  GemmArgs dn = base_args(w_down, pl);
+  dn.a = dy;
+  dn.lda = d;
+  dn.amode = kATokens;
+  dn.perm = p->perm;
+  dn.topk = k;
+  dn.y = dh;
+  dn.ldy = 2 * inter;
+  dn.epi = kEpiSwiGLUBwd;
+  dn.inter = inter;
+  dn.h = const_cast<uint16_t*>(h_saved);
+  dn.gates = topk_gates;
+  // dXp = dH . W_gate_up
+  GemmArgs gu = base_args(w_gate_up, pl);
+  gu.a = dh;
+  gu.lda = 2 * inter;
+  gu.amode = kASorted;
+  gu.perm = p->perm;
+  gu.topk = k;
+  gu.y = dxp;
+  gu.ldy = d;
+  gu.epi = kEpiStore;
+
+  if (variant == QGG_FUSED) {
+    QGG_HIP(launch_gemm_tn(dn, pl.mb, stream));
+    QGG_HIP(launch_gemm_tn(gu, pl.mb, stream));
+  } else {
+    int n_act = 0;
+    std::vector<int32_t> first;
+    qgg_status st = read_chunks(pl, p->n_active, E, C, stream, &n_act, first);
+    if (st != QGG_OK) return st;
+    const int nch = (n_act + C - 1) / C;
+    dn.src = gu.src = kSrcBF16;
+    dn.wbf16 = gu.wbf16 = sbuf;
+    for (int c = 0; c < nch; ++c) {
+      dn.range = gu.range = pl.chunk_first + c;
+      dn.max_tiles = gu.max_tiles = first[c + 1] - first[c];
+      dn.bf16_slot_base = gu.bf16_slot_base = c * C;
+      QGG_HIP(launch_dequant(w_down->fmt, w_down->packed, w_down->scales, d, inter, p->active,
+                             p->n_active, c * C, C, sbuf, stream));
+      QGG_HIP(launch_gemm_tn(dn, pl.mb, stream));
+      QGG_HIP(launch_dequant(w_gate_up->fmt, w_gate_up->packed, w_gate_up->scales, 2 * inter, d,
+                             p->active, p->n_active, c * C, C, sbuf, stream));
+      QGG_HIP(launch_gemm_tn(gu, pl.mb, stream));
+    }
+  }
+  QGG_HIP(launch_combine(dxp, d, p->inv_perm, nullptr, T, k, dx, stream));
+  return QGG_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,104 @@
+// Device helpers shared by the gfx950 kernels: BF16 conversion, wavefront
+// prefix sums, MFMA operand types and the 4-bit decoders.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace qgg {
+
+constexpr int kWave = 64;
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t h16) { return __uint_as_float(h16 << 16); }
+
+// Round-to-nearest-even fp32 -> BF16 in integer arithmetic; NaN -> quiet NaN
+// with the input's upper bits.
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// Two fp32 -> packed BF16 pair (v_cvt_pk_bf16_f32, round to nearest even).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  f32x2_t v = {lo, hi};
+  bf16x2_t b = __builtin_convertvector(v, bf16x2_t);
+  return __builtin_bit_cast(uint32_t, b);
+}
+
+// Inclusive prefix sum across the 64 lanes of a wavefront.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & (kWave - 1);
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int n = __shfl_up(v, off, kWave);
+    if (lane >= off) v += n;
+  }
+  return v;
+}
+
+// Exclusive prefix sum over a whole workgroup of `nthreads` threads (a
+// multiple of 64, <= 1024); `lds` holds >= 16 ints.  Returns the exclusive
+// prefix and writes the total to *total.  All threads must call it.
+__device__ __forceinline__ int block_excl_scan(int v, int* lds, int* total) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int nwaves = blockDim.x / kWave;
+  const int incl = wave_incl_scan(v);
+  if (lane == kWave - 1) lds[wave] = incl;
+  __syncthreads();
+  if (wave == 0) {
+    int s = lane < nwaves ? lds[lane] : 0;
+    s = wave_incl_scan(s);
+    if (lane < nwaves) lds[lane] = s;
+  }
+  __syncthreads();
+  const int before = wave ? lds[wave - 1] : 0;
+  *total = lds[nwaves - 1];
+  __syncthreads();
+  return before + incl - v;
+}
+
+// E8M0 exponent code -> fp32 scale 2^(c-127); code 0 is the subnormal 2^-127,
+// code 255 is NaN.
+__device__ __forceinline__ float e8m0_to_f32(uint32_t c) {
+  const uint32_t bits = c == 0 ? 0x00400000u : (c == 255 ? 0x7FC00000u : (c << 23));
+  return __uint_as_float(bits);
+}
+
+// Eight MXFP4 codes (one 32-bit word, element 2b in the low nibble of byte b)
+// times a power-of-two scale -> eight BF16 values packed in four words
+// (v_cvt_scalef32_pk_bf16_fp4; exact while the product is representable).
+__device__ __forceinline__ void dq8_mxfp4(uint32_t w, float scale, uint32_t out[4]) {
+  out[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0));
+  out[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1));
+  out[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2));
+  out[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3));
+}
+
+// Eight two's-complement INT4 codes times a BF16 scale s -> eight BF16 values.
+// With n' = q + 8 (the code XOR 8) as an exact float, fma(n', s, -8 s) is
+// q * s formed exactly and rounded once; q * s needs at most 12 significant
+// bits, so the fp32 value is exact and the BF16 rounding matches
+// bf16_rne(q * s).
+__device__ __forceinline__ void dq8_int4(uint32_t w, float s, float neg8s, uint32_t out[4]) {
+  const uint32_t b = w ^ 0x88888888u;
+  const uint32_t lo = b & 0x0F0F0F0Fu;          // elements 0, 2, 4, 6
+  const uint32_t hi = (b >> 4) & 0x0F0F0F0Fu;   // elements 1, 3, 5, 7
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float e0 = (float)((lo >> (8 * i)) & 0xFFu);
+    const float e1 = (float)((hi >> (8 * i)) & 0xFFu);
+    out[i] = pack_bf16x2(__builtin_fmaf(e0, s, neg8s), __builtin_fmaf(e1, s, neg8s));
+  }
+}
+
+__device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-z)); }
+
+}  // namespace qgg

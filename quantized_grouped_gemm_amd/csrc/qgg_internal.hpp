@@ -1,0 +1,80 @@
+// Host-side declarations shared between the C-ABI layer and the kernel files.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <algorithm>
+
+namespace qgg {
+
+struct PermPtrs {
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* perm;
+  int32_t* inv_perm;
+  int32_t* active;
+  int32_t* n_active;
+};
+
+enum WSource { kSrcBF16 = 0, kSrcMXFP4 = 1, kSrcINT4 = 2 };
+enum AMode { kASorted = 0, kATokens = 1 };
+enum Epilogue { kEpiStore = 0, kEpiSwiGLU = 1, kEpiSwiGLUBwd = 2 };
+
+// One grouped GEMM launch over the M-tiles [range[0], range[1]) of a plan.
+struct GemmArgs {
+  // weights: packed 4-bit (with scales) or BF16; W is [N][K] per expert
+  int src;                       // WSource
+  const uint8_t* packed;
+  const void* scales;
+  const uint16_t* wbf16;         // BF16 weights [slots][N][K] (src == kSrcBF16)
+  int N, K;
+  int bf16_slot_base;            // BF16 slot of tile = tile.active_index - base
+  // rows (A operand)
+  const uint16_t* a;
+  int lda;
+  int amode;                     // AMode
+  const int32_t* perm;
+  int topk;
+  // plan
+  const int4* tiles;
+  const int32_t* range;          // device: first and one-past-last tile
+  int max_tiles;                 // host bound on range[1] - range[0]
+  int mt_rows;                   // rows per M-tile (32 * MB)
+  // output
+  uint16_t* y;
+  int ldy;
+  int epi;                       // Epilogue
+  int inter;                     // SwiGLU width
+  uint16_t* h;                   // fwd: optional h save [P][2I]; bwd: saved h
+  const float* gates;            // bwd SwiGLU epilogue: topk gates [T*k]
+};
+
+hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* gates,
+                        int32_t* err, hipStream_t s);
+size_t permute_ws_bytes(int64_t P, int E);
+hipError_t launch_permute(const int32_t* ids, int64_t P, int E, const PermPtrs& pp, int32_t* err,
+                          void* ws, hipStream_t s);
+hipError_t launch_gather(const uint16_t* x, int d, const PermPtrs& pp, int E, int k, int64_t P,
+                         uint16_t* out, hipStream_t s);
+hipError_t launch_tile_plan(const PermPtrs& pp, int MT, int C, int4* tiles, int32_t* chunk_first,
+                            hipStream_t s);
+
+// y = a . W^T per tile (reduce over K); output columns are W rows.
+hipError_t launch_gemm_nt(const GemmArgs& g, int MB, hipStream_t s);
+// y = a . W per tile (reduce over N); output columns are W's K index.
+hipError_t launch_gemm_tn(const GemmArgs& g, int MB, hipStream_t s);
+
+// BF16 copy of the weights of active experts [first, first + count) of the
+// active list into dst[slot][N][K].
+hipError_t launch_dequant(int fmt, const uint8_t* packed, const void* scales, int N, int K,
+                          const int32_t* active, const int32_t* n_active, int first, int count,
+                          uint16_t* dst, hipStream_t s);
+
+// out[t] = sum_j w_j * rows[inv_perm[t*k+j]] (w_j = gates[t*k+j], or 1 when
+// gates is null), fp32 in ascending j, BF16 out.
+hipError_t launch_combine(const uint16_t* rows, int d, const int32_t* inv_perm,
+                          const float* gates, int T, int k, uint16_t* out, hipStream_t s);
+
+int num_cus();
+
+}  // namespace qgg

@@ -1,0 +1,341 @@
+"""GPU parity of the HIP path against the CPU oracle, at sizes the oracle
+finishes in seconds (several tiles, ragged tails).  Integer and byte outputs
+(routing ids, permutation, dequantized weights) must match bit for bit; GEMM
+outputs must be within max relative error 2e-2 (row-RMS floor)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quantized_grouped_gemm_amd as qgg
+import synth
+from synth.configs import CONFIGS, STREAM, Config, scaled
+
+from .gpu_util import (DEV, assert_close, bf16_to_f64, dev_bf16, dev_weights, host_u16, sync)
+
+pytestmark = pytest.mark.gpu
+
+
+def _inputs(cfg: Config):
+    logits = synth.configs.router_logits(cfg)
+    x = synth.configs.activations(cfg)
+    w = synth.configs.first_weights(cfg)
+    return logits, x, w
+
+
+# ---------------------------------------------------------------- routing
+
+ROUTE_CASES = [CONFIGS["tiny_mxfp4_proj"], CONFIGS["kimi_int4_gate_up"],
+               CONFIGS["mxfp4_ffn_prefill"], CONFIGS["int4_ffn_decode_zipf"],
+               scaled(CONFIGS["tiny_mxfp4_proj"], T=37, E=1000, k=32, name="wide")]
+
+
+@pytest.mark.parametrize("cfg", ROUTE_CASES, ids=lambda c: c.name)
+def test_route_and_permute_bit_exact(cfg):
+    print(f"case {cfg.name} T={cfg.T} E={cfg.E} k={cfg.k}", flush=True)
+    logits = synth.configs.router_logits(cfg)
+    if cfg.name == "wide":
+        logits[:, 3] = logits[:, 5]          # exact ties
+    ids_ref, gates_ref = oracle.route(logits, cfg.k)
+    lt = torch.from_numpy(logits).to(DEV)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    ids, gates = qgg.moe_route(lt, cfg.k, err_flag=err)
+    sync()
+    assert int(err.item()) == 0
+    np.testing.assert_array_equal(ids.cpu().numpy(), ids_ref)
+    g = gates.cpu().numpy().astype(np.float64)
+    assert np.max(np.abs(g - gates_ref)) <= 1e-6
+    assert np.max(np.abs(g.sum(1) - 1.0)) <= 1e-6
+
+    ref = oracle.permute(ids_ref, cfg.E)
+    x = synth.normal_bf16(cfg.seed, STREAM["x"], (cfg.T, 256))
+    p, x_perm = qgg.expert_permute(ids, cfg.E, x=dev_bf16(x), err_flag=err)
+    sync()
+    assert int(err.item()) == 0
+    for name in ("counts", "offsets", "perm", "inv_perm", "active"):
+        np.testing.assert_array_equal(getattr(p, name).cpu().numpy(), ref[name], err_msg=name)
+    assert int(p.n_active.item()) == ref["n_active"]
+    np.testing.assert_array_equal(host_u16(x_perm), x[ref["perm"] // cfg.k])
+
+
+def test_permute_skewed_and_ragged():
+    # every token picks the same experts; P = 4099 * 3 spans 4 segments raggedly
+    T, k, E = 4099, 3, 700
+    ids = np.tile(np.array([[699, 3, 0]], np.int32), (T, 1))
+    ids[::7] = np.array([5, 699, 1], np.int32)
+    ref = oracle.permute(ids, E)
+    p, _ = qgg.expert_permute(torch.from_numpy(ids).to(DEV), E)
+    sync()
+    for name in ("counts", "offsets", "perm", "inv_perm", "active"):
+        np.testing.assert_array_equal(getattr(p, name).cpu().numpy(), ref[name], err_msg=name)
+    assert int(p.n_active.item()) == ref["n_active"] == 5
+
+
+def test_route_flags_non_finite_and_permute_flags_bad_ids():
+    logits = np.zeros((4, 16), np.float32)
+    logits[2, 7] = np.nan
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    qgg.moe_route(torch.from_numpy(logits).to(DEV), 2, err_flag=err)
+    sync()
+    assert int(err.item()) & 1
+    err.zero_()
+    ids = torch.tensor([[0, 1], [2, 16]], dtype=torch.int32, device=DEV)
+    qgg.expert_permute(ids, 16, err_flag=err)
+    sync()
+    assert int(err.item()) & 2
+
+
+# ------------------------------------------------------------- dequantize
+
+def _single_expert_perm():
+    ids = torch.zeros((1, 1), dtype=torch.int32, device=DEV)
+    p, _ = qgg.expert_permute(ids, 1)
+    return p
+
+
+def test_dequant_only_mxfp4_exhaustive():
+    # 256 rows (one per E8M0 code) x 128 columns holding every E2M1 code
+    N, K = 256, 128
+    codes = np.arange(16, dtype=np.uint8)
+    row = (codes[0::2] | (codes[1::2] << 4)).astype(np.uint8)
+    packed = np.tile(row, (N, K // 16))[None]
+    scales = np.tile(np.arange(256, dtype=np.uint8)[:, None], (1, K // 32))[None]
+    w = dev_weights(1, packed, scales)
+    buf = qgg.dequant_grouped_gemm(w, None, _single_expert_perm(), 1, 1, qgg.CHUNKED, 1,
+                                   flags=qgg.DEQUANT_ONLY)
+    sync()
+    got = host_u16(buf[: N * K * 2].view(torch.bfloat16)).reshape(N, K)
+    ref32 = oracle.decode(1, packed[0], scales[0])
+    ref = oracle.bf16_view(ref32)
+    nan = np.isnan(ref32)
+    np.testing.assert_array_equal(got[~nan], ref[~nan])
+    assert np.all(got[nan] == 0x7FC0)
+
+
+def test_dequant_only_int4_all_bf16_scales():
+    N, K = 16384, 128                      # 65536 groups = every BF16 scale pattern
+    codes = np.arange(16, dtype=np.uint8)
+    row = (codes[0::2] | (codes[1::2] << 4)).astype(np.uint8)
+    packed = np.tile(row, (N, K // 16))[None]
+    scales = np.arange(65536, dtype=np.uint32).astype(np.uint16).reshape(1, N, K // 32)
+    w = dev_weights(2, packed, scales)
+    buf = qgg.dequant_grouped_gemm(w, None, _single_expert_perm(), 1, 1, qgg.CHUNKED, 1,
+                                   flags=qgg.DEQUANT_ONLY)
+    sync()
+    got = host_u16(buf[: N * K * 2].view(torch.bfloat16)).reshape(N, K)
+    ref32 = oracle.decode(2, packed[0], scales[0])
+    ref = oracle.bf16_view(ref32)
+    nan = np.isnan(ref32)
+    np.testing.assert_array_equal(got[~nan], ref[~nan])
+    assert np.all((got[nan] & 0x7F80) == 0x7F80) and np.all((got[nan] & 0x7F) != 0)
+
+
+# ------------------------------------------------------------ projections
+
+PROJ_CASES = [
+    CONFIGS["tiny_mxfp4_proj"],
+    scaled(CONFIGS["kimi_int4_gate_up"], T=160, d=384, E=24, k=4, N=320, chunks=(5,),
+           name="int4_ragged_n"),
+    scaled(CONFIGS["tiny_mxfp4_proj"], T=200, d=256, E=8, k=2, N=256, name="mxfp4_mb2"),
+    scaled(CONFIGS["kimi_int4_gate_up"], T=512, d=256, E=8, k=2, N=256, chunks=(3,),
+           name="int4_mb4"),
+]
+
+
+def _proj_ref(cfg, w, x, ids):
+    P = cfg.T * cfg.k
+    tok = np.arange(P, dtype=np.int32) // cfg.k
+    return oracle.project(cfg.fmt, w[0], w[1], x, tok, ids.reshape(-1))
+
+
+@pytest.mark.parametrize("cfg", PROJ_CASES, ids=lambda c: c.name)
+def test_grouped_gemm_parity_and_chunk_invariance(cfg):
+    print(f"case {cfg.name}", flush=True)
+    logits, x, w = _inputs(cfg)
+    ids_ref, _ = oracle.route(logits, cfg.k)
+    ref = _proj_ref(cfg, w, x, ids_ref)
+    ids, _ = qgg.moe_route(torch.from_numpy(logits).to(DEV), cfg.k)
+    p, _ = qgg.expert_permute(ids, cfg.E)
+    wd = dev_weights(cfg.fmt, *w)
+    xd = dev_bf16(x)
+    inv = p.inv_perm.cpu().numpy()
+    outs = {}
+    for variant, chunk in [(qgg.FUSED, 0), (qgg.CHUNKED, cfg.chunks[0]), (qgg.CHUNKED, 1),
+                           (qgg.CHUNKED, 0)]:
+        y = qgg.dequant_grouped_gemm(wd, xd, p, cfg.T, cfg.k, variant, chunk, flags=qgg.A_TOKENS)
+        sync()
+        yh = host_u16(y)
+        assert_close(bf16_to_f64(yh[inv]), ref, what=f"{cfg.name} v{variant} c{chunk}")
+        outs[(variant, chunk)] = yh
+    base = outs[(qgg.CHUNKED, 0)]
+    for key, v in outs.items():
+        np.testing.assert_array_equal(v, base, err_msg=f"variant/chunk {key} differs")
+
+
+def test_grouped_gemm_one_hot_rows_return_weight_columns():
+    # Rows of x that are one-hot pick single weight columns, so the output is
+    # the dequantized weights themselves (exactly representable in BF16).
+    for fmt in (1, 2):
+        E, N, K, k = 4, 256, 256, 1
+        T = K
+        packed, scales = synth.qweights(3, 3, fmt, E, N, K)
+        x = np.zeros((T, K), np.uint16)
+        x[np.arange(T), np.arange(K)] = 0x3F80
+        logits = np.full((T, E), -5.0, np.float32)
+        logits[:, 2] = 5.0                                   # all rows to expert 2
+        ids, _ = qgg.moe_route(torch.from_numpy(logits).to(DEV), k)
+        p, _ = qgg.expert_permute(ids, E)
+        wd = dev_weights(fmt, packed, scales)
+        for variant in (qgg.FUSED, qgg.CHUNKED):
+            y = qgg.dequant_grouped_gemm(wd, dev_bf16(x), p, T, k, variant, 0)
+            sync()
+            got = host_u16(y)                               # row t = W[:, t]
+            ref = oracle.bf16_view(oracle.decode(fmt, packed[2], scales[2]))
+            np.testing.assert_array_equal(got, ref.T, err_msg=f"fmt {fmt} variant {variant}")
+
+
+def test_grouped_gemm_exact_integer_inputs_bit_exact():
+    # Integer x and MXFP4 weights with unit scale keep every partial sum exact
+    # in fp32, so the GPU result equals the oracle's exact value rounded to
+    # BF16, bit for bit, whatever the summation order.
+    E, N, K, T, k = 6, 256, 512, 96, 2
+    rng = np.random.default_rng(5)
+    codes = rng.integers(0, 16, (E, N, K), dtype=np.uint8)
+    packed = (codes[..., 0::2] | (codes[..., 1::2] << 4)).astype(np.uint8)
+    scales = np.full((E, N, K // 32), 127, np.uint8)
+    xi = rng.integers(-3, 4, (T, K)).astype(np.float32)
+    x = (xi.view(np.uint32) >> 16).astype(np.uint16)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    ids_ref, _ = oracle.route(logits, k)
+    ref = oracle.project(1, packed, scales, x, np.arange(T * k, dtype=np.int32) // k,
+                         ids_ref.reshape(-1))
+    ref_bits = oracle.bf16_view(ref.astype(np.float32))
+    assert np.all(ref.astype(np.float32) == ref)            # exact in fp32
+    ids, _ = qgg.moe_route(torch.from_numpy(logits).to(DEV), k)
+    p, _ = qgg.expert_permute(ids, E)
+    inv = p.inv_perm.cpu().numpy()
+    wd = dev_weights(1, packed, scales)
+    for variant in (qgg.FUSED, qgg.CHUNKED):
+        y = qgg.dequant_grouped_gemm(wd, dev_bf16(x), p, T, k, variant, 2)
+        sync()
+        np.testing.assert_array_equal(host_u16(y)[inv], ref_bits)
+
+
+@pytest.mark.parametrize("fmt", [1, 2])
+def test_transposed_grouped_gemm_parity(fmt):
+    E, N, K, T, k = 10, 384, 512, 120, 3
+    packed, scales = synth.qweights(8, 4, fmt, E, N, K)
+    logits = synth.normal_f32(8, 1, (T, E))
+    ids_ref, _ = oracle.route(logits, k)
+    pref = oracle.permute(ids_ref, E)
+    a = synth.normal_bf16(8, 5, (T * k, N))                 # sorted rows, [P][N]
+    ref = oracle.project_t(fmt, packed, scales, a, ids_ref.reshape(-1)[pref["perm"]])
+    ids, _ = qgg.moe_route(torch.from_numpy(logits).to(DEV), k)
+    p, _ = qgg.expert_permute(ids, E)
+    wd = dev_weights(fmt, packed, scales)
+    outs = []
+    for variant, chunk in [(qgg.FUSED, 0), (qgg.CHUNKED, 4), (qgg.CHUNKED, 0)]:
+        y = qgg.dequant_grouped_gemm(wd, dev_bf16(a), p, T, k, variant, chunk,
+                                     flags=qgg.A_SORTED | qgg.TRANSPOSE_W)
+        sync()
+        outs.append(host_u16(y))
+        assert_close(bf16_to_f64(outs[-1]), ref, what=f"transposed v{variant} c{chunk}")
+    for o in outs[1:]:
+        np.testing.assert_array_equal(o, outs[0])
+
+
+# ------------------------------------------------------------------- FFN
+
+FFN_CASES = [
+    scaled(CONFIGS["mxfp4_ffn_prefill"], T=96, d=256, E=16, k=4, N=256, inter=128, chunks=(3,),
+           name="mxfp4_ffn_small"),
+    scaled(CONFIGS["int4_ffn_decode_zipf"], T=64, d=512, E=48, k=8, N=512, inter=256,
+           chunks=(8,), name="int4_zipf_decode_small"),
+    scaled(CONFIGS["mxfp4_ffn_prefill"], T=300, d=256, E=8, k=2, N=256, inter=128, chunks=(4,),
+           name="mxfp4_ffn_mb4"),
+]
+
+
+def _ffn_weights(cfg):
+    return synth.configs.first_weights(cfg), synth.configs.down_weights(cfg)
+
+
+@pytest.mark.parametrize("cfg", FFN_CASES, ids=lambda c: c.name)
+def test_moe_ffn_fwd_parity(cfg):
+    print(f"case {cfg.name}", flush=True)
+    logits = synth.configs.router_logits(cfg)
+    x = synth.configs.activations(cfg)
+    gu, dn = _ffn_weights(cfg)
+    ids_ref, gates_ref = oracle.route(logits, cfg.k)
+    toks = np.arange(cfg.T, dtype=np.int32)
+    y_ref, h_ref = oracle.ffn(cfg.fmt, gu, dn, x, ids_ref, gates_ref, toks, want_h=True)
+    wg, wd = dev_weights(cfg.fmt, *gu), dev_weights(cfg.fmt, *dn)
+    lt, xd = torch.from_numpy(logits).to(DEV), dev_bf16(x)
+    outs = []
+    for variant, chunk in [(qgg.FUSED, 0), (qgg.CHUNKED, cfg.chunks[0]), (qgg.CHUNKED, 1),
+                           (qgg.CHUNKED, 0)]:
+        r = qgg.moe_ffn_fwd(wg, wd, xd, lt, cfg.k, variant, chunk, save_h=True)
+        sync()
+        np.testing.assert_array_equal(r["topk_ids"].cpu().numpy(), ids_ref)
+        inv = r["perm"].inv_perm.cpu().numpy()
+        y = host_u16(r["y"])
+        h = host_u16(r["h"])
+        assert_close(bf16_to_f64(h[inv]), h_ref, what=f"{cfg.name} h v{variant} c{chunk}")
+        assert_close(bf16_to_f64(y), y_ref, what=f"{cfg.name} y v{variant} c{chunk}")
+        outs.append((y, h))
+    for y, h in outs[1:]:
+        np.testing.assert_array_equal(y, outs[0][0])
+        np.testing.assert_array_equal(h, outs[0][1])
+
+
+DX_CASES = [
+    scaled(CONFIGS["mxfp4_dx_bwd"], T=80, d=512, E=12, k=3, N=512, inter=256, chunks=(5,),
+           name="mxfp4_dx_small"),
+    scaled(CONFIGS["mxfp4_dx_bwd"], T=256, d=256, E=4, k=2, N=512, inter=256, chunks=(3,),
+           name="mxfp4_dx_mb4"),
+    scaled(CONFIGS["int4_ffn_decode_zipf"], T=40, d=256, E=20, k=4, N=512, inter=256,
+           chunks=(6,), kind="bwd", name="int4_dx_zipf"),
+]
+
+
+@pytest.mark.parametrize("cfg", DX_CASES, ids=lambda c: c.name)
+def test_moe_dx_bwd_parity(cfg):
+    print(f"case {cfg.name}", flush=True)
+    logits = synth.configs.router_logits(cfg)
+    x = synth.configs.activations(cfg)
+    dy = synth.configs.grad_output(cfg)
+    gu, dn = _ffn_weights(cfg)
+    ids_ref, gates_ref = oracle.route(logits, cfg.k)
+    toks = np.arange(cfg.T, dtype=np.int32)
+    dx_ref, _ = oracle.dx(cfg.fmt, gu, dn, x, dy, ids_ref, gates_ref, toks)
+    wg, wd = dev_weights(cfg.fmt, *gu), dev_weights(cfg.fmt, *dn)
+    fwd = qgg.moe_ffn_fwd(wg, wd, dev_bf16(x), torch.from_numpy(logits).to(DEV), cfg.k,
+                          qgg.FUSED, 0, save_h=True)
+    outs = []
+    for variant, chunk in [(qgg.FUSED, 0), (qgg.CHUNKED, cfg.chunks[0]), (qgg.CHUNKED, 0)]:
+        dx = qgg.moe_dx_bwd(wg, wd, dev_bf16(dy), fwd["topk_gates"], fwd["perm"], fwd["h"],
+                            cfg.k, variant, chunk)
+        sync()
+        outs.append(host_u16(dx))
+        assert_close(bf16_to_f64(outs[-1]), dx_ref, what=f"{cfg.name} dx v{variant} c{chunk}")
+    for o in outs[1:]:
+        np.testing.assert_array_equal(o, outs[0])
+
+
+def test_repeat_runs_bit_identical_and_outputs_fully_written():
+    cfg = FFN_CASES[0]
+    logits = synth.configs.router_logits(cfg)
+    x = synth.configs.activations(cfg)
+    gu, dn = _ffn_weights(cfg)
+    wg, wd = dev_weights(cfg.fmt, *gu), dev_weights(cfg.fmt, *dn)
+    lt, xd = torch.from_numpy(logits).to(DEV), dev_bf16(x)
+    ws = qgg.Workspace()
+    nb, _ = qgg.workspace_bytes(qgg.CALL_FFN_FWD, cfg.T, cfg.d, cfg.E, cfg.k, cfg.inter,
+                                qgg.FUSED, 0)
+    ws.get(nb, torch.device(DEV)).fill_(0xFF)               # NaN-poison the workspace
+    r1 = qgg.moe_ffn_fwd(wg, wd, xd, lt, cfg.k, qgg.FUSED, 0, save_h=True, ws=ws)
+    r2 = qgg.moe_ffn_fwd(wg, wd, xd, lt, cfg.k, qgg.FUSED, 0, save_h=True, ws=ws)
+    sync()
+    assert torch.isfinite(r1["y"].float()).all() and torch.isfinite(r1["h"].float()).all()
+    assert torch.equal(r1["y"].view(torch.int16), r2["y"].view(torch.int16))
+    assert torch.equal(r1["h"].view(torch.int16), r2["h"].view(torch.int16))

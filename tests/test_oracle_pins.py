@@ -281,6 +281,23 @@ def test_project_matches_numpy_matmul(fmt):
                                       _f32_bits(_decode_bits(fmt, p[e], s[e])))
 
 
+@pytest.mark.parametrize("fmt", [1, 2])
+def test_project_t_matches_numpy_matmul(fmt):
+    E, N, K = 3, 64, 96
+    p, s = synth.qweights(12, 4, fmt, E, N, K)
+    a = synth.normal_bf16(12, 5, (7, N))
+    ex = np.array([0, 2, 2, 1, 0, 1, 2], np.int32)
+    y = oracle.project_t(fmt, p, s, a, ex)
+    af = oracle.bf16_to_f64(a)
+    for i in range(7):
+        W = _decode_bits(fmt, p[ex[i]], s[ex[i]]).astype(np.float64)
+        np.testing.assert_allclose(y[i], af[i] @ W, rtol=1e-12, atol=1e-12)
+    # adjoint of the forward projection: <a, W x> = <a W, x>
+    x = synth.normal_bf16(12, 6, (1, K))
+    fwd = oracle.project(fmt, p, s, x, np.zeros(1, np.int32), np.array([2], np.int32))[0]
+    assert abs(np.dot(af[1], fwd) - np.dot(y[1], oracle.bf16_to_f64(x)[0])) < 1e-10
+
+
 def test_project_one_hot_returns_weight_column():
     E, N, K = 2, 32, 64
     p, s = synth.qweights(5, 3, 1, E, N, K)
