@@ -1,0 +1,136 @@
+"""GPU parity at the full workload sizes, in the launch configuration the bench
+times.  Routing and permutation are compared in full (bit-exact); GEMM outputs
+are compared on rows the oracle computes one by one (a seeded sample that
+covers every active expert), and every chunk size must reproduce the fused
+variant bit for bit over the whole output."""
+import gc
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quantized_grouped_gemm_amd as qgg
+import synth.configs as sc
+
+from .gpu_util import DEV, assert_close, bf16_to_f64, dev_bf16, dev_weights, host_u16, sync
+
+pytestmark = [pytest.mark.gpu, pytest.mark.timeout(900)]
+
+
+def _free():
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+def _check_routing(cfg, logits, ids, perm):
+    ids_ref, gates_ref = oracle.route(logits, cfg.k)
+    np.testing.assert_array_equal(ids.cpu().numpy(), ids_ref)
+    ref = oracle.permute(ids_ref, cfg.E)
+    for name in ("counts", "offsets", "perm", "inv_perm", "active"):
+        np.testing.assert_array_equal(getattr(perm, name).cpu().numpy(), ref[name], err_msg=name)
+    assert int(perm.n_active.item()) == ref["n_active"]
+    return ids_ref, gates_ref, ref
+
+
+def test_kimi_int4_gate_up_full():
+    cfg = sc.CONFIGS["kimi_int4_gate_up"]
+    print(f"case {cfg.name}: generating inputs", flush=True)
+    logits, x = sc.router_logits(cfg), sc.activations(cfg)
+    packed, scales = sc.first_weights(cfg)
+    w = dev_weights(cfg.fmt, packed, scales)
+    xd = dev_bf16(x)
+    ids, _ = qgg.moe_route(torch.from_numpy(logits).to(DEV), cfg.k)
+    p, _ = qgg.expert_permute(ids, cfg.E)
+    y_f = qgg.dequant_grouped_gemm(w, xd, p, cfg.T, cfg.k, qgg.FUSED, 0)
+    y_c = qgg.dequant_grouped_gemm(w, xd, p, cfg.T, cfg.k, qgg.CHUNKED, cfg.chunks[0])
+    sync()
+    print("case kimi: GPU done, checking", flush=True)
+    ids_ref, _, pref = _check_routing(cfg, logits, ids, p)
+    assert torch.equal(y_f.view(torch.int16), y_c.view(torch.int16))
+    # 8 seeded rows from every active expert
+    rng = np.random.default_rng(0)
+    rows = []
+    for e in pref["active"][:pref["n_active"]]:
+        seg = np.arange(pref["offsets"][e], pref["offsets"][e + 1])
+        rows.append(rng.choice(seg, min(8, seg.size), replace=False))
+    rows = np.sort(np.concatenate(rows))
+    pairs = pref["perm"][rows]
+    ref = oracle.project(cfg.fmt, packed, scales, x, (pairs // cfg.k).astype(np.int32),
+                         ids_ref.reshape(-1)[pairs])
+    got = host_u16(y_f[torch.from_numpy(rows).to(DEV)])
+    e = assert_close(bf16_to_f64(got), ref, what="kimi int4 gate_up")
+    print(f"case kimi: {rows.size} rows checked, max rel err {e:.2e}", flush=True)
+    del w, xd, y_f, y_c, packed, scales
+    _free()
+
+
+_FFN_CACHE = {}
+
+
+def _ffn_inputs(cfg):
+    key = (cfg.T, cfg.d, cfg.E, cfg.k, cfg.inter, cfg.fmt, cfg.seed, cfg.zipf_s)
+    if key not in _FFN_CACHE:
+        _FFN_CACHE.clear()
+        _FFN_CACHE[key] = (sc.router_logits(cfg), sc.activations(cfg), sc.first_weights(cfg),
+                           sc.down_weights(cfg))
+    return _FFN_CACHE[key]
+
+
+@pytest.mark.parametrize("name", ["mxfp4_ffn_prefill", "int4_ffn_decode_zipf"])
+def test_moe_ffn_fwd_full(name):
+    cfg = sc.CONFIGS[name]
+    print(f"case {cfg.name}: generating inputs", flush=True)
+    logits, x, gu, dn = _ffn_inputs(cfg)
+    wg, wd = dev_weights(cfg.fmt, *gu), dev_weights(cfg.fmt, *dn)
+    xd, lt = dev_bf16(x), torch.from_numpy(logits).to(DEV)
+    r = qgg.moe_ffn_fwd(wg, wd, xd, lt, cfg.k, qgg.FUSED, 0, save_h=True)
+    sync()
+    y0, h0 = host_u16(r["y"]), host_u16(r["h"])
+    for chunk in cfg.chunks:
+        rc = qgg.moe_ffn_fwd(wg, wd, xd, lt, cfg.k, qgg.CHUNKED, chunk, save_h=True)
+        sync()
+        np.testing.assert_array_equal(host_u16(rc["y"]), y0, err_msg=f"chunk {chunk}")
+        np.testing.assert_array_equal(host_u16(rc["h"]), h0, err_msg=f"chunk {chunk}")
+        del rc
+    print(f"case {cfg.name}: GPU done, checking", flush=True)
+    ids_ref, gates_ref, pref = _check_routing(cfg, logits, r["topk_ids"], r["perm"])
+    n_tok = cfg.T if cfg.T <= 64 else 48
+    toks = np.sort(np.random.default_rng(1).choice(cfg.T, n_tok, replace=False)).astype(np.int32)
+    y_ref, h_ref = oracle.ffn(cfg.fmt, gu, dn, x, ids_ref, gates_ref, toks, want_h=True)
+    e = assert_close(bf16_to_f64(y0[toks]), y_ref, what=f"{cfg.name} y")
+    slots = (toks[:, None] * cfg.k + np.arange(cfg.k)[None, :]).reshape(-1)
+    assert_close(bf16_to_f64(h0[pref["inv_perm"][slots]]), h_ref, what=f"{cfg.name} h")
+    print(f"case {cfg.name}: {n_tok} tokens checked, n_active {pref['n_active']}, "
+          f"max rel err {e:.2e}", flush=True)
+    del wg, wd, xd, lt, r
+    _free()
+
+
+def test_moe_dx_bwd_full():
+    cfg = sc.CONFIGS["mxfp4_dx_bwd"]
+    print(f"case {cfg.name}: generating inputs", flush=True)
+    logits, x, gu, dn = _ffn_inputs(cfg)
+    dy = sc.grad_output(cfg)
+    wg, wd = dev_weights(cfg.fmt, *gu), dev_weights(cfg.fmt, *dn)
+    fwd = qgg.moe_ffn_fwd(wg, wd, dev_bf16(x), torch.from_numpy(logits).to(DEV), cfg.k,
+                          qgg.FUSED, 0, save_h=True)
+    dyd = dev_bf16(dy)
+    dx0 = host_u16(qgg.moe_dx_bwd(wg, wd, dyd, fwd["topk_gates"], fwd["perm"], fwd["h"], cfg.k,
+                                  qgg.FUSED, 0))
+    for chunk in cfg.chunks:
+        dxc = qgg.moe_dx_bwd(wg, wd, dyd, fwd["topk_gates"], fwd["perm"], fwd["h"], cfg.k,
+                             qgg.CHUNKED, chunk)
+        sync()
+        np.testing.assert_array_equal(host_u16(dxc), dx0, err_msg=f"chunk {chunk}")
+        del dxc
+        _free()
+    print("case dx: GPU done, checking", flush=True)
+    ids_ref, gates_ref, _ = _check_routing(cfg, logits, fwd["topk_ids"], fwd["perm"])
+    toks = np.sort(np.random.default_rng(2).choice(cfg.T, 32, replace=False)).astype(np.int32)
+    dx_ref, _ = oracle.dx(cfg.fmt, gu, dn, x, dy, ids_ref, gates_ref, toks)
+    e = assert_close(bf16_to_f64(dx0[toks]), dx_ref, what="dx")
+    print(f"case dx: 32 tokens checked, max rel err {e:.2e}", flush=True)
+    del wg, wd, fwd, dyd
+    _FFN_CACHE.clear()
+    _free()
