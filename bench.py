@@ -121,8 +121,22 @@ def run(args):
             ev[1].record(stream)
         return p
 
+    if args.calib_copy_mib > 0:
+        # a plain device copy of known size, so that a counter run over this
+        # command can scale FETCH_SIZE / WRITE_SIZE to bytes
+        n = args.calib_copy_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     results = {}
-    for vname, variant, chunk in (("fused", qgg.FUSED, 0), ("chunked", qgg.CHUNKED, cfg.chunks[0])):
+    variants = [("fused", qgg.FUSED, 0), ("chunked", qgg.CHUNKED, cfg.chunks[0])]
+    if args.fused_only:
+        variants = variants[:1]
+    for vname, variant, chunk in variants:
         for _ in range(args.warmup):
             p = step(variant, chunk)
         torch.cuda.synchronize()
@@ -206,6 +220,9 @@ def main():
     ap.add_argument("--config", default="kimi_int4_gate_up")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="run a plain device copy of this size first (counter calibration)")
+    ap.add_argument("--fused-only", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this path runs on a single MI355X "
