@@ -124,11 +124,12 @@ def run(args):
     if args.calib_copy_mib > 0:
         # a plain device copy of known size, so that a counter run over this
         # command can scale FETCH_SIZE / WRITE_SIZE to bytes
+        # (an elementwise add: reads n bytes, writes n bytes, one kernel)
         n = args.calib_copy_mib << 20
-        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        src = torch.empty(n // 4, dtype=torch.float32, device=dev).fill_(1.0)
         dst = torch.empty_like(src)
         for _ in range(3):
-            dst.copy_(src)
+            torch.add(src, 1.0, out=dst)
         torch.cuda.synchronize()
         del src, dst
 

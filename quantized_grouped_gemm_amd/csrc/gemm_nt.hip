@@ -25,6 +25,8 @@
 #include "qgg_device.hpp"
 #include "qgg_internal.hpp"
 
+#include <type_traits>
+
 namespace qgg {
 
 namespace {
@@ -32,6 +34,9 @@ namespace {
 constexpr int kKL = 128;                 // K elements per LDS stage
 constexpr int kRowB = kKL * 2 + 16;      // padded LDS bytes per A row
 constexpr int kCPR = kKL * 2 / 16;       // 16-byte chunks per row per stage
+// weight steps in flight per wavefront (BF16 steps are 4x larger)
+template <int SRC>
+constexpr int ring_depth() { return SRC == kSrcBF16 ? 2 : 4; }
 
 __device__ __forceinline__ uint16_t bf16_hw(float v) {
   return __builtin_bit_cast(uint16_t, (__bf16)v);
@@ -40,7 +45,8 @@ __device__ __forceinline__ uint16_t bf16_hw(float v) {
 template <int SRC>
 struct BRegs {
   u32x4_t w[SRC == kSrcBF16 ? 4 : 1];
-  float s, neg8s;
+  uint32_t sraw;   // raw scale bits; converted only when decoding, so a
+                   // refill never waits for its own load
 };
 
 template <int SRC>
@@ -52,41 +58,247 @@ __device__ __forceinline__ void load_b(const GemmArgs& g, const uint8_t* wp, con
     for (int s = 0; s < 4; ++s) r.w[s] = src[s];
   } else {
     r.w[0] = *reinterpret_cast<const u32x4_t*>(wp + group * 16);
-    if constexpr (SRC == kSrcMXFP4) {
-      r.s = e8m0_to_f32(sp[group]);
-    } else {
-      r.s = bf16_to_f32(reinterpret_cast<const uint16_t*>(sp)[group]);
-      r.neg8s = -8.0f * r.s;
-    }
+    if constexpr (SRC == kSrcMXFP4) r.sraw = sp[group];
+    else r.sraw = reinterpret_cast<const uint16_t*>(sp)[group];
   }
+}
+
+// Scale of a loaded group in the form the decoder takes.
+template <int SRC>
+struct BScale {
+  float s, neg8s;
+};
+
+template <int SRC>
+__device__ __forceinline__ BScale<SRC> b_scale(const BRegs<SRC>& r) {
+  BScale<SRC> o{0.f, 0.f};
+  if constexpr (SRC == kSrcMXFP4) {
+    o.s = e8m0_to_f32(r.sraw);
+  } else if constexpr (SRC == kSrcINT4) {
+    o.s = bf16_to_f32(r.sraw);
+    o.neg8s = -8.0f * o.s;
+  }
+  return o;
 }
 
 // MFMA B operand for K step s (8 elements) of a loaded group.
 template <int SRC>
-__device__ __forceinline__ bf16x8_t b_operand(const BRegs<SRC>& r, int s) {
+__device__ __forceinline__ bf16x8_t b_operand(const BRegs<SRC>& r, const BScale<SRC>& sc, int s) {
   uint32_t o[4];
   if constexpr (SRC == kSrcBF16) {
     return __builtin_bit_cast(bf16x8_t, r.w[s]);
   } else if constexpr (SRC == kSrcMXFP4) {
-    dq8_mxfp4(r.w[0][s], r.s, o);
+    dq8_mxfp4(r.w[0][s], sc.s, o);
   } else {
-    dq8_int4(r.w[0][s], r.s, r.neg8s, o);
+    dq8_int4(r.w[0][s], sc.s, sc.neg8s, o);
   }
   u32x4_t v = {o[0], o[1], o[2], o[3]};
   return __builtin_bit_cast(bf16x8_t, v);
 }
 
-template <int SRC, int MB, int EPI, int AMODE>
-__global__ __launch_bounds__(256, MB == 4 ? 1 : 2) void k_gemm_nt(GemmArgs g) {
+// One work item: tile (expert, rows [row0, row0 + nrows)) x 256 output
+// columns, with NMB live 32-row blocks.  The K loop is branch-free: every
+// load index is clamped into range instead of guarded, so the compiler can
+// keep exact vmcnt counts and the weight ring stays in flight across the
+// workgroup barriers.
+template <int SRC, int MB, int EPI, int AMODE, int NMB>
+__device__ __forceinline__ void gemm_nt_item(const GemmArgs& g, uint8_t (*As)[32 * MB * kRowB],
+                                             int4 tile, int nt) {
   constexpr int MT = 32 * MB;
   constexpr int NCH = MT * kCPR / 256;   // A chunks per thread per stage
-  __shared__ __attribute__((aligned(16))) uint8_t As[2][MT * kRowB];
-
+  constexpr int kRing = ring_depth<SRC>();
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
   const int col = lane & 31;
   const int half = lane >> 5;
+  const int nstages = g.K / kKL;
+  const int nsteps = nstages * 2;
+  const int64_t rowbytes = g.K / 2;
+  const int64_t rowscales = g.K / 32;
+  const int expert = tile.x, row0 = tile.y, nrows = tile.z;
+
+  // A sources and LDS destinations of this thread's 16-byte chunks
+  const uint16_t* asrc[NCH];
+  int adst[NCH];
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) {
+    const int c = tid + 256 * i;
+    const int r = c / kCPR;
+    const int cc = c % kCPR;
+    const int rr = r < nrows ? r : 0;
+    int64_t srow;
+    if constexpr (AMODE == kATokens) srow = g.perm[row0 + rr] / g.topk;
+    else srow = row0 + rr;
+    asrc[i] = g.a + srow * g.lda + cc * 8;
+    adst[i] = r * kRowB + cc * 16;
+  }
+
+  // this wave's two 32-column blocks (W rows); a wave past the matrix edge
+  // computes on clamped rows and stores nothing
+  int wrow0, wrow1, ocol;
+  bool active;
+  if constexpr (EPI == kEpiSwiGLU) {
+    const int base = nt * 128 + wave * 32;
+    active = base < g.inter;
+    ocol = active ? base + col : g.inter - 32 + col;
+    wrow0 = ocol;
+    wrow1 = g.inter + ocol;
+  } else {
+    const int base = nt * 256 + wave * 64;
+    active = base < g.N;
+    ocol = active ? base + col : g.N - 64 + col;
+    wrow0 = ocol;
+    wrow1 = ocol + 32;
+  }
+  const uint8_t *wp0 = nullptr, *wp1 = nullptr, *sp0 = nullptr, *sp1 = nullptr;
+  const uint16_t *wb0 = nullptr, *wb1 = nullptr;
+  if constexpr (SRC == kSrcBF16) {
+    const int64_t slot = tile.w - g.bf16_slot_base;
+    wb0 = g.wbf16 + (slot * g.N + wrow0) * (int64_t)g.K;
+    wb1 = g.wbf16 + (slot * g.N + wrow1) * (int64_t)g.K;
+  } else {
+    const int sb = SRC == kSrcMXFP4 ? 1 : 2;
+    wp0 = g.packed + ((int64_t)expert * g.N + wrow0) * rowbytes;
+    wp1 = g.packed + ((int64_t)expert * g.N + wrow1) * rowbytes;
+    sp0 = static_cast<const uint8_t*>(g.scales) + ((int64_t)expert * g.N + wrow0) * rowscales * sb;
+    sp1 = static_cast<const uint8_t*>(g.scales) + ((int64_t)expert * g.N + wrow1) * rowscales * sb;
+  }
+
+  f32x16_t acc[NMB][2];
+#pragma unroll
+  for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[mb][nb][i] = 0.f;
+
+  // Weight stream: a ring of kRing 64-wide K steps held in registers.  A
+  // slot is refilled with the step kRing ahead as soon as its last operand
+  // is decoded, so the loads run kRing steps ahead of use.
+  BRegs<SRC> ring[kRing][2];
+#pragma unroll
+  for (int r = 0; r < kRing; ++r) {
+    const int st = r < nsteps ? r : nsteps - 1;
+    load_b<SRC>(g, wp0, sp0, wb0, st * 2 + half, ring[r][0]);
+    load_b<SRC>(g, wp1, sp1, wb1, st * 2 + half, ring[r][1]);
+  }
+  u32x4_t areg[NCH];
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) areg[i] = *reinterpret_cast<const u32x4_t*>(asrc[i]);
+#pragma unroll
+  for (int i = 0; i < NCH; ++i) *reinterpret_cast<u32x4_t*>(&As[0][adst[i]]) = areg[i];
+  __syncthreads();
+
+  // one 64-wide K step; SUB = step parity (two steps per LDS stage), BUF =
+  // the LDS buffer of the step's stage; both are compile-time here
+  auto kstep = [&](int step, BRegs<SRC>(&slot)[2], auto sub_c, auto buf_c) {
+    constexpr int SUB = decltype(sub_c)::value;
+    constexpr int BUF = decltype(buf_c)::value;
+    const int st = step >> 1;
+    if constexpr (SUB == 0) {
+      const int nx = st + 1 < nstages ? st + 1 : st;
+#pragma unroll
+      for (int i = 0; i < NCH; ++i)
+        areg[i] = *reinterpret_cast<const u32x4_t*>(asrc[i] + nx * kKL);
+    }
+    const BScale<SRC> sc0 = b_scale<SRC>(slot[0]);
+    const BScale<SRC> sc1 = b_scale<SRC>(slot[1]);
+    // A operands double-buffered across the four K sub-steps
+    bf16x8_t acur[NMB], anxt[NMB];
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb)
+      acur[mb] = *reinterpret_cast<const bf16x8_t*>(
+          &As[BUF][(mb * 32 + col) * kRowB + (SUB * 64 + half * 32) * 2]);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      if (s < 3) {
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb)
+          anxt[mb] = *reinterpret_cast<const bf16x8_t*>(
+              &As[BUF][(mb * 32 + col) * kRowB + (SUB * 64 + half * 32 + (s + 1) * 8) * 2]);
+      }
+      const bf16x8_t b0 = b_operand<SRC>(slot[0], sc0, s);
+      const bf16x8_t b1 = b_operand<SRC>(slot[1], sc1, s);
+      if (s == 3) {
+        const int nx = step + kRing < nsteps ? step + kRing : nsteps - 1;
+        load_b<SRC>(g, wp0, sp0, wb0, nx * 2 + half, slot[0]);
+        load_b<SRC>(g, wp1, sp1, wb1, nx * 2 + half, slot[1]);
+      }
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb) {
+        acc[mb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(acur[mb], b0, acc[mb][0], 0, 0, 0);
+        acc[mb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(acur[mb], b1, acc[mb][1], 0, 0, 0);
+      }
+      if (s < 3) {
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb) acur[mb] = anxt[mb];
+      }
+    }
+    if constexpr (SUB == 1) {
+#pragma unroll
+      for (int i = 0; i < NCH; ++i) *reinterpret_cast<u32x4_t*>(&As[BUF ^ 1][adst[i]]) = areg[i];
+      __syncthreads();
+    }
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+
+  int base = 0;
+  if constexpr (kRing == 4) {
+    for (; base + 4 <= nsteps; base += 4) {
+      kstep(base + 0, ring[0], I0{}, I0{});
+      kstep(base + 1, ring[1], I1{}, I0{});
+      kstep(base + 2, ring[2], I0{}, I1{});
+      kstep(base + 3, ring[3], I1{}, I1{});
+    }
+    if (base < nsteps) {                 // one stage left
+      kstep(base + 0, ring[0], I0{}, I0{});
+      kstep(base + 1, ring[1], I1{}, I0{});
+    }
+  } else {
+    for (; base < nsteps; base += 4) {   // kRing == 2: slots alternate per step
+      kstep(base + 0, ring[0], I0{}, I0{});
+      kstep(base + 1, ring[1], I1{}, I0{});
+      if (base + 2 < nsteps) {
+        kstep(base + 2, ring[0], I0{}, I1{});
+        kstep(base + 3, ring[1], I1{}, I1{});
+      }
+    }
+  }
+
+  if (!active) return;
+  // epilogue: lane holds column `col` of rows 8i + 4*half + j of each block
+#pragma unroll
+  for (int mb = 0; mb < NMB; ++mb) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = mb * 32 + 8 * i + 4 * half + j;
+        if (r < nrows) {
+          const int64_t orow = row0 + r;
+          const float v0 = acc[mb][0][i * 4 + j];
+          const float v1 = acc[mb][1][i * 4 + j];
+          if constexpr (EPI == kEpiSwiGLU) {
+            g.y[orow * g.ldy + ocol] = bf16_hw(silu_f32(v0) * v1);
+            if (g.h) {
+              g.h[orow * 2 * g.inter + ocol] = bf16_hw(v0);
+              g.h[orow * 2 * g.inter + g.inter + ocol] = bf16_hw(v1);
+            }
+          } else {
+            g.y[orow * g.ldy + wrow0] = bf16_hw(v0);
+            g.y[orow * g.ldy + wrow1] = bf16_hw(v1);
+          }
+        }
+      }
+    }
+  }
+}
+
+template <int SRC, int MB, int EPI, int AMODE>
+__global__ __launch_bounds__(256, MB == 4 ? 1 : 2) void k_gemm_nt(GemmArgs g) {
+  __shared__ __attribute__((aligned(16))) uint8_t As[2][32 * MB * kRowB];
   const int t_begin = g.range[0];
   const int t_end = g.range[1];
   const int n_tiles_n = EPI == kEpiSwiGLU ? (g.inter + 127) / 128 : (g.N + 255) / 256;
@@ -95,149 +307,18 @@ __global__ __launch_bounds__(256, MB == 4 ? 1 : 2) void k_gemm_nt(GemmArgs g) {
   const int xcd = blockIdx.x & 7;
   const int span = (items + 7) >> 3;
   const int q_end = min(items, (xcd + 1) * span);
-  const int nstages = g.K / kKL;
-  const int64_t rowbytes = g.K / 2;
-  const int64_t rowscales = g.K / 32;
-
   for (int q = xcd * span + (blockIdx.x >> 3); q < q_end; q += per_xcd) {
     const int4 tile = g.tiles[t_begin + q / n_tiles_n];
     const int nt = q % n_tiles_n;
-    const int expert = tile.x, row0 = tile.y, nrows = tile.z;
-
-    // A sources and LDS destinations of this thread's 16-byte chunks
-    const uint16_t* asrc[NCH];
-    int adst[NCH];
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) {
-      const int c = tid + 256 * i;
-      const int r = c / kCPR;
-      const int cc = c % kCPR;
-      const int rr = r < nrows ? r : 0;
-      int64_t srow;
-      if constexpr (AMODE == kATokens) srow = g.perm[row0 + rr] / g.topk;
-      else srow = row0 + rr;
-      asrc[i] = g.a + srow * g.lda + cc * 8;
-      adst[i] = r * kRowB + cc * 16;
-    }
-
-    // this wave's two 32-column blocks (W rows)
-    int wrow0, wrow1;
-    bool active;
-    if constexpr (EPI == kEpiSwiGLU) {
-      const int base = nt * 128 + wave * 32;
-      active = base < g.inter;
-      wrow0 = base + col;
-      wrow1 = g.inter + base + col;
+    const int nmb = (tile.z + 31) / 32;
+    if (MB == 1 || nmb <= 1) {
+      gemm_nt_item<SRC, MB, EPI, AMODE, 1>(g, As, tile, nt);
+    } else if (MB == 2 || nmb == 2) {
+      gemm_nt_item<SRC, MB, EPI, AMODE, (MB >= 2 ? 2 : 1)>(g, As, tile, nt);
+    } else if (nmb == 3) {
+      gemm_nt_item<SRC, MB, EPI, AMODE, (MB >= 4 ? 3 : 1)>(g, As, tile, nt);
     } else {
-      const int base = nt * 256 + wave * 64;
-      active = base < g.N;
-      wrow0 = base + col;
-      wrow1 = base + 32 + col;
-    }
-    const uint8_t *wp0 = nullptr, *wp1 = nullptr, *sp0 = nullptr, *sp1 = nullptr;
-    const uint16_t *wb0 = nullptr, *wb1 = nullptr;
-    if constexpr (SRC == kSrcBF16) {
-      const int64_t slot = tile.w - g.bf16_slot_base;
-      wb0 = g.wbf16 + (slot * g.N + wrow0) * (int64_t)g.K;
-      wb1 = g.wbf16 + (slot * g.N + wrow1) * (int64_t)g.K;
-    } else {
-      const int sb = SRC == kSrcMXFP4 ? 1 : 2;
-      wp0 = g.packed + ((int64_t)expert * g.N + wrow0) * rowbytes;
-      wp1 = g.packed + ((int64_t)expert * g.N + wrow1) * rowbytes;
-      sp0 = static_cast<const uint8_t*>(g.scales) + ((int64_t)expert * g.N + wrow0) * rowscales * sb;
-      sp1 = static_cast<const uint8_t*>(g.scales) + ((int64_t)expert * g.N + wrow1) * rowscales * sb;
-    }
-
-    f32x16_t acc[MB][2];
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[mb][nb][i] = 0.f;
-      }
-    }
-
-    BRegs<SRC> bcur0, bcur1, bnxt0, bnxt1;
-    if (active) {
-      load_b<SRC>(g, wp0, sp0, wb0, half, bcur0);
-      load_b<SRC>(g, wp1, sp1, wb1, half, bcur1);
-    }
-    u32x4_t areg[NCH];
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) areg[i] = *reinterpret_cast<const u32x4_t*>(asrc[i]);
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) *reinterpret_cast<u32x4_t*>(&As[0][adst[i]]) = areg[i];
-    __syncthreads();
-
-    for (int st = 0; st < nstages; ++st) {
-      const int buf = st & 1;
-      if (st + 1 < nstages) {
-#pragma unroll
-        for (int i = 0; i < NCH; ++i)
-          areg[i] = *reinterpret_cast<const u32x4_t*>(asrc[i] + (st + 1) * kKL);
-      }
-#pragma unroll
-      for (int sub = 0; sub < 2; ++sub) {
-        const int step = st * 2 + sub;  // 64-wide K step
-        if (active) {
-          if (step + 1 < nstages * 2) {
-            load_b<SRC>(g, wp0, sp0, wb0, (step + 1) * 2 + half, bnxt0);
-            load_b<SRC>(g, wp1, sp1, wb1, (step + 1) * 2 + half, bnxt1);
-          }
-#pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            const bf16x8_t b0 = b_operand<SRC>(bcur0, s);
-            const bf16x8_t b1 = b_operand<SRC>(bcur1, s);
-#pragma unroll
-            for (int mb = 0; mb < MB; ++mb) {
-              if (mb * 32 < nrows) {
-                const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(
-                    &As[buf][(mb * 32 + col) * kRowB + (sub * 64 + half * 32 + s * 8) * 2]);
-                acc[mb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b0, acc[mb][0], 0, 0, 0);
-                acc[mb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b1, acc[mb][1], 0, 0, 0);
-              }
-            }
-          }
-          bcur0 = bnxt0;
-          bcur1 = bnxt1;
-        }
-      }
-      if (st + 1 < nstages) {
-#pragma unroll
-        for (int i = 0; i < NCH; ++i)
-          *reinterpret_cast<u32x4_t*>(&As[buf ^ 1][adst[i]]) = areg[i];
-      }
-      __syncthreads();
-    }
-
-    if (!active) continue;
-    // epilogue: lane holds column `col` of rows 8i + 4*half + j of each block
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
-      if (mb * 32 >= nrows) continue;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int r = mb * 32 + 8 * i + 4 * half + j;
-          if (r >= nrows) continue;
-          const int64_t orow = row0 + r;
-          const float v0 = acc[mb][0][i * 4 + j];
-          const float v1 = acc[mb][1][i * 4 + j];
-          if constexpr (EPI == kEpiSwiGLU) {
-            const int c = wrow0;  // gate column in [0, inter)
-            g.y[orow * g.ldy + c] = bf16_hw(silu_f32(v0) * v1);
-            if (g.h) {
-              g.h[orow * 2 * g.inter + c] = bf16_hw(v0);
-              g.h[orow * 2 * g.inter + g.inter + c] = bf16_hw(v1);
-            }
-          } else {
-            g.y[orow * g.ldy + wrow0] = bf16_hw(v0);
-            g.y[orow * g.ldy + wrow1] = bf16_hw(v1);
-          }
-        }
-      }
+      gemm_nt_item<SRC, MB, EPI, AMODE, (MB >= 4 ? 4 : 1)>(g, As, tile, nt);
     }
   }
 }
