@@ -104,7 +104,10 @@ def run(args):
     pd = torch.from_numpy(packed).to(dev)
     sd = torch.from_numpy(scales.view(np.int16) if scales.dtype == np.uint16 else scales).to(dev)
     del packed, scales
-    w = qgg.QWeight(cfg.fmt, pd, sd)
+    # the frozen base is stored in the MFMA-tiled order (one repack at load)
+    w = qgg.repack(qgg.QWeight(cfg.fmt, pd, sd))
+    del pd, sd
+    torch.cuda.synchronize()
     P = cfg.P
     ws = qgg.Workspace()
     y = torch.empty((P, cfg.N), dtype=torch.bfloat16, device=dev)
@@ -189,7 +192,7 @@ def run(args):
         "data": "synthetic",
         "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "E": cfg.E, "top_k": cfg.k,
                    "N": cfg.N, "weights": cfg.fmt_name + " group-32", "chunk": cfg.chunks[0],
-                   "variant": "fused", "seed": cfg.seed},
+                   "variant": "fused", "weight_layout": "mfma-tiled", "seed": cfg.seed},
         "roofline": {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
                      "frac": round(achieved / peak, 4), "traffic": measured_traffic(),
                      "kernel": DOMINANT_KERNEL, "kernel_ms": round(fused["gemm_ms"], 4),

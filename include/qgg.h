@@ -76,16 +76,31 @@ typedef int qgg_status;
 #define QGG_CALL_FFN_FWD 3
 #define QGG_CALL_DX_BWD 4
 
+/* Storage layouts of the packed weights and scales (the bytes are the same,
+ * only their order differs):
+ * QGG_LAYOUT_ROWS  packed [E][N][K/2]: element k of a row is byte k>>1, low
+ *                  nibble for even k; scales [E][N][K/32].
+ * QGG_LAYOUT_MFMA  tiles of 32 rows x 64 K: packed [E][N/32][K/64][64][16]
+ *                  where slot L = 32*h + c holds the 16 bytes of scale group
+ *                  2*j + h of row 32*cb + c (tile (cb, j)), nibble order as
+ *                  in a row; scales [E][N/32][K/64][64] in the same slot
+ *                  order.  One wavefront reads one K step of 32 rows as a
+ *                  single contiguous 1 KiB block.  Produced from ROWS by
+ *                  qgg_repack_weights (once, when the frozen base is
+ *                  loaded); needs N % 32 == 0 and K % 64 == 0. */
+#define QGG_LAYOUT_ROWS 0
+#define QGG_LAYOUT_MFMA 1
+
 /* A frozen 4-bit weight tensor of E experts, each [N][K] (out x in).
- * packed: [E][N][K/2] bytes; element k of a row is byte k>>1, low nibble for
- *         even k.  scales: [E][N][K/32], uint8 E8M0 codes (value 2^(c-127),
- *         255 = NaN) for MXFP4, uint16 BF16 bits for INT4.  Host struct,
- *         device pointers, read only. */
+ * scales hold uint8 E8M0 codes (value 2^(c-127), 255 = NaN) for MXFP4 and
+ * uint16 BF16 bits for INT4, in the order `layout` names.  Host struct,
+ * device pointers, read only. */
 typedef struct {
   int32_t fmt;
   int32_t E, N, K;
   const uint8_t* packed;
   const void* scales;
+  int32_t layout;
 } qgg_qweight;
 
 /* Routing permutation, all device arrays written by expert_permute.
@@ -158,6 +173,13 @@ qgg_status moe_dx_bwd(const qgg_qweight* w_gate_up, const qgg_qweight* w_down,
                       const uint16_t* h_saved, int T, int d, int E, int k, int inter, int variant,
                       int chunk, void* workspace, size_t ws_bytes, uint16_t* dx,
                       qgg_stream_t stream);
+
+/* qgg_repack_weights -- copy a QGG_LAYOUT_ROWS weight tensor into the
+ * QGG_LAYOUT_MFMA order: packed_out gets E*N*K/2 bytes, scales_out E*N*K/32
+ * scale entries (device buffers the caller owns, not aliasing the source).
+ * A pure permutation of bytes and scale entries; values are untouched. */
+qgg_status qgg_repack_weights(const qgg_qweight* src, uint8_t* packed_out, void* scales_out,
+                              qgg_stream_t stream);
 
 /* Workspace bytes a call needs.  N_or_inter is N for QGG_CALL_GEMM (with K =
  * d) and inter for the FFN calls.  *scratch_bytes (nullable) receives the part

@@ -21,6 +21,8 @@ LIB_PATH = os.path.join(_HERE, "libqgg.so")
 
 FMT_MXFP4 = 1
 FMT_INT4 = 2
+LAYOUT_ROWS = 0
+LAYOUT_MFMA = 1
 CHUNKED = 0
 FUSED = 1
 A_SORTED = 0
@@ -36,7 +38,7 @@ STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too sm
 
 # Every symbol include/qgg.h declares.
 EXPORTS = ("moe_route", "expert_permute", "dequant_grouped_gemm", "moe_ffn_fwd", "moe_dx_bwd",
-           "qgg_workspace_bytes", "qgg_status_string", "qgg_version")
+           "qgg_repack_weights", "qgg_workspace_bytes", "qgg_status_string", "qgg_version")
 
 _lib = None
 
@@ -47,7 +49,8 @@ class QggError(RuntimeError):
 
 class _QWeight(ctypes.Structure):
     _fields_ = [("fmt", ctypes.c_int32), ("E", ctypes.c_int32), ("N", ctypes.c_int32),
-                ("K", ctypes.c_int32), ("packed", ctypes.c_void_p), ("scales", ctypes.c_void_p)]
+                ("K", ctypes.c_int32), ("packed", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("layout", ctypes.c_int32)]
 
 
 class _Perm(ctypes.Structure):
@@ -74,6 +77,8 @@ def lib():
         L.moe_dx_bwd.argtypes = [ctypes.POINTER(_QWeight), ctypes.POINTER(_QWeight), P, P,
                                  ctypes.POINTER(_Perm), P, i32, i32, i32, i32, i32, i32, i32, P,
                                  sz, P, P]
+        L.qgg_repack_weights.argtypes = [ctypes.POINTER(_QWeight), P, P, P]
+        L.qgg_repack_weights.restype = ctypes.c_int
         L.qgg_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32,
                                           ctypes.POINTER(ctypes.c_size_t)]
         L.qgg_workspace_bytes.restype = ctypes.c_size_t
@@ -103,27 +108,47 @@ def _stream():
 
 @dataclass
 class QWeight:
-    """Frozen 4-bit expert weights on the device: packed [E][N][K/2] uint8 and
-    scales [E][N][K/32] (uint8 E8M0 for MXFP4, BF16 bits for INT4)."""
+    """Frozen 4-bit expert weights on the device: packed bytes and scales
+    (uint8 E8M0 for MXFP4, BF16 bits for INT4) of E experts of [N][K], in
+    LAYOUT_ROWS ([E][N][K/2], [E][N][K/32]) or LAYOUT_MFMA order (same sizes,
+    see include/qgg.h).  Shapes are given by E, N, K."""
     fmt: int
     packed: "object"
     scales: "object"
+    layout: int = LAYOUT_ROWS
+    shape: tuple = None
+
+    def __post_init__(self):
+        if self.shape is None:
+            self.shape = (self.packed.shape[0], self.packed.shape[1], self.packed.shape[2] * 2)
 
     @property
     def E(self):
-        return self.packed.shape[0]
+        return self.shape[0]
 
     @property
     def N(self):
-        return self.packed.shape[1]
+        return self.shape[1]
 
     @property
     def K(self):
-        return self.packed.shape[2] * 2
+        return self.shape[2]
 
     def c(self):
         return _QWeight(self.fmt, self.E, self.N, self.K, self.packed.data_ptr(),
-                        self.scales.data_ptr())
+                        self.scales.data_ptr(), self.layout)
+
+
+def repack(w: "QWeight") -> "QWeight":
+    """The MFMA-tiled copy of row-layout weights (qgg_repack_weights)."""
+    import torch
+    assert w.layout == LAYOUT_ROWS
+    p = torch.empty_like(w.packed)
+    s = torch.empty_like(w.scales)
+    wc = w.c()
+    _check(lib().qgg_repack_weights(ctypes.byref(wc), _ptr(p), _ptr(s), _stream()),
+           "qgg_repack_weights")
+    return QWeight(w.fmt, p, s, LAYOUT_MFMA, w.shape)
 
 
 @dataclass

@@ -17,16 +17,28 @@ namespace {
 __constant__ float kE2M1Val[16] = {0.0f,  0.5f,  1.0f,  1.5f,  2.0f,  3.0f,  4.0f,  6.0f,
                                    -0.0f, -0.5f, -1.0f, -1.5f, -2.0f, -3.0f, -4.0f, -6.0f};
 
+// Offset, in 16-byte units (and in scale entries), of scale group g of row n
+// of expert e: rows layout, or the MFMA-tiled layout (tiles of 32 rows x 64
+// K, slot 32 * (g % 2) + n % 32).
+__device__ __forceinline__ int64_t group_index(int layout, int64_t e, int64_t n, int64_t g,
+                                               int N, int K) {
+  if (layout == 1)
+    return ((e * (N / 32) + (n >> 5)) * (K / 64) + (g >> 1)) * 64 + (g & 1) * 32 + (n & 31);
+  return (e * N + n) * (K / 32) + g;
+}
+
 // One thread per 32-element group: 16 packed bytes + 1 scale -> 64 bytes of
 // BF16.  The product code value x scale is formed in fp32 (exact unless it
 // overflows) and rounded to BF16 to nearest even; an E8M0 code of 255 (NaN)
-// yields the quiet NaN 0x7FC0 for the whole group.
+// yields the quiet NaN 0x7FC0 for the whole group.  Output row-major
+// [slot][N][K], or MFMA-tiled BF16 (see launch_dequant).
 template <int FMT>
 __global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ packed,
-                                                 const void* __restrict__ scales, int N, int K,
-                                                 const int32_t* __restrict__ active,
+                                                 const void* __restrict__ scales, int layout,
+                                                 int N, int K, const int32_t* __restrict__ active,
                                                  const int32_t* __restrict__ n_active, int first,
-                                                 int count, uint16_t* __restrict__ dst) {
+                                                 int count, int tiled_out,
+                                                 uint16_t* __restrict__ dst) {
   const int64_t groups_per_expert = (int64_t)N * (K / 32);
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int slot = (int)(gid / groups_per_expert);
@@ -35,10 +47,13 @@ __global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ pac
   if (a >= *n_active) return;
   const int64_t e = active[a];
   const int64_t gi = gid % groups_per_expert;  // n * (K/32) + group
-  const u32x4_t w = reinterpret_cast<const u32x4_t*>(packed + e * groups_per_expert * 16)[gi];
+  const int64_t n = gi / (K / 32);
+  const int64_t g = gi % (K / 32);
+  const int64_t src = group_index(layout, e, n, g, N, K);
+  const u32x4_t w = reinterpret_cast<const u32x4_t*>(packed)[src];
   uint32_t out[16];
   if constexpr (FMT == 1) {
-    const uint32_t code = static_cast<const uint8_t*>(scales)[e * groups_per_expert + gi];
+    const uint32_t code = static_cast<const uint8_t*>(scales)[src];
     const float s = e8m0_to_f32(code);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -49,7 +64,7 @@ __global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ pac
       out[i] = lo | (hi << 16);
     }
   } else {
-    const float s = bf16_to_f32(static_cast<const uint16_t*>(scales)[e * groups_per_expert + gi]);
+    const float s = bf16_to_f32(static_cast<const uint16_t*>(scales)[src]);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const uint32_t byte = (w[i >> 2] >> (8 * (i & 3))) & 0xFFu;
@@ -58,12 +73,49 @@ __global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ pac
       out[i] = f32_to_bf16_rne((float)q0 * s) | (f32_to_bf16_rne((float)q1 * s) << 16);
     }
   }
-  u32x4_t* o = reinterpret_cast<u32x4_t*>(dst + ((int64_t)slot * groups_per_expert + gi) * 32);
+  if (tiled_out) {
+    // piece s of slot L of tile (n / 32, g / 2): 16 bytes at (s * 64 + L) * 16
+    uint8_t* tile = reinterpret_cast<uint8_t*>(dst) +
+                    (((int64_t)slot * (N / 32) + (n >> 5)) * (K / 64) + (g >> 1)) * 4096;
+    const int L = (int)((g & 1) * 32 + (n & 31));
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    u32x4_t v = {out[4 * i], out[4 * i + 1], out[4 * i + 2], out[4 * i + 3]};
-    o[i] = v;
+    for (int i = 0; i < 4; ++i) {
+      u32x4_t v = {out[4 * i], out[4 * i + 1], out[4 * i + 2], out[4 * i + 3]};
+      *reinterpret_cast<u32x4_t*>(tile + (i * 64 + L) * 16) = v;
+    }
+  } else {
+    u32x4_t* o = reinterpret_cast<u32x4_t*>(dst + ((int64_t)slot * groups_per_expert + gi) * 32);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      u32x4_t v = {out[4 * i], out[4 * i + 1], out[4 * i + 2], out[4 * i + 3]};
+      o[i] = v;
+    }
   }
+}
+
+// Rows -> MFMA-tiled copy: one thread per 16-byte group chunk, written in
+// tiled order so the stores are contiguous across the wavefront.
+template <int SB>
+__global__ __launch_bounds__(256) void k_repack(const uint8_t* __restrict__ packed,
+                                                const uint8_t* __restrict__ scales, int E, int N,
+                                                int K, uint8_t* __restrict__ packed_out,
+                                                uint8_t* __restrict__ scales_out) {
+  const int64_t total = (int64_t)E * N * (K / 32);
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= total) return;
+  // t enumerates the tiled order: ((e, cb, j), slot L)
+  const int L = (int)(t & 63);
+  const int64_t tile = t >> 6;
+  const int64_t j = tile % (K / 64);
+  const int64_t ecb = tile / (K / 64);
+  const int64_t cb = ecb % (N / 32);
+  const int64_t e = ecb / (N / 32);
+  const int64_t n = cb * 32 + (L & 31);
+  const int64_t g = j * 2 + (L >> 5);
+  const int64_t src = (e * N + n) * (K / 32) + g;
+  reinterpret_cast<u32x4_t*>(packed_out)[t] = reinterpret_cast<const u32x4_t*>(packed)[src];
+#pragma unroll
+  for (int i = 0; i < SB; ++i) scales_out[t * SB + i] = scales[src * SB + i];
 }
 
 // out[t][:] = sum over j ascending of w_j * rows[inv_perm[t*k+j]][:], fp32
@@ -100,18 +152,32 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ ro
 
 }  // namespace
 
-hipError_t launch_dequant(int fmt, const uint8_t* packed, const void* scales, int N, int K,
-                          const int32_t* active, const int32_t* n_active, int first, int count,
-                          uint16_t* dst, hipStream_t s) {
+hipError_t launch_dequant(int fmt, const uint8_t* packed, const void* scales, int layout, int N,
+                          int K, const int32_t* active, const int32_t* n_active, int first,
+                          int count, bool tiled_out, uint16_t* dst, hipStream_t s) {
   const int64_t groups = (int64_t)count * N * (K / 32);
   if (groups <= 0) return hipSuccess;
   const dim3 grid((unsigned)((groups + 255) / 256));
   if (fmt == 1)
-    hipLaunchKernelGGL(k_dequant<1>, grid, dim3(256), 0, s, packed, scales, N, K, active,
-                       n_active, first, count, dst);
+    hipLaunchKernelGGL(k_dequant<1>, grid, dim3(256), 0, s, packed, scales, layout, N, K, active,
+                       n_active, first, count, tiled_out ? 1 : 0, dst);
   else
-    hipLaunchKernelGGL(k_dequant<2>, grid, dim3(256), 0, s, packed, scales, N, K, active,
-                       n_active, first, count, dst);
+    hipLaunchKernelGGL(k_dequant<2>, grid, dim3(256), 0, s, packed, scales, layout, N, K, active,
+                       n_active, first, count, tiled_out ? 1 : 0, dst);
+  return hipGetLastError();
+}
+
+hipError_t launch_repack(int fmt, const uint8_t* packed, const void* scales, int E, int N, int K,
+                         uint8_t* packed_out, void* scales_out, hipStream_t s) {
+  const int64_t total = (int64_t)E * N * (K / 32);
+  if (total <= 0) return hipSuccess;
+  const dim3 grid((unsigned)((total + 255) / 256));
+  const uint8_t* sc = static_cast<const uint8_t*>(scales);
+  uint8_t* so = static_cast<uint8_t*>(scales_out);
+  if (fmt == 1)
+    hipLaunchKernelGGL(k_repack<1>, grid, dim3(256), 0, s, packed, sc, E, N, K, packed_out, so);
+  else
+    hipLaunchKernelGGL(k_repack<2>, grid, dim3(256), 0, s, packed, sc, E, N, K, packed_out, so);
   return hipGetLastError();
 }
 

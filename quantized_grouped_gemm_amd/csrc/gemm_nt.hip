@@ -31,7 +31,7 @@ namespace qgg {
 
 namespace {
 
-constexpr int kKL = 128;                 // K elements per LDS stage
+constexpr int kKL = 64;                  // K elements per LDS stage (one K step)
 constexpr int kRowB = kKL * 2 + 16;      // padded LDS bytes per A row
 constexpr int kCPR = kKL * 2 / 16;       // 16-byte chunks per row per stage
 // weight steps in flight per wavefront (BF16 steps are 4x larger)
@@ -49,18 +49,62 @@ struct BRegs {
                    // refill never waits for its own load
 };
 
+// Per-lane weight stream: byte pointers to this lane's first K step and the
+// byte strides from one 64-wide K step to the next.
+struct BStream {
+  const uint8_t* w;
+  const uint8_t* s;
+  int64_t wstep, sstep;
+};
+
 template <int SRC>
-__device__ __forceinline__ void load_b(const GemmArgs& g, const uint8_t* wp, const uint8_t* sp,
-                                       const uint16_t* wb, int group, BRegs<SRC>& r) {
+__device__ __forceinline__ void load_b(const BStream& b, int step, BRegs<SRC>& r) {
+  const uint8_t* wp = b.w + step * b.wstep;
   if constexpr (SRC == kSrcBF16) {
-    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(wb + group * 32);
+    // tiled BF16: the four 8-element pieces of a lane sit 1 KiB apart
 #pragma unroll
-    for (int s = 0; s < 4; ++s) r.w[s] = src[s];
+    for (int s = 0; s < 4; ++s) r.w[s] = *reinterpret_cast<const u32x4_t*>(wp + s * 1024);
   } else {
-    r.w[0] = *reinterpret_cast<const u32x4_t*>(wp + group * 16);
-    if constexpr (SRC == kSrcMXFP4) r.sraw = sp[group];
-    else r.sraw = reinterpret_cast<const uint16_t*>(sp)[group];
+    r.w[0] = *reinterpret_cast<const u32x4_t*>(wp);
+    const uint8_t* sp = b.s + step * b.sstep;
+    if constexpr (SRC == kSrcMXFP4) r.sraw = *sp;
+    else r.sraw = *reinterpret_cast<const uint16_t*>(sp);
   }
+}
+
+// Stream of W row `wrow` (a multiple-of-32 block plus this lane's column) for
+// lane `lane` = 32 * half + col.
+template <int SRC>
+__device__ __forceinline__ BStream make_stream(const GemmArgs& g, int64_t expert_or_slot,
+                                               int wrow, int lane) {
+  BStream b;
+  const int64_t nkt = g.K / 64;                // K steps
+  const int64_t cb = wrow >> 5;
+  const int half = lane >> 5;
+  if constexpr (SRC == kSrcBF16) {
+    b.w = reinterpret_cast<const uint8_t*>(g.wbf16) +
+          ((expert_or_slot * (g.N / 32) + cb) * nkt * 4096) + lane * 16;
+    b.wstep = 4096;
+    b.s = nullptr;
+    b.sstep = 0;
+  } else {
+    const int sb = SRC == kSrcMXFP4 ? 1 : 2;
+    const uint8_t* sc = static_cast<const uint8_t*>(g.scales);
+    if (g.layout == 1) {   // MFMA-tiled
+      const int64_t t0 = (expert_or_slot * (g.N / 32) + cb) * nkt;
+      b.w = g.packed + t0 * 1024 + lane * 16;
+      b.wstep = 1024;
+      b.s = sc + (t0 * 64 + lane) * sb;
+      b.sstep = 64 * sb;
+    } else {               // rows
+      const int64_t row = expert_or_slot * g.N + wrow;
+      b.w = g.packed + row * (g.K / 2) + half * 16;
+      b.wstep = 32;
+      b.s = sc + (row * (g.K / 32) + half) * sb;
+      b.sstep = 2 * sb;
+    }
+  }
+  return b;
 }
 
 // Scale of a loaded group in the form the decoder takes.
@@ -75,8 +119,9 @@ __device__ __forceinline__ BScale<SRC> b_scale(const BRegs<SRC>& r) {
   if constexpr (SRC == kSrcMXFP4) {
     o.s = e8m0_to_f32(r.sraw);
   } else if constexpr (SRC == kSrcINT4) {
-    o.s = bf16_to_f32(r.sraw);
-    o.neg8s = -8.0f * o.s;
+    const float sc = bf16_to_f32(r.sraw);
+    o.s = 512.0f * sc;
+    o.neg8s = -8.0f * sc;
   }
   return o;
 }
@@ -112,10 +157,7 @@ __device__ __forceinline__ void gemm_nt_item(const GemmArgs& g, uint8_t (*As)[32
   const int lane = tid & 63;
   const int col = lane & 31;
   const int half = lane >> 5;
-  const int nstages = g.K / kKL;
-  const int nsteps = nstages * 2;
-  const int64_t rowbytes = g.K / 2;
-  const int64_t rowscales = g.K / 32;
+  const int nsteps = g.K / kKL;
   const int expert = tile.x, row0 = tile.y, nrows = tile.z;
 
   // A sources and LDS destinations of this thread's 16-byte chunks
@@ -151,19 +193,9 @@ __device__ __forceinline__ void gemm_nt_item(const GemmArgs& g, uint8_t (*As)[32
     wrow0 = ocol;
     wrow1 = ocol + 32;
   }
-  const uint8_t *wp0 = nullptr, *wp1 = nullptr, *sp0 = nullptr, *sp1 = nullptr;
-  const uint16_t *wb0 = nullptr, *wb1 = nullptr;
-  if constexpr (SRC == kSrcBF16) {
-    const int64_t slot = tile.w - g.bf16_slot_base;
-    wb0 = g.wbf16 + (slot * g.N + wrow0) * (int64_t)g.K;
-    wb1 = g.wbf16 + (slot * g.N + wrow1) * (int64_t)g.K;
-  } else {
-    const int sb = SRC == kSrcMXFP4 ? 1 : 2;
-    wp0 = g.packed + ((int64_t)expert * g.N + wrow0) * rowbytes;
-    wp1 = g.packed + ((int64_t)expert * g.N + wrow1) * rowbytes;
-    sp0 = static_cast<const uint8_t*>(g.scales) + ((int64_t)expert * g.N + wrow0) * rowscales * sb;
-    sp1 = static_cast<const uint8_t*>(g.scales) + ((int64_t)expert * g.N + wrow1) * rowscales * sb;
-  }
+  const int64_t wsel = SRC == kSrcBF16 ? (int64_t)(tile.w - g.bf16_slot_base) : (int64_t)expert;
+  const BStream bs0 = make_stream<SRC>(g, wsel, wrow0, lane);
+  const BStream bs1 = make_stream<SRC>(g, wsel, wrow1, lane);
 
   f32x16_t acc[NMB][2];
 #pragma unroll
@@ -180,8 +212,8 @@ __device__ __forceinline__ void gemm_nt_item(const GemmArgs& g, uint8_t (*As)[32
 #pragma unroll
   for (int r = 0; r < kRing; ++r) {
     const int st = r < nsteps ? r : nsteps - 1;
-    load_b<SRC>(g, wp0, sp0, wb0, st * 2 + half, ring[r][0]);
-    load_b<SRC>(g, wp1, sp1, wb1, st * 2 + half, ring[r][1]);
+    load_b<SRC>(bs0, st, ring[r][0]);
+    load_b<SRC>(bs1, st, ring[r][1]);
   }
   u32x4_t areg[NCH];
 #pragma unroll
@@ -195,51 +227,54 @@ __device__ __forceinline__ void gemm_nt_item(const GemmArgs& g, uint8_t (*As)[32
   auto kstep = [&](int step, BRegs<SRC>(&slot)[2], auto sub_c, auto buf_c) {
     constexpr int SUB = decltype(sub_c)::value;
     constexpr int BUF = decltype(buf_c)::value;
-    const int st = step >> 1;
-    if constexpr (SUB == 0) {
-      const int nx = st + 1 < nstages ? st + 1 : st;
+    {
+      const int nx = step + 1 < nsteps ? step + 1 : step;
 #pragma unroll
       for (int i = 0; i < NCH; ++i)
         areg[i] = *reinterpret_cast<const u32x4_t*>(asrc[i] + nx * kKL);
     }
     const BScale<SRC> sc0 = b_scale<SRC>(slot[0]);
     const BScale<SRC> sc1 = b_scale<SRC>(slot[1]);
-    // A operands double-buffered across the four K sub-steps
+    // A operands: double-buffered across the four K sub-steps when the
+    // tile is short; loaded just in time when registers are scarce
+    constexpr bool kDbl = NMB <= 2;
     bf16x8_t acur[NMB], anxt[NMB];
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb)
       acur[mb] = *reinterpret_cast<const bf16x8_t*>(
-          &As[BUF][(mb * 32 + col) * kRowB + (SUB * 64 + half * 32) * 2]);
+          &As[BUF][(mb * 32 + col) * kRowB + (half * 32) * 2]);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      if (s < 3) {
+      if (kDbl && s < 3) {
 #pragma unroll
         for (int mb = 0; mb < NMB; ++mb)
           anxt[mb] = *reinterpret_cast<const bf16x8_t*>(
-              &As[BUF][(mb * 32 + col) * kRowB + (SUB * 64 + half * 32 + (s + 1) * 8) * 2]);
+              &As[BUF][(mb * 32 + col) * kRowB + (half * 32 + (s + 1) * 8) * 2]);
       }
       const bf16x8_t b0 = b_operand<SRC>(slot[0], sc0, s);
       const bf16x8_t b1 = b_operand<SRC>(slot[1], sc1, s);
       if (s == 3) {
         const int nx = step + kRing < nsteps ? step + kRing : nsteps - 1;
-        load_b<SRC>(g, wp0, sp0, wb0, nx * 2 + half, slot[0]);
-        load_b<SRC>(g, wp1, sp1, wb1, nx * 2 + half, slot[1]);
+        load_b<SRC>(bs0, nx, slot[0]);
+        load_b<SRC>(bs1, nx, slot[1]);
       }
 #pragma unroll
       for (int mb = 0; mb < NMB; ++mb) {
+        if (!kDbl && s > 0)
+          acur[mb] = *reinterpret_cast<const bf16x8_t*>(
+              &As[BUF][(mb * 32 + col) * kRowB + (half * 32 + s * 8) * 2]);
         acc[mb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(acur[mb], b0, acc[mb][0], 0, 0, 0);
         acc[mb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(acur[mb], b1, acc[mb][1], 0, 0, 0);
       }
-      if (s < 3) {
+      if (kDbl && s < 3) {
 #pragma unroll
         for (int mb = 0; mb < NMB; ++mb) acur[mb] = anxt[mb];
       }
     }
-    if constexpr (SUB == 1) {
 #pragma unroll
-      for (int i = 0; i < NCH; ++i) *reinterpret_cast<u32x4_t*>(&As[BUF ^ 1][adst[i]]) = areg[i];
-      __syncthreads();
-    }
+    for (int i = 0; i < NCH; ++i) *reinterpret_cast<u32x4_t*>(&As[BUF ^ 1][adst[i]]) = areg[i];
+    __syncthreads();
+    (void)sub_c;
   };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
@@ -248,20 +283,20 @@ __device__ __forceinline__ void gemm_nt_item(const GemmArgs& g, uint8_t (*As)[32
   if constexpr (kRing == 4) {
     for (; base + 4 <= nsteps; base += 4) {
       kstep(base + 0, ring[0], I0{}, I0{});
-      kstep(base + 1, ring[1], I1{}, I0{});
-      kstep(base + 2, ring[2], I0{}, I1{});
+      kstep(base + 1, ring[1], I1{}, I1{});
+      kstep(base + 2, ring[2], I0{}, I0{});
       kstep(base + 3, ring[3], I1{}, I1{});
     }
-    if (base < nsteps) {                 // one stage left
+    if (base < nsteps) {                 // two steps left (K % 128 == 0)
       kstep(base + 0, ring[0], I0{}, I0{});
-      kstep(base + 1, ring[1], I1{}, I0{});
+      kstep(base + 1, ring[1], I1{}, I1{});
     }
   } else {
     for (; base < nsteps; base += 4) {   // kRing == 2: slots alternate per step
       kstep(base + 0, ring[0], I0{}, I0{});
-      kstep(base + 1, ring[1], I1{}, I0{});
+      kstep(base + 1, ring[1], I1{}, I1{});
       if (base + 2 < nsteps) {
-        kstep(base + 2, ring[0], I0{}, I1{});
+        kstep(base + 2, ring[0], I0{}, I0{});
         kstep(base + 3, ring[1], I1{}, I1{});
       }
     }
@@ -297,7 +332,7 @@ __device__ __forceinline__ void gemm_nt_item(const GemmArgs& g, uint8_t (*As)[32
 }
 
 template <int SRC, int MB, int EPI, int AMODE>
-__global__ __launch_bounds__(256, MB == 4 ? 1 : 2) void k_gemm_nt(GemmArgs g) {
+__global__ __launch_bounds__(256, 2) void k_gemm_nt(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) uint8_t As[2][32 * MB * kRowB];
   const int t_begin = g.range[0];
   const int t_end = g.range[1];
@@ -328,7 +363,7 @@ hipError_t launch_nt_t(const GemmArgs& g, hipStream_t s) {
   const int n_tiles_n = EPI == kEpiSwiGLU ? (g.inter + 127) / 128 : (g.N + 255) / 256;
   const int64_t bound = (int64_t)g.max_tiles * n_tiles_n;
   if (bound <= 0) return hipSuccess;
-  int64_t grid = std::min<int64_t>(bound, (int64_t)num_cus() * (MB == 4 ? 1 : 2));
+  int64_t grid = std::min<int64_t>(bound, (int64_t)num_cus() * 2);
   grid = (grid + 7) / 8 * 8;
   hipLaunchKernelGGL((k_gemm_nt<SRC, MB, EPI, AMODE>), dim3((unsigned)grid), dim3(256), 0, s, g);
   return hipGetLastError();

@@ -51,11 +51,20 @@ __device__ __forceinline__ void load_bt(const GemmArgs& g, int64_t slot_or_exper
     b.s0 = b.s1 = 0.f;
     return;
   }
+  // element (n, k) of an MFMA-tiled tensor: tile (n / 32, k / 64), slot
+  // 32 * ((k % 64) / 32) + n % 32; rows r and r + 1 are adjacent slots
+  const int64_t cb = r >> 5;
+  const int64_t j = c >> 6;
+  const int lslot = ((c & 63) >> 5) * 32 + (r & 31);
+  const int64_t tile = (slot_or_expert * (g.N / 32) + cb) * (g.K / 64) + j;
   if constexpr (SRC == kSrcBF16) {
-    const uint16_t* w0 = g.wbf16 + (slot_or_expert * g.N + r) * (int64_t)g.K + c;
-    const u32x4_t* a0 = reinterpret_cast<const u32x4_t*>(w0);
-    const u32x4_t* a1 = reinterpret_cast<const u32x4_t*>(w0 + g.K);
-    const u32x4_t x0 = a0[0], x1 = a0[1], y0 = a1[0], y1 = a1[1];
+    // 16 consecutive k = the pieces s0 and s0 + 1 (8 elements each)
+    const int s0 = (c & 31) >> 3;
+    const uint8_t* base = reinterpret_cast<const uint8_t*>(g.wbf16) + tile * 4096;
+    const u32x4_t x0 = *reinterpret_cast<const u32x4_t*>(base + (s0 * 64 + lslot) * 16);
+    const u32x4_t x1 = *reinterpret_cast<const u32x4_t*>(base + ((s0 + 1) * 64 + lslot) * 16);
+    const u32x4_t y0 = *reinterpret_cast<const u32x4_t*>(base + (s0 * 64 + lslot + 1) * 16);
+    const u32x4_t y1 = *reinterpret_cast<const u32x4_t*>(base + ((s0 + 1) * 64 + lslot + 1) * 16);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       b.p[i] = x0[i];
@@ -64,24 +73,37 @@ __device__ __forceinline__ void load_bt(const GemmArgs& g, int64_t slot_or_exper
       b.p[12 + i] = y1[i];
     }
   } else {
-    const int64_t rowbytes = g.K / 2;
-    const uint8_t* w0 = g.packed + (slot_or_expert * g.N + r) * rowbytes + c / 2;
+    const int sbytes = SRC == kSrcMXFP4 ? 1 : 2;
+    const uint8_t* sp = static_cast<const uint8_t*>(g.scales);
+    const uint8_t* w0;
+    int64_t wnext, si, snext;
+    if (g.layout == 1) {
+      w0 = g.packed + (tile * 64 + lslot) * 16 + ((c & 31) >> 1);
+      wnext = 16;
+      si = tile * 64 + lslot;
+      snext = 1;
+    } else {
+      const int64_t rowbytes = g.K / 2;
+      w0 = g.packed + (slot_or_expert * g.N + r) * rowbytes + c / 2;
+      wnext = rowbytes;
+      si = (slot_or_expert * g.N + r) * (int64_t)(g.K / 32) + c / 32;
+      snext = g.K / 32;
+    }
     const uint2 x = *reinterpret_cast<const uint2*>(w0);
-    const uint2 y = *reinterpret_cast<const uint2*>(w0 + rowbytes);
+    const uint2 y = *reinterpret_cast<const uint2*>(w0 + wnext);
     b.p[0] = x.x;
     b.p[1] = x.y;
     b.p[2] = y.x;
     b.p[3] = y.y;
-    const int64_t si = (slot_or_expert * g.N + r) * (int64_t)(g.K / 32) + c / 32;
     if constexpr (SRC == kSrcMXFP4) {
-      const uint8_t* sp = static_cast<const uint8_t*>(g.scales);
       b.s0 = e8m0_to_f32(sp[si]);
-      b.s1 = e8m0_to_f32(sp[si + g.K / 32]);
+      b.s1 = e8m0_to_f32(sp[si + snext]);
     } else {
-      const uint16_t* sp = static_cast<const uint16_t*>(g.scales);
-      b.s0 = bf16_to_f32(sp[si]);
-      b.s1 = bf16_to_f32(sp[si + g.K / 32]);
+      const uint16_t* sp16 = reinterpret_cast<const uint16_t*>(sp);
+      b.s0 = bf16_to_f32(sp16[si]);
+      b.s1 = bf16_to_f32(sp16[si + snext]);
     }
+    (void)sbytes;
   }
 }
 
@@ -103,10 +125,11 @@ __device__ __forceinline__ void store_bt(const BStage<SRC>& b, uint8_t* Bs, int 
     dq8_mxfp4(b.p[3], b.s1, r1 + 4);
   } else {
     const float n0 = -8.0f * b.s0, n1 = -8.0f * b.s1;
-    dq8_int4(b.p[0], b.s0, n0, r0);
-    dq8_int4(b.p[1], b.s0, n0, r0 + 4);
-    dq8_int4(b.p[2], b.s1, n1, r1);
-    dq8_int4(b.p[3], b.s1, n1, r1 + 4);
+    const float m0 = 512.0f * b.s0, m1 = 512.0f * b.s1;
+    dq8_int4(b.p[0], m0, n0, r0);
+    dq8_int4(b.p[1], m0, n0, r0 + 4);
+    dq8_int4(b.p[2], m1, n1, r1);
+    dq8_int4(b.p[3], m1, n1, r1 + 4);
   }
 #pragma unroll
   for (int i = 0; i < 8; ++i) {

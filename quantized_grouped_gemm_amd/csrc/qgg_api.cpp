@@ -7,7 +7,7 @@
 #include <mutex>
 #include <vector>
 
-#include "../../include/qgg.h"
+#include "qgg.h"
 #include "qgg_internal.hpp"
 
 namespace qgg {
@@ -72,9 +72,11 @@ void carve_plan(Carver& cv, int64_t P, int E, Plan& pl) {
 
 bool valid_fmt(int f) { return f == QGG_FMT_MXFP4 || f == QGG_FMT_INT4; }
 
+bool valid_layout(int l) { return l == QGG_LAYOUT_ROWS || l == QGG_LAYOUT_MFMA; }
+
 bool valid_weight(const qgg_qweight* w, int E, int N, int K) {
-  return w && valid_fmt(w->fmt) && w->E == E && w->N == N && w->K == K && w->packed &&
-         w->scales;
+  return w && valid_fmt(w->fmt) && valid_layout(w->layout) && w->E == E && w->N == N &&
+         w->K == K && w->packed && w->scales;
 }
 
 bool valid_perm(const qgg_perm* p) {
@@ -103,6 +105,7 @@ GemmArgs base_args(const qgg_qweight* w, const Plan& pl) {
   g.src = src_of(w->fmt);
   g.packed = w->packed;
   g.scales = w->scales;
+  g.layout = w->layout;
   g.N = w->N;
   g.K = w->K;
   g.tiles = pl.tiles;
@@ -142,7 +145,21 @@ const char* qgg_status_string(qgg_status s) {
   }
 }
 
-const char* qgg_version(void) { return "qgg 0.1 gfx950"; }
+const char* qgg_version(void) { return "qgg 0.2 gfx950"; }
+
+qgg_status qgg_repack_weights(const qgg_qweight* src, uint8_t* packed_out, void* scales_out,
+                              qgg_stream_t stream) {
+  if (!src || !valid_fmt(src->fmt) || src->layout != QGG_LAYOUT_ROWS || !src->packed ||
+      !src->scales || !packed_out || !scales_out || src->E <= 0 || src->N <= 0 || src->K <= 0)
+    return QGG_ERR_INVALID_ARG;
+  if (src->N % 32 || src->K % 64) return QGG_ERR_UNSUPPORTED;
+  if (static_cast<const void*>(packed_out) == static_cast<const void*>(src->packed) ||
+      scales_out == src->scales)
+    return QGG_ERR_INVALID_ARG;
+  QGG_HIP(launch_repack(src->fmt, src->packed, src->scales, src->E, src->N, src->K, packed_out,
+                        scales_out, stream));
+  return QGG_OK;
+}
 
 // Workspace layout per call (each piece 256-byte aligned, in this order):
 //  PERMUTE  segment counts
@@ -221,7 +238,8 @@ qgg_status dequant_grouped_gemm(const qgg_qweight* w, const uint16_t* a, int fla
                                 const qgg_perm* p, int T, int k, int variant, int chunk,
                                 void* workspace, size_t ws_bytes, uint16_t* y,
                                 qgg_stream_t stream) {
-  if (!w || !valid_perm(p) || !valid_fmt(w->fmt)) return QGG_ERR_INVALID_ARG;
+  if (!w || !valid_perm(p) || !valid_fmt(w->fmt) || !valid_layout(w->layout))
+    return QGG_ERR_INVALID_ARG;
   const int E = w->E, N = w->N, K = w->K;
   if (!valid_route_dims(T, E, k) || N <= 0 || K <= 0 || chunk < 0) return QGG_ERR_INVALID_ARG;
   if (!w->packed || !w->scales) return QGG_ERR_INVALID_ARG;
@@ -243,8 +261,8 @@ qgg_status dequant_grouped_gemm(const qgg_qweight* w, const uint16_t* a, int fla
   uint16_t* sbuf = cv.take<uint16_t>(scratch);
 
   if (dq_only) {
-    QGG_HIP(launch_dequant(w->fmt, w->packed, w->scales, N, K, p->active, p->n_active, 0, C,
-                           static_cast<uint16_t*>(workspace), stream));
+    QGG_HIP(launch_dequant(w->fmt, w->packed, w->scales, w->layout, N, K, p->active, p->n_active,
+                           0, C, false, static_cast<uint16_t*>(workspace), stream));
     return QGG_OK;
   }
   if (P == 0) return QGG_OK;
@@ -272,8 +290,8 @@ qgg_status dequant_grouped_gemm(const qgg_qweight* w, const uint16_t* a, int fla
   g.src = kSrcBF16;
   g.wbf16 = sbuf;
   for (int c = 0; c < nch; ++c) {
-    QGG_HIP(launch_dequant(w->fmt, w->packed, w->scales, N, K, p->active, p->n_active, c * C, C,
-                           sbuf, stream));
+    QGG_HIP(launch_dequant(w->fmt, w->packed, w->scales, w->layout, N, K, p->active,
+                           p->n_active, c * C, C, true, sbuf, stream));
     g.range = pl.chunk_first + c;
     g.max_tiles = first[c + 1] - first[c];
     g.bf16_slot_base = c * C;
@@ -352,11 +370,12 @@ qgg_status moe_ffn_fwd(const qgg_qweight* w_gate_up, const qgg_qweight* w_down,
       gu.range = dn.range = pl.chunk_first + c;
       gu.max_tiles = dn.max_tiles = first[c + 1] - first[c];
       gu.bf16_slot_base = dn.bf16_slot_base = c * C;
-      QGG_HIP(launch_dequant(w_gate_up->fmt, w_gate_up->packed, w_gate_up->scales, 2 * inter, d,
-                             p->active, p->n_active, c * C, C, sbuf, stream));
+      QGG_HIP(launch_dequant(w_gate_up->fmt, w_gate_up->packed, w_gate_up->scales,
+                             w_gate_up->layout, 2 * inter, d, p->active, p->n_active, c * C, C,
+                             true, sbuf, stream));
       QGG_HIP(launch_gemm_nt(gu, pl.mb, stream));
-      QGG_HIP(launch_dequant(w_down->fmt, w_down->packed, w_down->scales, d, inter, p->active,
-                             p->n_active, c * C, C, sbuf, stream));
+      QGG_HIP(launch_dequant(w_down->fmt, w_down->packed, w_down->scales, w_down->layout, d,
+                             inter, p->active, p->n_active, c * C, C, true, sbuf, stream));
       QGG_HIP(launch_gemm_nt(dn, pl.mb, stream));
     }
   }
@@ -433,11 +452,12 @@ qgg_status moe_dx_bwd(const qgg_qweight* w_gate_up, const qgg_qweight* w_down,
       dn.range = gu.range = pl.chunk_first + c;
       dn.max_tiles = gu.max_tiles = first[c + 1] - first[c];
       dn.bf16_slot_base = gu.bf16_slot_base = c * C;
-      QGG_HIP(launch_dequant(w_down->fmt, w_down->packed, w_down->scales, d, inter, p->active,
-                             p->n_active, c * C, C, sbuf, stream));
+      QGG_HIP(launch_dequant(w_down->fmt, w_down->packed, w_down->scales, w_down->layout, d,
+                             inter, p->active, p->n_active, c * C, C, true, sbuf, stream));
       QGG_HIP(launch_gemm_tn(dn, pl.mb, stream));
-      QGG_HIP(launch_dequant(w_gate_up->fmt, w_gate_up->packed, w_gate_up->scales, 2 * inter, d,
-                             p->active, p->n_active, c * C, C, sbuf, stream));
+      QGG_HIP(launch_dequant(w_gate_up->fmt, w_gate_up->packed, w_gate_up->scales,
+                             w_gate_up->layout, 2 * inter, d, p->active, p->n_active, c * C, C,
+                             true, sbuf, stream));
       QGG_HIP(launch_gemm_tn(gu, pl.mb, stream));
     }
   }

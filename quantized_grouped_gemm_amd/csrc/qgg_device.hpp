@@ -83,20 +83,26 @@ __device__ __forceinline__ void dq8_mxfp4(uint32_t w, float scale, uint32_t out[
 }
 
 // Eight two's-complement INT4 codes times a BF16 scale s -> eight BF16 values.
-// With n' = q + 8 (the code XOR 8) as an exact float, fma(n', s, -8 s) is
+// With n' = q + 8 (the code XOR 8), each n' in 0..15 is moved into a byte;
+// read as an FP8 E4M3 code, byte n' is exactly n' * 2^-9 (codes 0..7 are the
+// subnormals m * 2^-9, codes 8..15 the first binade (8 + m) * 2^-9), so one
+// v_cvt_pk_f32_fp8 yields two exact values.  fma(n' 2^-9, 512 s, -8 s) is
 // q * s formed exactly and rounded once; q * s needs at most 12 significant
 // bits, so the fp32 value is exact and the BF16 rounding matches
-// bf16_rne(q * s).
-__device__ __forceinline__ void dq8_int4(uint32_t w, float s, float neg8s, uint32_t out[4]) {
+// bf16_rne(q * s).  s512 = 512 s and neg8s = -8 s are exact powers-of-two
+// multiples of s (finite for every scale below 2^118).
+__device__ __forceinline__ void dq8_int4(uint32_t w, float s512, float neg8s, uint32_t out[4]) {
   const uint32_t b = w ^ 0x88888888u;
   const uint32_t lo = b & 0x0F0F0F0Fu;          // elements 0, 2, 4, 6
   const uint32_t hi = (b >> 4) & 0x0F0F0F0Fu;   // elements 1, 3, 5, 7
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float e0 = (float)((lo >> (8 * i)) & 0xFFu);
-    const float e1 = (float)((hi >> (8 * i)) & 0xFFu);
-    out[i] = pack_bf16x2(__builtin_fmaf(e0, s, neg8s), __builtin_fmaf(e1, s, neg8s));
-  }
+  const f32x2_t e02 = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, false);
+  const f32x2_t e46 = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, true);
+  const f32x2_t e13 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, false);
+  const f32x2_t e57 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, true);
+  out[0] = pack_bf16x2(__builtin_fmaf(e02[0], s512, neg8s), __builtin_fmaf(e13[0], s512, neg8s));
+  out[1] = pack_bf16x2(__builtin_fmaf(e02[1], s512, neg8s), __builtin_fmaf(e13[1], s512, neg8s));
+  out[2] = pack_bf16x2(__builtin_fmaf(e46[0], s512, neg8s), __builtin_fmaf(e57[0], s512, neg8s));
+  out[3] = pack_bf16x2(__builtin_fmaf(e46[1], s512, neg8s), __builtin_fmaf(e57[1], s512, neg8s));
 }
 
 __device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-z)); }

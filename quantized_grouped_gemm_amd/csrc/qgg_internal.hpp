@@ -26,7 +26,8 @@ struct GemmArgs {
   int src;                       // WSource
   const uint8_t* packed;
   const void* scales;
-  const uint16_t* wbf16;         // BF16 weights [slots][N][K] (src == kSrcBF16)
+  int layout;                    // QGG_LAYOUT_ROWS | QGG_LAYOUT_MFMA (packed/scales)
+  const uint16_t* wbf16;         // BF16 weights, MFMA-tiled, [slots] (src == kSrcBF16)
   int N, K;
   int bf16_slot_base;            // BF16 slot of tile = tile.active_index - base
   // rows (A operand)
@@ -65,10 +66,17 @@ hipError_t launch_gemm_nt(const GemmArgs& g, int MB, hipStream_t s);
 hipError_t launch_gemm_tn(const GemmArgs& g, int MB, hipStream_t s);
 
 // BF16 copy of the weights of active experts [first, first + count) of the
-// active list into dst[slot][N][K].
-hipError_t launch_dequant(int fmt, const uint8_t* packed, const void* scales, int N, int K,
-                          const int32_t* active, const int32_t* n_active, int first, int count,
-                          uint16_t* dst, hipStream_t s);
+// active list: dst[slot][N][K] row-major, or (tiled_out) in the MFMA-tiled
+// BF16 order the grouped GEMMs read: tiles of 32 rows x 64 K, 4 KiB each,
+// [slot][N/32][K/64][s = 0..3][slot L = 32*h + c][8 elements], holding
+// elements 8*s .. 8*s+7 of scale group 2*j + h of row 32*cb + c.
+hipError_t launch_dequant(int fmt, const uint8_t* packed, const void* scales, int layout, int N,
+                          int K, const int32_t* active, const int32_t* n_active, int first,
+                          int count, bool tiled_out, uint16_t* dst, hipStream_t s);
+
+// ROWS -> MFMA-tiled copy of packed weights and scales.
+hipError_t launch_repack(int fmt, const uint8_t* packed, const void* scales, int E, int N, int K,
+                         uint8_t* packed_out, void* scales_out, hipStream_t s);
 
 // out[t] = sum_j w_j * rows[inv_perm[t*k+j]] (w_j = gates[t*k+j], or 1 when
 // gates is null), fp32 in ascending j, BF16 out.

@@ -18,13 +18,20 @@ def host_u16(t: torch.Tensor) -> np.ndarray:
     return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
 
 
-def dev_weights(fmt: int, packed: np.ndarray, scales: np.ndarray) -> qgg.QWeight:
+def dev_weights(fmt: int, packed: np.ndarray, scales: np.ndarray,
+                layout: int = qgg.LAYOUT_ROWS) -> qgg.QWeight:
+    """Row-layout weights on the device, repacked by the library when the
+    MFMA-tiled layout is asked for."""
     p = torch.from_numpy(np.ascontiguousarray(packed)).to(DEV)
     if scales.dtype == np.uint16:
         s = torch.from_numpy(np.ascontiguousarray(scales).view(np.int16)).to(DEV)
     else:
         s = torch.from_numpy(np.ascontiguousarray(scales)).to(DEV)
-    return qgg.QWeight(fmt, p, s)
+    w = qgg.QWeight(fmt, p, s)
+    return qgg.repack(w) if layout == qgg.LAYOUT_MFMA else w
+
+
+LAYOUTS = (qgg.LAYOUT_ROWS, qgg.LAYOUT_MFMA)
 
 
 def bf16_to_f64(u16: np.ndarray) -> np.ndarray:

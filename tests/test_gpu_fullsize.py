@@ -38,13 +38,17 @@ def test_kimi_int4_gate_up_full():
     print(f"case {cfg.name}: generating inputs", flush=True)
     logits, x = sc.router_logits(cfg), sc.activations(cfg)
     packed, scales = sc.first_weights(cfg)
-    w = dev_weights(cfg.fmt, packed, scales)
+    w_rows = dev_weights(cfg.fmt, packed, scales)
+    w = qgg.repack(w_rows)
     xd = dev_bf16(x)
     ids, _ = qgg.moe_route(torch.from_numpy(logits).to(DEV), cfg.k)
     p, _ = qgg.expert_permute(ids, cfg.E)
     y_f = qgg.dequant_grouped_gemm(w, xd, p, cfg.T, cfg.k, qgg.FUSED, 0)
     y_c = qgg.dequant_grouped_gemm(w, xd, p, cfg.T, cfg.k, qgg.CHUNKED, cfg.chunks[0])
+    y_r = qgg.dequant_grouped_gemm(w_rows, xd, p, cfg.T, cfg.k, qgg.FUSED, 0)
     sync()
+    assert torch.equal(y_f.view(torch.int16), y_r.view(torch.int16))
+    del w_rows, y_r
     print("case kimi: GPU done, checking", flush=True)
     ids_ref, _, pref = _check_routing(cfg, logits, ids, p)
     assert torch.equal(y_f.view(torch.int16), y_c.view(torch.int16))
@@ -82,7 +86,8 @@ def test_moe_ffn_fwd_full(name):
     cfg = sc.CONFIGS[name]
     print(f"case {cfg.name}: generating inputs", flush=True)
     logits, x, gu, dn = _ffn_inputs(cfg)
-    wg, wd = dev_weights(cfg.fmt, *gu), dev_weights(cfg.fmt, *dn)
+    wg = dev_weights(cfg.fmt, *gu, layout=qgg.LAYOUT_MFMA)
+    wd = dev_weights(cfg.fmt, *dn, layout=qgg.LAYOUT_MFMA)
     xd, lt = dev_bf16(x), torch.from_numpy(logits).to(DEV)
     r = qgg.moe_ffn_fwd(wg, wd, xd, lt, cfg.k, qgg.FUSED, 0, save_h=True)
     sync()
@@ -112,7 +117,8 @@ def test_moe_dx_bwd_full():
     print(f"case {cfg.name}: generating inputs", flush=True)
     logits, x, gu, dn = _ffn_inputs(cfg)
     dy = sc.grad_output(cfg)
-    wg, wd = dev_weights(cfg.fmt, *gu), dev_weights(cfg.fmt, *dn)
+    wg = dev_weights(cfg.fmt, *gu, layout=qgg.LAYOUT_MFMA)
+    wd = dev_weights(cfg.fmt, *dn, layout=qgg.LAYOUT_MFMA)
     fwd = qgg.moe_ffn_fwd(wg, wd, dev_bf16(x), torch.from_numpy(logits).to(DEV), cfg.k,
                           qgg.FUSED, 0, save_h=True)
     dyd = dev_bf16(dy)

@@ -11,7 +11,8 @@ import quantized_grouped_gemm_amd as qgg
 import synth
 from synth.configs import CONFIGS, STREAM, Config, scaled
 
-from .gpu_util import (DEV, assert_close, bf16_to_f64, dev_bf16, dev_weights, host_u16, sync)
+from .gpu_util import (DEV, LAYOUTS, assert_close, bf16_to_f64, dev_bf16, dev_weights, host_u16,
+                       sync)
 
 pytestmark = pytest.mark.gpu
 
@@ -130,6 +131,35 @@ def test_dequant_only_int4_all_bf16_scales():
     assert np.all((got[nan] & 0x7F80) == 0x7F80) and np.all((got[nan] & 0x7F) != 0)
 
 
+@pytest.mark.parametrize("fmt", [1, 2])
+def test_repack_is_the_documented_permutation(fmt):
+    E, N, K = 3, 128, 256
+    packed, scales = synth.qweights(4, 3, fmt, E, N, K)
+    w = dev_weights(fmt, packed, scales, layout=qgg.LAYOUT_MFMA)
+    sync()
+    got_p = w.packed.cpu().numpy().reshape(E, N // 32, K // 64, 64, 16)
+    got_s = w.scales.cpu().numpy().reshape(E, N // 32, K // 64, 64)
+    if fmt == 2:
+        got_s = got_s.view(np.uint16)
+    for L in range(64):
+        h, c = divmod(L, 32)
+        rows = np.arange(N // 32) * 32 + c
+        for j in range(K // 64):
+            g = 2 * j + h
+            np.testing.assert_array_equal(got_p[:, :, j, L, :],
+                                          packed[:, rows, g * 16:(g + 1) * 16])
+            np.testing.assert_array_equal(got_s[:, :, j, L], scales[:, rows, g])
+    # the chunked hook decodes the tiled tensor to the same row-major BF16
+    ids = torch.zeros((1, 1), dtype=torch.int32, device=DEV)
+    perm1, _ = qgg.expert_permute(ids, E)
+    a = qgg.dequant_grouped_gemm(dev_weights(fmt, packed, scales), None, perm1, 1, 1,
+                                 qgg.CHUNKED, 1, flags=qgg.DEQUANT_ONLY)[: N * K * 2].clone()
+    b = qgg.dequant_grouped_gemm(w, None, perm1, 1, 1, qgg.CHUNKED, 1,
+                                 flags=qgg.DEQUANT_ONLY)[: N * K * 2].clone()
+    sync()
+    assert torch.equal(a, b)
+
+
 # ------------------------------------------------------------ projections
 
 PROJ_CASES = [
@@ -156,20 +186,23 @@ def test_grouped_gemm_parity_and_chunk_invariance(cfg):
     ref = _proj_ref(cfg, w, x, ids_ref)
     ids, _ = qgg.moe_route(torch.from_numpy(logits).to(DEV), cfg.k)
     p, _ = qgg.expert_permute(ids, cfg.E)
-    wd = dev_weights(cfg.fmt, *w)
     xd = dev_bf16(x)
     inv = p.inv_perm.cpu().numpy()
     outs = {}
-    for variant, chunk in [(qgg.FUSED, 0), (qgg.CHUNKED, cfg.chunks[0]), (qgg.CHUNKED, 1),
-                           (qgg.CHUNKED, 0)]:
-        y = qgg.dequant_grouped_gemm(wd, xd, p, cfg.T, cfg.k, variant, chunk, flags=qgg.A_TOKENS)
-        sync()
-        yh = host_u16(y)
-        assert_close(bf16_to_f64(yh[inv]), ref, what=f"{cfg.name} v{variant} c{chunk}")
-        outs[(variant, chunk)] = yh
-    base = outs[(qgg.CHUNKED, 0)]
+    for layout in LAYOUTS:
+        wd = dev_weights(cfg.fmt, *w, layout=layout)
+        for variant, chunk in [(qgg.FUSED, 0), (qgg.CHUNKED, cfg.chunks[0]), (qgg.CHUNKED, 1),
+                               (qgg.CHUNKED, 0)]:
+            y = qgg.dequant_grouped_gemm(wd, xd, p, cfg.T, cfg.k, variant, chunk,
+                                         flags=qgg.A_TOKENS)
+            sync()
+            yh = host_u16(y)
+            assert_close(bf16_to_f64(yh[inv]), ref,
+                         what=f"{cfg.name} layout{layout} v{variant} c{chunk}")
+            outs[(layout, variant, chunk)] = yh
+    base = outs[(qgg.LAYOUT_ROWS, qgg.CHUNKED, 0)]
     for key, v in outs.items():
-        np.testing.assert_array_equal(v, base, err_msg=f"variant/chunk {key} differs")
+        np.testing.assert_array_equal(v, base, err_msg=f"layout/variant/chunk {key} differs")
 
 
 def test_grouped_gemm_one_hot_rows_return_weight_columns():
@@ -185,8 +218,8 @@ def test_grouped_gemm_one_hot_rows_return_weight_columns():
         logits[:, 2] = 5.0                                   # all rows to expert 2
         ids, _ = qgg.moe_route(torch.from_numpy(logits).to(DEV), k)
         p, _ = qgg.expert_permute(ids, E)
-        wd = dev_weights(fmt, packed, scales)
-        for variant in (qgg.FUSED, qgg.CHUNKED):
+        for layout, variant in [(lo, v) for lo in LAYOUTS for v in (qgg.FUSED, qgg.CHUNKED)]:
+            wd = dev_weights(fmt, packed, scales, layout=layout)
             y = qgg.dequant_grouped_gemm(wd, dev_bf16(x), p, T, k, variant, 0)
             sync()
             got = host_u16(y)                               # row t = W[:, t]
@@ -195,7 +228,8 @@ def test_grouped_gemm_one_hot_rows_return_weight_columns():
             # products is +0, and the two are the same value
             ref = np.where(ref == 0x8000, 0, ref).astype(np.uint16)
             assert np.count_nonzero(ref) > ref.size // 2
-            np.testing.assert_array_equal(got, ref.T, err_msg=f"fmt {fmt} variant {variant}")
+            np.testing.assert_array_equal(got, ref.T,
+                                          err_msg=f"fmt {fmt} layout {layout} variant {variant}")
 
 
 def test_grouped_gemm_exact_integer_inputs_bit_exact():
@@ -218,8 +252,8 @@ def test_grouped_gemm_exact_integer_inputs_bit_exact():
     ids, _ = qgg.moe_route(torch.from_numpy(logits).to(DEV), k)
     p, _ = qgg.expert_permute(ids, E)
     inv = p.inv_perm.cpu().numpy()
-    wd = dev_weights(1, packed, scales)
-    for variant in (qgg.FUSED, qgg.CHUNKED):
+    for layout, variant in [(lo, v) for lo in LAYOUTS for v in (qgg.FUSED, qgg.CHUNKED)]:
+        wd = dev_weights(1, packed, scales, layout=layout)
         y = qgg.dequant_grouped_gemm(wd, dev_bf16(x), p, T, k, variant, 2)
         sync()
         np.testing.assert_array_equal(host_u16(y)[inv], ref_bits)
@@ -236,9 +270,10 @@ def test_transposed_grouped_gemm_parity(fmt):
     ref = oracle.project_t(fmt, packed, scales, a, ids_ref.reshape(-1)[pref["perm"]])
     ids, _ = qgg.moe_route(torch.from_numpy(logits).to(DEV), k)
     p, _ = qgg.expert_permute(ids, E)
-    wd = dev_weights(fmt, packed, scales)
     outs = []
-    for variant, chunk in [(qgg.FUSED, 0), (qgg.CHUNKED, 4), (qgg.CHUNKED, 0)]:
+    for layout, variant, chunk in [(lo, v, c) for lo in LAYOUTS
+                                   for v, c in [(qgg.FUSED, 0), (qgg.CHUNKED, 4), (qgg.CHUNKED, 0)]]:
+        wd = dev_weights(fmt, packed, scales, layout=layout)
         y = qgg.dequant_grouped_gemm(wd, dev_bf16(a), p, T, k, variant, chunk,
                                      flags=qgg.A_SORTED | qgg.TRANSPOSE_W)
         sync()
@@ -273,11 +308,13 @@ def test_moe_ffn_fwd_parity(cfg):
     ids_ref, gates_ref = oracle.route(logits, cfg.k)
     toks = np.arange(cfg.T, dtype=np.int32)
     y_ref, h_ref = oracle.ffn(cfg.fmt, gu, dn, x, ids_ref, gates_ref, toks, want_h=True)
-    wg, wd = dev_weights(cfg.fmt, *gu), dev_weights(cfg.fmt, *dn)
     lt, xd = torch.from_numpy(logits).to(DEV), dev_bf16(x)
     outs = []
-    for variant, chunk in [(qgg.FUSED, 0), (qgg.CHUNKED, cfg.chunks[0]), (qgg.CHUNKED, 1),
-                           (qgg.CHUNKED, 0)]:
+    runs = [(lo, v, c) for lo in LAYOUTS for v, c in
+            [(qgg.FUSED, 0), (qgg.CHUNKED, cfg.chunks[0]), (qgg.CHUNKED, 1), (qgg.CHUNKED, 0)]]
+    for layout, variant, chunk in runs:
+        wg = dev_weights(cfg.fmt, *gu, layout=layout)
+        wd = dev_weights(cfg.fmt, *dn, layout=layout)
         r = qgg.moe_ffn_fwd(wg, wd, xd, lt, cfg.k, variant, chunk, save_h=True)
         sync()
         np.testing.assert_array_equal(r["topk_ids"].cpu().numpy(), ids_ref)
@@ -316,7 +353,11 @@ def test_moe_dx_bwd_parity(cfg):
     fwd = qgg.moe_ffn_fwd(wg, wd, dev_bf16(x), torch.from_numpy(logits).to(DEV), cfg.k,
                           qgg.FUSED, 0, save_h=True)
     outs = []
-    for variant, chunk in [(qgg.FUSED, 0), (qgg.CHUNKED, cfg.chunks[0]), (qgg.CHUNKED, 0)]:
+    runs = [(lo, v, c) for lo in LAYOUTS for v, c in
+            [(qgg.FUSED, 0), (qgg.CHUNKED, cfg.chunks[0]), (qgg.CHUNKED, 0)]]
+    for layout, variant, chunk in runs:
+        wg = dev_weights(cfg.fmt, *gu, layout=layout)
+        wd = dev_weights(cfg.fmt, *dn, layout=layout)
         dx = qgg.moe_dx_bwd(wg, wd, dev_bf16(dy), fwd["topk_gates"], fwd["perm"], fwd["h"],
                             cfg.k, variant, chunk)
         sync()
