@@ -46,9 +46,19 @@ __global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ pac
   const int a = first + slot;
   if (a >= *n_active) return;
   const int64_t e = active[a];
-  const int64_t gi = gid % groups_per_expert;  // n * (K/32) + group
-  const int64_t n = gi / (K / 32);
-  const int64_t g = gi % (K / 32);
+  const int64_t gi = gid % groups_per_expert;
+  int64_t n, g;
+  if (tiled_out) {
+    // threads walk the tiled order (tile, slot L) so that each wavefront's
+    // stores of one piece are one contiguous KiB
+    const int L = (int)(gi & 63);
+    const int64_t tile = gi >> 6;
+    n = (tile / (K / 64)) * 32 + (L & 31);
+    g = (tile % (K / 64)) * 2 + (L >> 5);
+  } else {
+    n = gi / (K / 32);          // row-major order: n * (K/32) + group
+    g = gi % (K / 32);
+  }
   const int64_t src = group_index(layout, e, n, g, N, K);
   const u32x4_t w = reinterpret_cast<const u32x4_t*>(packed)[src];
   uint32_t out[16];
