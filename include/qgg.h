@@ -28,8 +28,12 @@
  *    as a status; nothing aborts.  Data errors found on the device (a
  *    non-finite router logit, an expert id outside [0, E)) set *err_flag to a
  *    nonzero value when err_flag is not NULL; the caller zeroes it first.
- *  - Limits: 1 <= k <= 32, k <= E <= 1024, T*k < 2^31, K % 128 == 0,
- *    N % 64 == 0 (inter % 64 == 0 for the FFN calls).
+ *  - Limits: 1 <= k <= 32, k <= E <= 1024, T*k < 2^31; K % 128 == 0 and
+ *    N % 64 == 0 for dequant_grouped_gemm, d % 128 == 0 and inter % 128 == 0
+ *    for moe_ffn_fwd, d % 256 == 0 and inter % 256 == 0 for moe_dx_bwd; every
+ *    BF16 matrix read as a GEMM A operand (the activations and the P x inter
+ *    or P x 2 inter intermediates) under 4 GiB.  Sizes outside these return
+ *    QGG_ERR_UNSUPPORTED.
  *  - Pair index p = t*k + j names token t's j-th routed expert.  "Sorted
  *    order" lists pairs expert by expert (ascending id), ascending p inside an
  *    expert; row i of a sorted tensor belongs to pair perm[i].

@@ -31,12 +31,61 @@ namespace qgg {
 
 namespace {
 
-constexpr int kKL = 64;                  // K elements per LDS stage (one K step)
-constexpr int kRowB = kKL * 2 + 16;      // padded LDS bytes per A row
-constexpr int kCPR = kKL * 2 / 16;       // 16-byte chunks per row per stage
+constexpr int kKL = 64;                  // K elements per stage (one K step)
+constexpr int kStageRowB = kKL * 2;      // A bytes per tile row per stage
+constexpr int kNBuf = 4;                 // stages in the LDS ring of A tiles
 // weight steps in flight per wavefront (BF16 steps are 4x larger)
 template <int SRC>
 constexpr int ring_depth() { return SRC == kSrcBF16 ? 2 : 4; }
+// vector-memory instructions one stage issues to refill the weight ring
+template <int SRC>
+constexpr int b_loads_per_stage() { return SRC == kSrcBF16 ? 8 : 4; }
+
+// A tiles in LDS: tile row r of a stage is 128 contiguous bytes whose eight
+// 16-byte K chunks are permuted, chunk kc at slot kc ^ swz(r), so that an
+// MFMA operand read (one chunk of 32 consecutive rows) hits distinct banks.
+__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
+
+// s_waitcnt immediate: wait until at most n vector-memory operations are
+// outstanding and all LDS operations are done (gfx9 encoding: vmcnt in bits
+// [3:0] and [15:14], expcnt [6:4] left at its maximum, lgkmcnt [11:8] = 0).
+constexpr int vm_lgkm0_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4); }
+
+// Compiler-only fence: no memory access moves across it; emits nothing.
+__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
+
+// 16 bytes from a buffer -> LDS without a register round trip
+// (buffer_load_dwordx4 ... lds): lane i of the wavefront writes lds + 16 i,
+// so the LDS pointer must be the same for the whole wavefront.  Offsets past
+// the buffer's size read zeros.  (The buffer form, unlike the global one, is
+// tracked by the compiler as an ordinary in-order vector-memory load, so its
+// own waits for register loads keep exact counts.)
+__device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff,
+                                              uint32_t soff, void* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds, 16,
+                                           voff, soff, 0, 0);
+}
+
+// Raw (untyped, unswizzled) buffer resource over [base, base + bytes).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_buffer(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+// Barrier between two stages of the A ring.  A wavefront first waits until
+// at most N of its vector-memory operations are outstanding -- those are the
+// loads of the two most recent stages, so its copies of the next stage's A
+// tile have landed while the younger copies and weight loads stay in flight
+// -- then meets the others.  No memory fence: at workgroup scope one would
+// drain every outstanding load, LDS copies included.
+template <int N>
+__device__ __forceinline__ void stage_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  compiler_fence();
+  __builtin_amdgcn_s_waitcnt(vm_lgkm0_imm(N));
+  __builtin_amdgcn_s_barrier();
+  compiler_fence();
+}
 
 __device__ __forceinline__ uint16_t bf16_hw(float v) {
   return __builtin_bit_cast(uint16_t, (__bf16)v);
@@ -143,38 +192,56 @@ __device__ __forceinline__ bf16x8_t b_operand(const BRegs<SRC>& r, const BScale<
 
 // One work item: tile (expert, rows [row0, row0 + nrows)) x 256 output
 // columns, with NMB live 32-row blocks.  The K loop is branch-free: every
-// load index is clamped into range instead of guarded, so the compiler can
-// keep exact vmcnt counts and the weight ring stays in flight across the
-// workgroup barriers.
+// load index is clamped into range instead of guarded, so the compiler keeps
+// exact vmcnt counts.  Both operand streams run ahead of the MFMAs: the A
+// tile is copied global -> LDS kNBuf - 1 stages ahead into a ring of kNBuf
+// stage buffers, the weights ring_depth steps ahead into registers, and the
+// stage barrier waits only for the copies of the next stage.
 template <int SRC, int MB, int EPI, int AMODE, int NMB>
-__device__ __forceinline__ void gemm_nt_item(const GemmArgs& g, uint8_t (*As)[32 * MB * kRowB],
-                                             int4 tile, int nt) {
-  constexpr int MT = 32 * MB;
-  constexpr int NCH = MT * kCPR / 256;   // A chunks per thread per stage
+__device__ __forceinline__ void gemm_nt_item(const GemmArgs& g,
+                                             uint8_t (*As)[32 * MB * kStageRowB], int4 tile,
+                                             int nt) {
   constexpr int kRing = ring_depth<SRC>();
+  constexpr int kBL = b_loads_per_stage<SRC>();
+  constexpr int kStageLoads = NMB + kBL;            // vector-memory ops per stage
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int col = lane & 31;
   const int half = lane >> 5;
   const int nsteps = g.K / kKL;
   const int expert = tile.x, row0 = tile.y, nrows = tile.z;
 
-  // A sources and LDS destinations of this thread's 16-byte chunks
-  const uint16_t* asrc[NCH];
-  int adst[NCH];
+  // A copies: 16-byte slot p = 256 i + tid of a stage (i < NMB: block i
+  // covers tile rows 32 i .. 32 i + 31) receives K chunk (p & 7) ^ swz(r) of
+  // tile row r = p >> 3; rows past the tile's end copy its first row
+  // (byte offsets into the A buffer; the host keeps A under 4 GiB)
+  const __amdgpu_buffer_rsrc_t arsrc = raw_buffer(g.a, (uint32_t)(g.a_rows * g.lda * 2));
+  uint32_t aoffs[NMB];
 #pragma unroll
-  for (int i = 0; i < NCH; ++i) {
-    const int c = tid + 256 * i;
-    const int r = c / kCPR;
-    const int cc = c % kCPR;
+  for (int i = 0; i < NMB; ++i) {
+    const int p = 256 * i + tid;
+    const int r = p >> 3;
+    const int kc = (p & 7) ^ swz(r);
     const int rr = r < nrows ? r : 0;
     int64_t srow;
     if constexpr (AMODE == kATokens) srow = g.perm[row0 + rr] / g.topk;
     else srow = row0 + rr;
-    asrc[i] = g.a + srow * g.lda + cc * 8;
-    adst[i] = r * kRowB + cc * 16;
+    aoffs[i] = (uint32_t)((srow * g.lda + kc * 8) * 2);
   }
+  auto copy_a = [&](int st, auto buf_c) {
+    constexpr int BUF = decltype(buf_c)::value;
+    const uint32_t soff = (uint32_t)((st < nsteps ? st : nsteps - 1) * kStageRowB);
+#pragma unroll
+    for (int i = 0; i < NMB; ++i)
+      copy16_to_lds(arsrc, aoffs[i], soff, &As[BUF][(256 * i + 64 * wave) * 16]);
+  };
+  // LDS offsets of this lane's A operand chunks (row col of a block, K chunk
+  // 4 half + s): the chunk's slot is xb ^ c with c = s ^ 4 (mb & 1)
+  const int xb = (half << 2) ^ swz(col);
+  int aoff[8];
+#pragma unroll
+  for (int c = 0; c < 8; ++c) aoff[c] = col * kStageRowB + ((xb ^ c) << 4);
 
   // this wave's two 32-column blocks (W rows); a wave past the matrix edge
   // computes on clamped rows and stores nothing
@@ -205,51 +272,54 @@ __device__ __forceinline__ void gemm_nt_item(const GemmArgs& g, uint8_t (*As)[32
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[mb][nb][i] = 0.f;
 
-  // Weight stream: a ring of kRing 64-wide K steps held in registers.  A
-  // slot is refilled with the step kRing ahead as soon as its last operand
-  // is decoded, so the loads run kRing steps ahead of use.
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+
+  // Prologue: A stages 0, 1, 2, then the weight ring (kRing steps).  The
+  // fences pin that issue order: waiting for all but the loads issued after
+  // stage 0's copies lands stage 0, and the stage barriers below can count
+  // on at least 2 kStageLoads loads being younger than stage 1's or 2's
+  // copies.
   BRegs<SRC> ring[kRing][2];
+  copy_a(0, I0{});
+  compiler_fence();
+  copy_a(1, I1{});
+  compiler_fence();
+  copy_a(2, I2{});
+  compiler_fence();
 #pragma unroll
   for (int r = 0; r < kRing; ++r) {
     const int st = r < nsteps ? r : nsteps - 1;
     load_b<SRC>(bs0, st, ring[r][0]);
     load_b<SRC>(bs1, st, ring[r][1]);
   }
-  u32x4_t areg[NCH];
-#pragma unroll
-  for (int i = 0; i < NCH; ++i) areg[i] = *reinterpret_cast<const u32x4_t*>(asrc[i]);
-#pragma unroll
-  for (int i = 0; i < NCH; ++i) *reinterpret_cast<u32x4_t*>(&As[0][adst[i]]) = areg[i];
-  __syncthreads();
+  static_assert(kRing * kBL >= kStageLoads, "prologue leaves too few younger loads");
+  stage_barrier<2 * NMB + kRing * kBL>();
 
-  // one 64-wide K step; SUB = step parity (two steps per LDS stage), BUF =
-  // the LDS buffer of the step's stage; both are compile-time here
-  auto kstep = [&](int step, BRegs<SRC>(&slot)[2], auto sub_c, auto buf_c) {
-    constexpr int SUB = decltype(sub_c)::value;
+  // one stage = one 64-wide K step; BUF = stage % kNBuf (compile-time)
+  auto kstage = [&](int step, BRegs<SRC>(&slot)[2], auto buf_c) {
     constexpr int BUF = decltype(buf_c)::value;
-    {
-      const int nx = step + 1 < nsteps ? step + 1 : step;
-#pragma unroll
-      for (int i = 0; i < NCH; ++i)
-        areg[i] = *reinterpret_cast<const u32x4_t*>(asrc[i] + nx * kKL);
-    }
+    copy_a(step + kNBuf - 1, std::integral_constant<int, (BUF + kNBuf - 1) % kNBuf>{});
     const BScale<SRC> sc0 = b_scale<SRC>(slot[0]);
     const BScale<SRC> sc1 = b_scale<SRC>(slot[1]);
+    const uint8_t* at = As[BUF];
+    auto a_op = [&](int mb, int s) {
+      return *reinterpret_cast<const bf16x8_t*>(at + mb * 32 * kStageRowB +
+                                                aoff[s ^ ((mb & 1) << 2)]);
+    };
     // A operands: double-buffered across the four K sub-steps when the
     // tile is short; loaded just in time when registers are scarce
-    constexpr bool kDbl = NMB <= 2;
+    constexpr bool kDbl = NMB <= 3;
     bf16x8_t acur[NMB], anxt[NMB];
 #pragma unroll
-    for (int mb = 0; mb < NMB; ++mb)
-      acur[mb] = *reinterpret_cast<const bf16x8_t*>(
-          &As[BUF][(mb * 32 + col) * kRowB + (half * 32) * 2]);
+    for (int mb = 0; mb < NMB; ++mb) acur[mb] = a_op(mb, 0);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       if (kDbl && s < 3) {
 #pragma unroll
-        for (int mb = 0; mb < NMB; ++mb)
-          anxt[mb] = *reinterpret_cast<const bf16x8_t*>(
-              &As[BUF][(mb * 32 + col) * kRowB + (half * 32 + (s + 1) * 8) * 2]);
+        for (int mb = 0; mb < NMB; ++mb) anxt[mb] = a_op(mb, s + 1);
       }
       const bf16x8_t b0 = b_operand<SRC>(slot[0], sc0, s);
       const bf16x8_t b1 = b_operand<SRC>(slot[1], sc1, s);
@@ -260,9 +330,7 @@ __device__ __forceinline__ void gemm_nt_item(const GemmArgs& g, uint8_t (*As)[32
       }
 #pragma unroll
       for (int mb = 0; mb < NMB; ++mb) {
-        if (!kDbl && s > 0)
-          acur[mb] = *reinterpret_cast<const bf16x8_t*>(
-              &As[BUF][(mb * 32 + col) * kRowB + (half * 32 + s * 8) * 2]);
+        if (!kDbl && s > 0) acur[mb] = a_op(mb, s);
         acc[mb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(acur[mb], b0, acc[mb][0], 0, 0, 0);
         acc[mb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(acur[mb], b1, acc[mb][1], 0, 0, 0);
       }
@@ -271,36 +339,24 @@ __device__ __forceinline__ void gemm_nt_item(const GemmArgs& g, uint8_t (*As)[32
         for (int mb = 0; mb < NMB; ++mb) acur[mb] = anxt[mb];
       }
     }
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) *reinterpret_cast<u32x4_t*>(&As[BUF ^ 1][adst[i]]) = areg[i];
-    __syncthreads();
-    (void)sub_c;
+    // the copies of stage step + 1 were issued two stages ago
+    stage_barrier<2 * kStageLoads>();
   };
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
 
   int base = 0;
-  if constexpr (kRing == 4) {
-    for (; base + 4 <= nsteps; base += 4) {
-      kstep(base + 0, ring[0], I0{}, I0{});
-      kstep(base + 1, ring[1], I1{}, I1{});
-      kstep(base + 2, ring[2], I0{}, I0{});
-      kstep(base + 3, ring[3], I1{}, I1{});
-    }
-    if (base < nsteps) {                 // two steps left (K % 128 == 0)
-      kstep(base + 0, ring[0], I0{}, I0{});
-      kstep(base + 1, ring[1], I1{}, I1{});
-    }
-  } else {
-    for (; base < nsteps; base += 4) {   // kRing == 2: slots alternate per step
-      kstep(base + 0, ring[0], I0{}, I0{});
-      kstep(base + 1, ring[1], I1{}, I1{});
-      if (base + 2 < nsteps) {
-        kstep(base + 2, ring[0], I0{}, I0{});
-        kstep(base + 3, ring[1], I1{}, I1{});
-      }
-    }
+  for (; base + 4 <= nsteps; base += 4) {
+    kstage(base + 0, ring[0], I0{});
+    kstage(base + 1, ring[1 % kRing], I1{});
+    kstage(base + 2, ring[2 % kRing], I2{});
+    kstage(base + 3, ring[3 % kRing], I3{});
   }
+  if (base < nsteps) {                   // two steps left (K % 128 == 0)
+    kstage(base + 0, ring[0], I0{});
+    kstage(base + 1, ring[1 % kRing], I1{});
+  }
+  // drain the clamped copies past the last stage before the LDS ring is
+  // reused by the next item
+  __builtin_amdgcn_s_waitcnt(vm_lgkm0_imm(0));
 
   if (!active) return;
   // epilogue: lane holds column `col` of rows 8i + 4*half + j of each block
@@ -333,7 +389,7 @@ __device__ __forceinline__ void gemm_nt_item(const GemmArgs& g, uint8_t (*As)[32
 
 template <int SRC, int MB, int EPI, int AMODE>
 __global__ __launch_bounds__(256, 2) void k_gemm_nt(GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) uint8_t As[2][32 * MB * kRowB];
+  __shared__ __attribute__((aligned(16))) uint8_t As[kNBuf][32 * MB * kStageRowB];
   const int t_begin = g.range[0];
   const int t_end = g.range[1];
   const int n_tiles_n = EPI == kEpiSwiGLU ? (g.inter + 127) / 128 : (g.N + 255) / 256;

@@ -88,6 +88,10 @@ bool valid_route_dims(int T, int E, int k) {
          (int64_t)T * k < (int64_t)1 << 31;
 }
 
+// The GEMM kernels address each A operand (activations, intermediates)
+// through a 32-bit buffer offset.
+bool a_fits(int64_t rows, int64_t ld) { return rows * ld * 2 <= (int64_t)0xFFFFFFFF; }
+
 PermPtrs to_ptrs(const qgg_perm* p) {
   return PermPtrs{p->counts, p->offsets, p->perm, p->inv_perm, p->active, p->n_active};
 }
@@ -251,6 +255,7 @@ qgg_status dequant_grouped_gemm(const qgg_qweight* w, const uint16_t* a, int fla
   if (dq_only && variant != QGG_CHUNKED) return QGG_ERR_INVALID_ARG;
   if (!dq_only && (!a || !y) && T > 0) return QGG_ERR_INVALID_ARG;
   const int64_t P = (int64_t)T * k;
+  if (!a_fits((flags & QGG_A_TOKENS) ? T : P, trans ? N : K)) return QGG_ERR_UNSUPPORTED;
   size_t scratch = 0;
   const size_t need = qgg_workspace_bytes(QGG_CALL_GEMM, T, K, E, k, N, variant, chunk, &scratch);
   if (!workspace || ws_bytes < need) return QGG_ERR_WORKSPACE_TOO_SMALL;
@@ -273,6 +278,7 @@ qgg_status dequant_grouped_gemm(const qgg_qweight* w, const uint16_t* a, int fla
   g.a = a;
   g.lda = trans ? N : K;
   g.amode = (flags & QGG_A_TOKENS) ? kATokens : kASorted;
+  g.a_rows = g.amode == kATokens ? T : P;
   g.perm = p->perm;
   g.topk = k;
   g.y = y;
@@ -314,6 +320,7 @@ qgg_status moe_ffn_fwd(const qgg_qweight* w_gate_up, const qgg_qweight* w_down,
   if (T > 0 && (!x || !logits || !topk_ids || !topk_gates || !y)) return QGG_ERR_INVALID_ARG;
   if (d % 128 || inter % 128) return QGG_ERR_UNSUPPORTED;
   const int64_t P = (int64_t)T * k;
+  if (!a_fits(T, d) || !a_fits(P, inter)) return QGG_ERR_UNSUPPORTED;
   size_t scratch = 0;
   const size_t need =
       qgg_workspace_bytes(QGG_CALL_FFN_FWD, T, d, E, k, inter, variant, chunk, &scratch);
@@ -337,6 +344,7 @@ qgg_status moe_ffn_fwd(const qgg_qweight* w_gate_up, const qgg_qweight* w_down,
   GemmArgs gu = base_args(w_gate_up, pl);
   gu.a = x;
   gu.lda = d;
+  gu.a_rows = T;
   gu.amode = kATokens;
   gu.perm = p->perm;
   gu.topk = k;
@@ -348,6 +356,7 @@ qgg_status moe_ffn_fwd(const qgg_qweight* w_gate_up, const qgg_qweight* w_down,
   GemmArgs dn = base_args(w_down, pl);
   dn.a = abuf;
   dn.lda = inter;
+  dn.a_rows = P;
   dn.amode = kASorted;
   dn.perm = p->perm;
   dn.topk = k;
@@ -397,6 +406,7 @@ qgg_status moe_dx_bwd(const qgg_qweight* w_gate_up, const qgg_qweight* w_down,
   if (T > 0 && (!dy || !topk_gates || !h_saved || !dx)) return QGG_ERR_INVALID_ARG;
   if (d % 256 || inter % 256) return QGG_ERR_UNSUPPORTED;
   const int64_t P = (int64_t)T * k;
+  if (!a_fits(T, d) || !a_fits(P, 2 * inter)) return QGG_ERR_UNSUPPORTED;
   size_t scratch = 0;
   const size_t need =
       qgg_workspace_bytes(QGG_CALL_DX_BWD, T, d, E, k, inter, variant, chunk, &scratch);
@@ -417,6 +427,7 @@ qgg_status moe_dx_bwd(const qgg_qweight* w_gate_up, const qgg_qweight* w_down,
   GemmArgs dn = base_args(w_down, pl);
   dn.a = dy;
   dn.lda = d;
+  dn.a_rows = T;
   dn.amode = kATokens;
   dn.perm = p->perm;
   dn.topk = k;
@@ -430,6 +441,7 @@ qgg_status moe_dx_bwd(const qgg_qweight* w_gate_up, const qgg_qweight* w_down,
   GemmArgs gu = base_args(w_gate_up, pl);
   gu.a = dh;
   gu.lda = 2 * inter;
+  gu.a_rows = P;
   gu.amode = kASorted;
   gu.perm = p->perm;
   gu.topk = k;

@@ -33,6 +33,7 @@ struct GemmArgs {
   // rows (A operand)
   const uint16_t* a;
   int lda;
+  int64_t a_rows;                // rows of the A matrix (bounds its buffer resource)
   int amode;                     // AMode
   const int32_t* perm;
   int topk;
