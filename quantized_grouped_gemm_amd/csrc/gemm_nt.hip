@@ -46,47 +46,6 @@ constexpr int b_loads_per_stage() { return SRC == kSrcBF16 ? 8 : 4; }
 // MFMA operand read (one chunk of 32 consecutive rows) hits distinct banks.
 __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
 
-// s_waitcnt immediate: wait until at most n vector-memory operations are
-// outstanding and all LDS operations are done (gfx9 encoding: vmcnt in bits
-// [3:0] and [15:14], expcnt [6:4] left at its maximum, lgkmcnt [11:8] = 0).
-constexpr int vm_lgkm0_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4); }
-
-// Compiler-only fence: no memory access moves across it; emits nothing.
-__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
-
-// 16 bytes from a buffer -> LDS without a register round trip
-// (buffer_load_dwordx4 ... lds): lane i of the wavefront writes lds + 16 i,
-// so the LDS pointer must be the same for the whole wavefront.  Offsets past
-// the buffer's size read zeros.  (The buffer form, unlike the global one, is
-// tracked by the compiler as an ordinary in-order vector-memory load, so its
-// own waits for register loads keep exact counts.)
-__device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff,
-                                              uint32_t soff, void* lds) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds, 16,
-                                           voff, soff, 0, 0);
-}
-
-// Raw (untyped, unswizzled) buffer resource over [base, base + bytes).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_buffer(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
-                                           0x00020000);
-}
-
-// Barrier between two stages of the A ring.  A wavefront first waits until
-// at most N of its vector-memory operations are outstanding -- those are the
-// loads of the two most recent stages, so its copies of the next stage's A
-// tile have landed while the younger copies and weight loads stay in flight
-// -- then meets the others.  No memory fence: at workgroup scope one would
-// drain every outstanding load, LDS copies included.
-template <int N>
-__device__ __forceinline__ void stage_barrier() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  compiler_fence();
-  __builtin_amdgcn_s_waitcnt(vm_lgkm0_imm(N));
-  __builtin_amdgcn_s_barrier();
-  compiler_fence();
-}
-
 __device__ __forceinline__ uint16_t bf16_hw(float v) {
   return __builtin_bit_cast(uint16_t, (__bf16)v);
 }
@@ -98,58 +57,66 @@ struct BRegs {
                    // refill never waits for its own load
 };
 
-// Per-lane weight stream: byte pointers to this lane's first K step and the
-// byte strides from one 64-wide K step to the next.
+// Per-lane weight stream: buffer resources over one expert's (or BF16
+// slot's) weight and scale bytes, this lane's byte offsets at K step 0, and
+// the wave-uniform byte strides from one 64-wide K step to the next (so a
+// step's address is a scalar add, and offsets past the slice read zeros).
 struct BStream {
-  const uint8_t* w;
-  const uint8_t* s;
-  int64_t wstep, sstep;
+  __amdgpu_buffer_rsrc_t w, s;
+  uint32_t wv, sv;
+  int wstep, sstep;
 };
 
 template <int SRC>
 __device__ __forceinline__ void load_b(const BStream& b, int step, BRegs<SRC>& r) {
-  const uint8_t* wp = b.w + step * b.wstep;
   if constexpr (SRC == kSrcBF16) {
     // tiled BF16: the four 8-element pieces of a lane sit 1 KiB apart
 #pragma unroll
-    for (int s = 0; s < 4; ++s) r.w[s] = *reinterpret_cast<const u32x4_t*>(wp + s * 1024);
+    for (int s = 0; s < 4; ++s)
+      r.w[s] = __builtin_amdgcn_raw_buffer_load_b128(b.w, b.wv + s * 1024, step * b.wstep, 0);
   } else {
-    r.w[0] = *reinterpret_cast<const u32x4_t*>(wp);
-    const uint8_t* sp = b.s + step * b.sstep;
-    if constexpr (SRC == kSrcMXFP4) r.sraw = *sp;
-    else r.sraw = *reinterpret_cast<const uint16_t*>(sp);
+    r.w[0] = __builtin_amdgcn_raw_buffer_load_b128(b.w, b.wv, step * b.wstep, 0);
+    if constexpr (SRC == kSrcMXFP4)
+      r.sraw = __builtin_amdgcn_raw_buffer_load_b8(b.s, b.sv, step * b.sstep, 0);
+    else
+      r.sraw = __builtin_amdgcn_raw_buffer_load_b16(b.s, b.sv, step * b.sstep, 0);
   }
 }
 
-// Stream of W row `wrow` (a multiple-of-32 block plus this lane's column) for
-// lane `lane` = 32 * half + col.
+// Stream of W rows 32 cb .. 32 cb + 31 (cb wave-uniform) for lane
+// `lane` = 32 * half + col, which reads row 32 cb + col.
 template <int SRC>
-__device__ __forceinline__ BStream make_stream(const GemmArgs& g, int64_t expert_or_slot,
-                                               int wrow, int lane) {
+__device__ __forceinline__ BStream make_stream(const GemmArgs& g, int64_t expert_or_slot, int cb,
+                                               int lane) {
   BStream b;
-  const int64_t nkt = g.K / 64;                // K steps
-  const int64_t cb = wrow >> 5;
+  const int nkt = g.K / 64;                    // K steps
   const int half = lane >> 5;
+  const int col = lane & 31;
   if constexpr (SRC == kSrcBF16) {
-    b.w = reinterpret_cast<const uint8_t*>(g.wbf16) +
-          ((expert_or_slot * (g.N / 32) + cb) * nkt * 4096) + lane * 16;
+    const uint32_t bytes = (uint32_t)g.N * (uint32_t)g.K * 2u;
+    b.w = raw_buffer(reinterpret_cast<const uint8_t*>(g.wbf16) + expert_or_slot * bytes, bytes);
+    b.s = b.w;
+    b.wv = (uint32_t)(cb * nkt) * 4096u + lane * 16;
     b.wstep = 4096;
-    b.s = nullptr;
+    b.sv = 0;
     b.sstep = 0;
   } else {
     const int sb = SRC == kSrcMXFP4 ? 1 : 2;
-    const uint8_t* sc = static_cast<const uint8_t*>(g.scales);
-    if (g.layout == 1) {   // MFMA-tiled
-      const int64_t t0 = (expert_or_slot * (g.N / 32) + cb) * nkt;
-      b.w = g.packed + t0 * 1024 + lane * 16;
+    const uint32_t wbytes = (uint32_t)g.N * (uint32_t)(g.K / 2);
+    const uint32_t sbytes = (uint32_t)g.N * (uint32_t)(g.K / 32) * sb;
+    b.w = raw_buffer(g.packed + expert_or_slot * wbytes, wbytes);
+    b.s = raw_buffer(static_cast<const uint8_t*>(g.scales) + expert_or_slot * sbytes, sbytes);
+    if (g.layout == 1) {   // MFMA-tiled: 1 KiB per (32 rows, 64 K) tile
+      const uint32_t t0 = (uint32_t)(cb * nkt);
+      b.wv = t0 * 1024u + lane * 16;
       b.wstep = 1024;
-      b.s = sc + (t0 * 64 + lane) * sb;
+      b.sv = (t0 * 64u + lane) * sb;
       b.sstep = 64 * sb;
     } else {               // rows
-      const int64_t row = expert_or_slot * g.N + wrow;
-      b.w = g.packed + row * (g.K / 2) + half * 16;
+      const uint32_t row = (uint32_t)(cb * 32 + col);
+      b.wv = row * (uint32_t)(g.K / 2) + half * 16;
       b.wstep = 32;
-      b.s = sc + (row * (g.K / 32) + half) * sb;
+      b.sv = (row * (uint32_t)(g.K / 32) + half) * sb;
       b.sstep = 2 * sb;
     }
   }
@@ -199,7 +166,7 @@ __device__ __forceinline__ bf16x8_t b_operand(const BRegs<SRC>& r, const BScale<
 // stage barrier waits only for the copies of the next stage.
 template <int SRC, int MB, int EPI, int AMODE, int NMB>
 __device__ __forceinline__ void gemm_nt_item(const GemmArgs& g,
-                                             uint8_t (*As)[32 * MB * kStageRowB], int4 tile,
+                                             const LdsRing4& As, int4 tile,
                                              int nt) {
   constexpr int kRing = ring_depth<SRC>();
   constexpr int kBL = b_loads_per_stage<SRC>();
@@ -234,7 +201,7 @@ __device__ __forceinline__ void gemm_nt_item(const GemmArgs& g,
     const uint32_t soff = (uint32_t)((st < nsteps ? st : nsteps - 1) * kStageRowB);
 #pragma unroll
     for (int i = 0; i < NMB; ++i)
-      copy16_to_lds(arsrc, aoffs[i], soff, &As[BUF][(256 * i + 64 * wave) * 16]);
+      copy16_to_lds(arsrc, aoffs[i], soff, As.b[BUF] + (256 * i + 64 * wave) * 16);
   };
   // LDS offsets of this lane's A operand chunks (row col of a block, K chunk
   // 4 half + s): the chunk's slot is xb ^ c with c = s ^ 4 (mb & 1)
@@ -243,26 +210,30 @@ __device__ __forceinline__ void gemm_nt_item(const GemmArgs& g,
 #pragma unroll
   for (int c = 0; c < 8; ++c) aoff[c] = col * kStageRowB + ((xb ^ c) << 4);
 
-  // this wave's two 32-column blocks (W rows); a wave past the matrix edge
-  // computes on clamped rows and stores nothing
-  int wrow0, wrow1, ocol;
+  // this wave's two 32-column blocks (W rows 32 cb0.., 32 cb1..; wave-
+  // uniform); a wave past the matrix edge computes on clamped rows and
+  // stores nothing
+  int cb0, cb1, ocol;
   bool active;
   if constexpr (EPI == kEpiSwiGLU) {
     const int base = nt * 128 + wave * 32;
     active = base < g.inter;
-    ocol = active ? base + col : g.inter - 32 + col;
-    wrow0 = ocol;
-    wrow1 = g.inter + ocol;
+    const int cbase = active ? base : g.inter - 32;
+    ocol = cbase + col;
+    cb0 = cbase >> 5;                  // gate rows
+    cb1 = (g.inter + cbase) >> 5;      // up rows
   } else {
     const int base = nt * 256 + wave * 64;
     active = base < g.N;
-    ocol = active ? base + col : g.N - 64 + col;
-    wrow0 = ocol;
-    wrow1 = ocol + 32;
+    const int cbase = active ? base : g.N - 64;
+    ocol = cbase + col;
+    cb0 = cbase >> 5;
+    cb1 = cb0 + 1;
   }
+  const int wrow0 = cb0 * 32 + col, wrow1 = cb1 * 32 + col;
   const int64_t wsel = SRC == kSrcBF16 ? (int64_t)(tile.w - g.bf16_slot_base) : (int64_t)expert;
-  const BStream bs0 = make_stream<SRC>(g, wsel, wrow0, lane);
-  const BStream bs1 = make_stream<SRC>(g, wsel, wrow1, lane);
+  const BStream bs0 = make_stream<SRC>(g, wsel, cb0, lane);
+  const BStream bs1 = make_stream<SRC>(g, wsel, cb1, lane);
 
   f32x16_t acc[NMB][2];
 #pragma unroll
@@ -304,7 +275,7 @@ __device__ __forceinline__ void gemm_nt_item(const GemmArgs& g,
     copy_a(step + kNBuf - 1, std::integral_constant<int, (BUF + kNBuf - 1) % kNBuf>{});
     const BScale<SRC> sc0 = b_scale<SRC>(slot[0]);
     const BScale<SRC> sc1 = b_scale<SRC>(slot[1]);
-    const uint8_t* at = As[BUF];
+    const uint8_t* at = As.b[BUF];
     auto a_op = [&](int mb, int s) {
       return *reinterpret_cast<const bf16x8_t*>(at + mb * 32 * kStageRowB +
                                                 aoff[s ^ ((mb & 1) << 2)]);
@@ -337,6 +308,17 @@ __device__ __forceinline__ void gemm_nt_item(const GemmArgs& g,
       if (kDbl && s < 3) {
 #pragma unroll
         for (int mb = 0; mb < NMB; ++mb) acur[mb] = anxt[mb];
+      }
+    }
+    if constexpr (SRC != kSrcBF16) {
+      // schedule the stage as MFMA, up to kV VALU, MFMA, ... so that the
+      // decode of the next sub-step runs on the vector ALU while the matrix
+      // core works (the compiler otherwise bunches the decode)
+      constexpr int kV = (28 + NMB - 1) / NMB;
+#pragma unroll
+      for (int i = 0; i < 8 * NMB; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, kV, 0);
       }
     }
     // the copies of stage step + 1 were issued two stages ago
@@ -387,9 +369,19 @@ __device__ __forceinline__ void gemm_nt_item(const GemmArgs& g,
   }
 }
 
+// workgroups per CU: short tiles (decode-sized expert groups) need fewer
+// registers, and a third workgroup keeps more weight loads in flight
+template <int MB>
+constexpr int nt_occupancy() { return MB == 1 ? 3 : 2; }
+
 template <int SRC, int MB, int EPI, int AMODE>
-__global__ __launch_bounds__(256, 2) void k_gemm_nt(GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) uint8_t As[kNBuf][32 * MB * kStageRowB];
+__global__ __launch_bounds__(256, nt_occupancy<MB>()) void k_gemm_nt(GemmArgs g) {
+  __shared__ __attribute__((aligned(16))) uint8_t A0[32 * MB * kStageRowB];
+  __shared__ __attribute__((aligned(16))) uint8_t A1[32 * MB * kStageRowB];
+  __shared__ __attribute__((aligned(16))) uint8_t A2[32 * MB * kStageRowB];
+  __shared__ __attribute__((aligned(16))) uint8_t A3[32 * MB * kStageRowB];
+  const LdsRing4 As{{A0, A1, A2, A3}};
+  static_assert(kNBuf == 4, "four A stage buffers");
   const int t_begin = g.range[0];
   const int t_end = g.range[1];
   const int n_tiles_n = EPI == kEpiSwiGLU ? (g.inter + 127) / 128 : (g.N + 255) / 256;
@@ -419,7 +411,7 @@ hipError_t launch_nt_t(const GemmArgs& g, hipStream_t s) {
   const int n_tiles_n = EPI == kEpiSwiGLU ? (g.inter + 127) / 128 : (g.N + 255) / 256;
   const int64_t bound = (int64_t)g.max_tiles * n_tiles_n;
   if (bound <= 0) return hipSuccess;
-  int64_t grid = std::min<int64_t>(bound, (int64_t)num_cus() * 2);
+  int64_t grid = std::min<int64_t>(bound, (int64_t)num_cus() * nt_occupancy<MB>());
   grid = (grid + 7) / 8 * 8;
   hipLaunchKernelGGL((k_gemm_nt<SRC, MB, EPI, AMODE>), dim3((unsigned)grid), dim3(256), 0, s, g);
   return hipGetLastError();

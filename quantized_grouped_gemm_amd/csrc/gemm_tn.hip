@@ -9,13 +9,18 @@
 //
 // Work decomposition: as the forward kernel (persistent grid, XCD-contiguous
 // item ranges, 4 wavefronts x 64 output columns, v_mfma_f32_32x32x16_bf16),
-// but both operands are staged through double-buffered LDS, 32 reduction
-// rows per stage.  Each stage's weight tile (32 W rows x 256 columns) is
-// loaded once per workgroup with each thread taking two adjacent rows and 16
-// columns; the decoded values are paired row-wise with v_perm_b32 and written
-// column-major, so a B operand (8 consecutive reduction rows of one column) is
-// one 16-byte LDS read.  The SwiGLU-backward epilogue applies the gate and the
-// SwiGLU derivative from the saved forward activations.
+// with 32 reduction rows (W rows) per stage:
+//  - A (rows of the routed activations) is copied global -> LDS three stages
+//    ahead into a ring of four stage buffers, as in the forward kernel;
+//  - each stage's weight tile (32 W rows x 256 columns) is loaded once per
+//    workgroup, one 32-element scale group per thread (a single 16-byte load
+//    and one scale), decoded to BF16 and stored row-major in LDS one stage
+//    ahead of use;
+//  - the MFMA B operand (8 consecutive W rows of one column) is read back with
+//    two transposing LDS reads (ds_read_b64_tr_b16), so no register shuffle
+//    is needed to turn rows into columns.
+// The SwiGLU-backward epilogue applies the gate and the SwiGLU derivative
+// from the saved forward activations.
 #include "qgg_device.hpp"
 #include "qgg_internal.hpp"
 
@@ -25,160 +30,214 @@ namespace qgg {
 
 namespace {
 
-constexpr int kKR = 32;               // reduction rows per stage
-constexpr int kRowBT = kKR * 2 + 16;  // padded LDS bytes per row (A) / column (B)
-// B columns get an extra 64 bytes every 16 columns so that the 64 lanes of a
-// wavefront writing (row pair, column) words hit 64 distinct banks.
-constexpr int kBsBytes = 256 * kRowBT + 16 * 64;
-__device__ __forceinline__ int bcol(int c) { return c * kRowBT + (c >> 4) * 64; }
+constexpr int kKR = 32;                   // reduction rows per stage
+constexpr int kNBufA = 4;                 // stages in the LDS ring of A tiles
+constexpr int kARowB = kKR * 2;           // A bytes per tile row per stage
+// A stage buffer: MT rows, but at least the 4 KiB one round of 16-byte copies
+// by 256 threads fills
+template <int MB>
+constexpr int a_stage_bytes() { return 32 * MB * kARowB > 4096 ? 32 * MB * kARowB : 4096; }
+// B tile: 32 rows of 256 BF16 columns; the 16-byte piece P of row r is
+// stored at piece position P ^ swz_b(r), which keeps both the transposing
+// reads (4 rows x 32 bytes per 16 lanes) and the row stores (8 rows x 16
+// bytes per 8 lanes) free of bank conflicts.
+constexpr int kBRowB = 256 * 2;
+constexpr int kBStage = kKR * kBRowB;
+__device__ __forceinline__ int swz_b(int r) { return 2 * (r & 3) + ((r >> 2) & 1); }
+// weight stages in flight per thread (BF16 stages are 4x larger)
+template <int SRC>
+constexpr int tn_ring_depth() { return SRC == kSrcBF16 ? 2 : 4; }
+// vector-memory instructions one stage issues for the weight ring
+template <int SRC>
+constexpr int tn_b_loads() { return SRC == kSrcBF16 ? 4 : 2; }
+
+// A chunk slot of tile row r: its four 16-byte K chunks are permuted (chunk
+// kc at slot kc ^ swz_a(r)) so that operand reads of 32 consecutive rows hit
+// distinct banks.
+__device__ __forceinline__ int swz_a(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
 
 __device__ __forceinline__ uint16_t bf16_hw_t(float v) {
   return __builtin_bit_cast(uint16_t, (__bf16)v);
 }
 
 template <int SRC>
-struct BStage {
-  // two W rows, 16 columns each
-  uint32_t p[SRC == kSrcBF16 ? 16 : 4];
-  uint32_t sraw0, sraw1;   // raw scale bits, converted when decoding
+struct BGroup {
+  u32x4_t w[SRC == kSrcBF16 ? 4 : 1];   // one row's 32 consecutive columns
+  uint32_t sraw;                        // raw scale bits
+};
+
+// This thread's slice of the weight stream: W row 32 st + jr, columns
+// c0 + 32 sg .. + 31, i.e. one 32-element scale group per stage.  Offsets
+// are bytes within one expert's (or BF16 slot's) weights; a stage adds the
+// wave-uniform wstep / sstep.
+struct BStreamT {
+  __amdgpu_buffer_rsrc_t w, s;
+  uint32_t wv, sv;
+  int wstep, sstep;
 };
 
 template <int SRC>
-__device__ __forceinline__ void load_bt(const GemmArgs& g, int64_t slot_or_expert, int r,
-                                        int c, BStage<SRC>& b) {
-  // rows r, r+1 of W (reduction index), columns c..c+15 (W's K index)
-  // element (n, k) of an MFMA-tiled tensor: tile (n / 32, k / 64), slot
-  // 32 * ((k % 64) / 32) + n % 32; rows r and r + 1 are adjacent slots
-  const int64_t cb = r >> 5;
-  const int64_t j = c >> 6;
-  const int lslot = ((c & 63) >> 5) * 32 + (r & 31);
-  const int64_t tile = (slot_or_expert * (g.N / 32) + cb) * (g.K / 64) + j;
+__device__ __forceinline__ BStreamT make_stream_t(const GemmArgs& g, int64_t expert_or_slot,
+                                                  int jr, int kcol) {
+  // kcol: first of the 32 columns (a multiple of 32, may lie past K)
+  BStreamT b;
+  const int nkt = g.K / 64;
+  const uint32_t slot = 32u * ((kcol >> 5) & 1) + jr;   // MFMA-tiled slot of row jr
   if constexpr (SRC == kSrcBF16) {
-    // 16 consecutive k = the pieces s0 and s0 + 1 (8 elements each)
-    const int s0 = (c & 31) >> 3;
-    const uint8_t* base = reinterpret_cast<const uint8_t*>(g.wbf16) + tile * 4096;
-    const u32x4_t x0 = *reinterpret_cast<const u32x4_t*>(base + (s0 * 64 + lslot) * 16);
-    const u32x4_t x1 = *reinterpret_cast<const u32x4_t*>(base + ((s0 + 1) * 64 + lslot) * 16);
-    const u32x4_t y0 = *reinterpret_cast<const u32x4_t*>(base + (s0 * 64 + lslot + 1) * 16);
-    const u32x4_t y1 = *reinterpret_cast<const u32x4_t*>(base + ((s0 + 1) * 64 + lslot + 1) * 16);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      b.p[i] = x0[i];
-      b.p[4 + i] = x1[i];
-      b.p[8 + i] = y0[i];
-      b.p[12 + i] = y1[i];
-    }
+    const uint32_t bytes = (uint32_t)g.N * (uint32_t)g.K * 2u;
+    b.w = raw_buffer(reinterpret_cast<const uint8_t*>(g.wbf16) + expert_or_slot * bytes, bytes);
+    b.s = b.w;
+    b.wv = (uint32_t)(kcol >> 6) * 4096u + slot * 16u;
+    b.wstep = nkt * 4096;
+    b.sv = 0;
+    b.sstep = 0;
   } else {
-    const int sbytes = SRC == kSrcMXFP4 ? 1 : 2;
-    const uint8_t* sp = static_cast<const uint8_t*>(g.scales);
-    const uint8_t* w0;
-    int64_t wnext, si, snext;
-    if (g.layout == 1) {
-      w0 = g.packed + (tile * 64 + lslot) * 16 + ((c & 31) >> 1);
-      wnext = 16;
-      si = tile * 64 + lslot;
-      snext = 1;
-    } else {
-      const int64_t rowbytes = g.K / 2;
-      w0 = g.packed + (slot_or_expert * g.N + r) * rowbytes + c / 2;
-      wnext = rowbytes;
-      si = (slot_or_expert * g.N + r) * (int64_t)(g.K / 32) + c / 32;
-      snext = g.K / 32;
+    const int sb = SRC == kSrcMXFP4 ? 1 : 2;
+    const uint32_t wbytes = (uint32_t)g.N * (uint32_t)(g.K / 2);
+    const uint32_t sbytes = (uint32_t)g.N * (uint32_t)(g.K / 32) * sb;
+    b.w = raw_buffer(g.packed + expert_or_slot * wbytes, wbytes);
+    b.s = raw_buffer(static_cast<const uint8_t*>(g.scales) + expert_or_slot * sbytes, sbytes);
+    if (g.layout == 1) {   // MFMA-tiled: tile (row block, 64 columns), slot
+      const uint32_t t = (uint32_t)(kcol >> 6);
+      b.wv = (t * 64u + slot) * 16u;
+      b.wstep = nkt * 1024;
+      b.sv = (t * 64u + slot) * sb;
+      b.sstep = nkt * 64 * sb;
+    } else {               // rows
+      b.wv = (uint32_t)jr * (uint32_t)(g.K / 2) + (uint32_t)(kcol / 2);
+      b.wstep = 32 * (g.K / 2);
+      b.sv = ((uint32_t)jr * (uint32_t)(g.K / 32) + (uint32_t)(kcol / 32)) * sb;
+      b.sstep = 32 * (g.K / 32) * sb;
     }
-    const uint2 x = *reinterpret_cast<const uint2*>(w0);
-    const uint2 y = *reinterpret_cast<const uint2*>(w0 + wnext);
-    b.p[0] = x.x;
-    b.p[1] = x.y;
-    b.p[2] = y.x;
-    b.p[3] = y.y;
-    if constexpr (SRC == kSrcMXFP4) {
-      b.sraw0 = sp[si];
-      b.sraw1 = sp[si + snext];
-    } else {
-      const uint16_t* sp16 = reinterpret_cast<const uint16_t*>(sp);
-      b.sraw0 = sp16[si];
-      b.sraw1 = sp16[si + snext];
-    }
-    (void)sbytes;
+  }
+  return b;
+}
+
+template <int SRC>
+__device__ __forceinline__ void load_bt(const BStreamT& b, int st, BGroup<SRC>& r) {
+  if constexpr (SRC == kSrcBF16) {
+    // tiled BF16: the four 8-element pieces of a slot sit 1 KiB apart
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      r.w[i] = __builtin_amdgcn_raw_buffer_load_b128(b.w, b.wv + i * 1024, st * b.wstep, 0);
+  } else {
+    r.w[0] = __builtin_amdgcn_raw_buffer_load_b128(b.w, b.wv, st * b.wstep, 0);
+    if constexpr (SRC == kSrcMXFP4)
+      r.sraw = __builtin_amdgcn_raw_buffer_load_b8(b.s, b.sv, st * b.sstep, 0);
+    else
+      r.sraw = __builtin_amdgcn_raw_buffer_load_b16(b.s, b.sv, st * b.sstep, 0);
   }
 }
 
-// Decode both rows to BF16 pairs, interleave row-wise per column and store
-// column-major: Bs[col][r..r+1].
+// Decode one group (32 columns of one W row) to BF16 and store its four
+// 16-byte pieces at the given LDS byte offsets.
 template <int SRC>
-__device__ __forceinline__ void store_bt(const BStage<SRC>& b, uint8_t* Bs, int cl, int rp) {
-  uint32_t r0[8], r1[8];
+__device__ __forceinline__ void store_bt(const BGroup<SRC>& b, uint8_t* base, const int (&off)[4]) {
+  u32x4_t v[4];
   if constexpr (SRC == kSrcBF16) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      r0[i] = b.p[i];
-      r1[i] = b.p[8 + i];
-    }
-  } else if constexpr (SRC == kSrcMXFP4) {
-    const float s0 = e8m0_to_f32(b.sraw0), s1 = e8m0_to_f32(b.sraw1);
-    dq8_mxfp4(b.p[0], s0, r0);
-    dq8_mxfp4(b.p[1], s0, r0 + 4);
-    dq8_mxfp4(b.p[2], s1, r1);
-    dq8_mxfp4(b.p[3], s1, r1 + 4);
+    for (int i = 0; i < 4; ++i) v[i] = b.w[i];
   } else {
-    const float s0 = bf16_to_f32(b.sraw0), s1 = bf16_to_f32(b.sraw1);
-    const float n0 = -8.0f * s0, n1 = -8.0f * s1;
-    const float m0 = 512.0f * s0, m1 = 512.0f * s1;
-    dq8_int4(b.p[0], m0, n0, r0);
-    dq8_int4(b.p[1], m0, n0, r0 + 4);
-    dq8_int4(b.p[2], m1, n1, r1);
-    dq8_int4(b.p[3], m1, n1, r1 + 4);
+    uint32_t o[16];
+    if constexpr (SRC == kSrcMXFP4) {
+      const float sc = e8m0_to_f32(b.sraw);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dq8_mxfp4(b.w[0][i], sc, o + 4 * i);
+    } else {
+      const float sc = bf16_to_f32(b.sraw);
+      const float m = 512.0f * sc, n8 = -8.0f * sc;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dq8_int4(b.w[0][i], m, n8, o + 4 * i);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = u32x4_t{o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]};
   }
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    // column 2i: low halves; column 2i+1: high halves
-    const uint32_t lo = __builtin_amdgcn_perm(r1[i], r0[i], 0x05040100u);
-    const uint32_t hi = __builtin_amdgcn_perm(r1[i], r0[i], 0x07060302u);
-    *reinterpret_cast<uint32_t*>(Bs + bcol(cl + 2 * i) + rp * 4) = lo;
-    *reinterpret_cast<uint32_t*>(Bs + bcol(cl + 2 * i + 1) + rp * 4) = hi;
-  }
+  for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4_t*>(base + off[i]) = v[i];
+}
+
+// 4 BF16 of a B column (rows r .. r + 3) by a transposing LDS read: within
+// each 16-lane group, lane i receives element i % 4 of the 8-byte rows that
+// lanes i / 4, i / 4 + 4, i / 4 + 8, i / 4 + 12 point at.
+__device__ __forceinline__ uint2 lds_tr4(const uint8_t* p) {
+  typedef short s16x4_t __attribute__((ext_vector_type(4)));
+  const s16x4_t v =
+      __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)p);
+  return __builtin_bit_cast(uint2, v);
 }
 
 // One work item: tile (rows [row0, row0 + nrows) of one expert) x 256 output
 // columns starting at c0, NMB live 32-row blocks.  Branch-free like the
-// forward kernel: out-of-range loads are clamped, the weight stages come
-// through a two-deep register ring, the LDS buffer parity is static.
+// forward kernel: out-of-range loads are clamped (or read zeros through the
+// buffer bounds) and only the stores are guarded.
 template <int SRC, int MB, int EPI, int AMODE, int NMB>
-__device__ __forceinline__ void gemm_tn_item(const GemmArgs& g, uint8_t (*As)[32 * MB * kRowBT],
-                                             uint8_t (*Bs)[kBsBytes], int4 tile, int c0) {
-  constexpr int MT = 32 * MB;
-  constexpr int ACH = MT * 4;                    // 16-byte A chunks per stage
-  constexpr int NCH = (ACH + 255) / 256;
+__device__ __forceinline__ void gemm_tn_item(const GemmArgs& g, const LdsRing4& As,
+                                             uint8_t (*Bs)[kBStage], int4 tile, int c0) {
+  constexpr int kRing = tn_ring_depth<SRC>();
+  constexpr int kBL = tn_b_loads<SRC>();
+  constexpr int kNCA = (128 * NMB + 255) / 256;   // A copies per thread per stage
+  constexpr int kStageLoads = kNCA + kBL;
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int col = lane & 31;
   const int half = lane >> 5;
   const int nstages = g.N / kKR;
   const int row0 = tile.y, nrows = tile.z;
   const int64_t wsel = SRC == kSrcBF16 ? (int64_t)(tile.w - g.bf16_slot_base) : tile.x;
-  // B loader role: rows 2*rp, 2*rp+1 of the stage, columns 16*bq .. +15
-  // (columns past K are clamped; only idle wavefronts would read them)
-  const int rp = tid & 15;
-  const int bq = tid >> 4;
-  const int bcol0 = min(c0 + 16 * bq, g.K - 16);
 
-  // A chunks: when a stage has fewer chunks than threads (MB == 1), the
-  // spare threads repeat a chunk, writing the same bytes to the same place
-  const uint16_t* asrc[NCH];
-  int adst[NCH];
+  // A copies: chunk slot p = 256 i + tid of a stage holds K chunk
+  // (p & 3) ^ swz_a(r) of tile row r = p >> 2 (slots past the live blocks
+  // copy clamped rows that no operand read touches)
+  const __amdgpu_buffer_rsrc_t arsrc = raw_buffer(g.a, (uint32_t)(g.a_rows * g.lda * 2));
+  uint32_t aoffs[kNCA];
 #pragma unroll
-  for (int i = 0; i < NCH; ++i) {
-    const int c = (tid + 256 * i) % ACH;
-    const int r = c >> 2;
-    const int cc = c & 3;
+  for (int i = 0; i < kNCA; ++i) {
+    const int p = 256 * i + tid;
+    const int r = p >> 2;
+    const int kc = (p & 3) ^ swz_a(r);
     const int rr = r < nrows ? r : 0;
     int64_t srow;
     if constexpr (AMODE == kATokens) srow = g.perm[row0 + rr] / g.topk;
     else srow = row0 + rr;
-    asrc[i] = g.a + srow * g.lda + cc * 8;
-    adst[i] = r * kRowBT + cc * 16;
+    aoffs[i] = (uint32_t)((srow * g.lda + kc * 8) * 2);
   }
+  auto copy_a = [&](int st, auto buf_c) {
+    constexpr int BUF = decltype(buf_c)::value;
+    const uint32_t soff = (uint32_t)((st < nstages ? st : nstages - 1) * kARowB);
+#pragma unroll
+    for (int i = 0; i < kNCA; ++i)
+      copy16_to_lds(arsrc, aoffs[i], soff, As.b[BUF] + (256 * i + 64 * wave) * 16);
+  };
+  // A operand offsets: row col of a block, chunk 2 s + half
+  int aoff[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) aoff[s] = col * kARowB + (((2 * s + half) ^ swz_a(col)) << 4);
+
+  // B loader role: W row jr of the stage, columns c0 + 32 sg .. + 31 (the
+  // row's pieces 4 sg .. 4 sg + 3); lanes 0..31 of a wavefront take 32
+  // consecutive rows of one column group
+  const int jr = tid & 31;
+  const int sg = tid >> 5;
+  const BStreamT bst = make_stream_t<SRC>(g, wsel, jr, c0 + 32 * sg);
+  int bwoff[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) bwoff[k] = jr * kBRowB + (((4 * sg + k) ^ swz_b(jr)) << 4);
+  // B operand reads: lane 16 G + i of the wavefront points at row
+  // 16 s + 8 (G >> 1) + 4 up + i / 4 (up: the upper four of the eight rows),
+  // column 64 wave + 32 nb + 16 (G & 1) + 4 (i & 3); that row's swizzle is
+  // 2 (i / 4) + up
+  const int bg = lane >> 4, bi = lane & 15;
+  int broff[2][2];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+    for (int up = 0; up < 2; ++up) {
+      const int piece = 8 * wave + 4 * nb + 2 * (bg & 1) + ((bi & 3) >> 1);
+      broff[nb][up] = (8 * (bg >> 1) + 4 * up + (bi >> 2)) * kBRowB +
+                      ((piece ^ (2 * (bi >> 2) + up)) << 4) + 8 * (bi & 1);
+    }
+
   const int wbase = c0 + wave * 64;
   const bool active = wbase < g.K;
 
@@ -190,59 +249,77 @@ __device__ __forceinline__ void gemm_tn_item(const GemmArgs& g, uint8_t (*As)[32
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[mb][nb][i] = 0.f;
 
-  BStage<SRC> ring[2];
-  load_bt<SRC>(g, wsel, 2 * rp, bcol0, ring[0]);
-  load_bt<SRC>(g, wsel, (nstages > 1 ? kKR : 0) + 2 * rp, bcol0, ring[1]);
-  u32x4_t areg[NCH];
-#pragma unroll
-  for (int i = 0; i < NCH; ++i) areg[i] = *reinterpret_cast<const u32x4_t*>(asrc[i]);
-  store_bt<SRC>(ring[0], Bs[0], 16 * bq, rp);
-  load_bt<SRC>(g, wsel, (nstages > 2 ? 2 * kKR : 0) + 2 * rp, bcol0, ring[0]);
-#pragma unroll
-  for (int i = 0; i < NCH; ++i) *reinterpret_cast<u32x4_t*>(&As[0][adst[i]]) = areg[i];
-  __syncthreads();
-
-  // stage st computes from buffer BUF while the ring slot holding stage st+1
-  // is decoded into the other buffer and refilled with stage st+3
-  auto kstage = [&](int st, BStage<SRC>& nxt, auto buf_c) {
-    constexpr int BUF = decltype(buf_c)::value;
-    const int s1 = st + 1 < nstages ? st + 1 : st;
-#pragma unroll
-    for (int i = 0; i < NCH; ++i)
-      areg[i] = *reinterpret_cast<const u32x4_t*>(asrc[i] + s1 * kKR);
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const bf16x8_t b0 = *reinterpret_cast<const bf16x8_t*>(
-          &Bs[BUF][bcol(wave * 64 + col) + (16 * s + 8 * half) * 2]);
-      const bf16x8_t b1 = *reinterpret_cast<const bf16x8_t*>(
-          &Bs[BUF][bcol(wave * 64 + 32 + col) + (16 * s + 8 * half) * 2]);
-#pragma unroll
-      for (int mb = 0; mb < NMB; ++mb) {
-        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(
-            &As[BUF][(mb * 32 + col) * kRowBT + (16 * s + 8 * half) * 2]);
-        acc[mb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b0, acc[mb][0], 0, 0, 0);
-        acc[mb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b1, acc[mb][1], 0, 0, 0);
-      }
-    }
-    store_bt<SRC>(nxt, Bs[BUF ^ 1], 16 * bq, rp);
-    {
-      const int s3 = st + 3 < nstages ? st + 3 : nstages - 1;
-      load_bt<SRC>(g, wsel, s3 * kKR + 2 * rp, bcol0, nxt);
-    }
-#pragma unroll
-    for (int i = 0; i < NCH; ++i) *reinterpret_cast<u32x4_t*>(&As[BUF ^ 1][adst[i]]) = areg[i];
-    __syncthreads();
-  };
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
-  // on entry ring[1] holds stage 1 and ring[0] stage 2; stage st + 1 lives
-  // in ring[(st + 1) & 1]
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+
+  // Prologue: A stages 0, 1, 2 (issue order pinned), weight stages
+  // 0 .. kRing - 1; stage 0's weights are decoded into Bs[0] and its ring
+  // slot refilled with stage kRing.
+  BGroup<SRC> ring[kRing];
+  copy_a(0, I0{});
+  compiler_fence();
+  copy_a(1, I1{});
+  compiler_fence();
+  copy_a(2, I2{});
+  compiler_fence();
+#pragma unroll
+  for (int r = 0; r < kRing; ++r) load_bt<SRC>(bst, r < nstages ? r : nstages - 1, ring[r]);
+  store_bt<SRC>(ring[0], Bs[0], bwoff);
+  load_bt<SRC>(bst, kRing < nstages ? kRing : nstages - 1, ring[0]);
+  static_assert(kRing * kBL >= kStageLoads, "prologue leaves too few younger loads");
+  stage_barrier<2 * kNCA + (kRing + 1) * kBL>();
+
+  // stage st: MFMAs from As[st % 4] and Bs[st % 2]; the weights of stage
+  // st + 1 (ring slot (st + 1) % kRing) are decoded into Bs[(st + 1) % 2]
+  // and the slot refilled with stage st + 1 + kRing
+  auto kstage = [&](int st, auto abuf_c) {
+    constexpr int ABUF = decltype(abuf_c)::value;
+    constexpr int BBUF = ABUF & 1;
+    constexpr int SLOT = (ABUF + 1) % kRing;
+    copy_a(st + kNBufA - 1, std::integral_constant<int, (ABUF + kNBufA - 1) % kNBufA>{});
+    const uint8_t* at = As.b[ABUF];
+    const uint8_t* bt = Bs[BBUF];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      bf16x8_t b[2];
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const uint2 lo = lds_tr4(bt + 16 * s * kBRowB + broff[nb][0]);
+        const uint2 hi = lds_tr4(bt + 16 * s * kBRowB + broff[nb][1]);
+        b[nb] = __builtin_bit_cast(bf16x8_t, u32x4_t{lo.x, lo.y, hi.x, hi.y});
+      }
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb) {
+        const bf16x8_t a =
+            *reinterpret_cast<const bf16x8_t*>(at + mb * 32 * kARowB + aoff[s]);
+        acc[mb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b[0], acc[mb][0], 0, 0, 0);
+        acc[mb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b[1], acc[mb][1], 0, 0, 0);
+      }
+    }
+    store_bt<SRC>(ring[SLOT], Bs[BBUF ^ 1], bwoff);
+    {
+      const int nx = st + 1 + kRing;
+      load_bt<SRC>(bst, nx < nstages ? nx : nstages - 1, ring[SLOT]);
+    }
+    // A copies of stage st + 1 were issued two stages ago
+    stage_barrier<2 * kStageLoads>();
+  };
+
   int st = 0;
-  for (; st + 2 <= nstages; st += 2) {
-    kstage(st, ring[1], I0{});
-    kstage(st + 1, ring[0], I1{});
+  for (; st + 4 <= nstages; st += 4) {
+    kstage(st + 0, I0{});
+    kstage(st + 1, I1{});
+    kstage(st + 2, I2{});
+    kstage(st + 3, I3{});
   }
-  if (st < nstages) kstage(st, ring[1], I0{});
+  // tail: nstages is even (N % 64 == 0)
+  if (st < nstages) {
+    kstage(st + 0, I0{});
+    kstage(st + 1, I1{});
+  }
+  __builtin_amdgcn_s_waitcnt(vm_lgkm0_imm(0));
 
   if (!active) return;
 #pragma unroll
@@ -281,9 +358,14 @@ __device__ __forceinline__ void gemm_tn_item(const GemmArgs& g, uint8_t (*As)[32
 }
 
 template <int SRC, int MB, int EPI, int AMODE>
-__global__ __launch_bounds__(256, MB == 4 ? 1 : 2) void k_gemm_tn(GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) uint8_t As[2][32 * MB * kRowBT];
-  __shared__ __attribute__((aligned(16))) uint8_t Bs[2][kBsBytes];
+__global__ __launch_bounds__(256, 2) void k_gemm_tn(GemmArgs g) {
+  __shared__ __attribute__((aligned(16))) uint8_t A0[a_stage_bytes<MB>()];
+  __shared__ __attribute__((aligned(16))) uint8_t A1[a_stage_bytes<MB>()];
+  __shared__ __attribute__((aligned(16))) uint8_t A2[a_stage_bytes<MB>()];
+  __shared__ __attribute__((aligned(16))) uint8_t A3[a_stage_bytes<MB>()];
+  const LdsRing4 As{{A0, A1, A2, A3}};
+  static_assert(kNBufA == 4, "four A stage buffers");
+  __shared__ __attribute__((aligned(16))) uint8_t Bs[2][kBStage];
   const int t_begin = g.range[0];
   const int t_end = g.range[1];
   const int n_tiles_n = (g.K + 255) / 256;      // output columns = W's K index
@@ -313,7 +395,7 @@ hipError_t launch_tn_t(const GemmArgs& g, hipStream_t s) {
   const int n_tiles_n = (g.K + 255) / 256;
   const int64_t bound = (int64_t)g.max_tiles * n_tiles_n;
   if (bound <= 0) return hipSuccess;
-  int64_t grid = std::min<int64_t>(bound, (int64_t)num_cus() * (MB == 4 ? 1 : 2));
+  int64_t grid = std::min<int64_t>(bound, (int64_t)num_cus() * 2);
   grid = (grid + 7) / 8 * 8;
   hipLaunchKernelGGL((k_gemm_tn<SRC, MB, EPI, AMODE>), dim3((unsigned)grid), dim3(256), 0, s, g);
   return hipGetLastError();

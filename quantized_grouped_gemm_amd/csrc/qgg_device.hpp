@@ -105,6 +105,57 @@ __device__ __forceinline__ void dq8_int4(uint32_t w, float s512, float neg8s, ui
   out[3] = pack_bf16x2(__builtin_fmaf(e46[1], s512, neg8s), __builtin_fmaf(e57[1], s512, neg8s));
 }
 
+// ---- memory pipeline helpers shared by the GEMM kernels
+
+// s_waitcnt immediate: wait until at most n vector-memory operations are
+// outstanding and all LDS operations are done (gfx9 encoding: vmcnt in bits
+// [3:0] and [15:14], expcnt [6:4] left at its maximum, lgkmcnt [11:8] = 0).
+constexpr int vm_lgkm0_imm(int n) { return (n & 0xF) | ((n >> 4) << 14) | (0x7 << 4); }
+
+// Compiler-only fence: no memory access moves across it; emits nothing.
+__device__ __forceinline__ void compiler_fence() { asm volatile("" ::: "memory"); }
+
+// 16 bytes from a buffer -> LDS without a register round trip
+// (buffer_load_dwordx4 ... lds): lane i of the wavefront writes lds + 16 i,
+// so the LDS pointer must be the same for the whole wavefront.  Offsets past
+// the buffer's size read zeros.  (The buffer form, unlike the global one, is
+// tracked by the compiler as an ordinary in-order vector-memory load, so its
+// own waits for register loads keep exact counts.)
+__device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t rsrc, uint32_t voff,
+                                              uint32_t soff, void* lds) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)lds, 16,
+                                           voff, soff, 0, 0);
+}
+
+// Raw (untyped, unswizzled) buffer resource over [base, base + bytes).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_buffer(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+// Barrier between two pipeline stages.  A wavefront first waits until at
+// most N of its vector-memory operations are outstanding (the caller picks N
+// as the loads issued after its LDS copies for the next stage, so those have
+// landed while the younger copies and weight loads stay in flight) and its
+// LDS operations are done, then meets the others.  No memory fence: at
+// workgroup scope one would drain every outstanding load, LDS copies
+// included.
+template <int N>
+__device__ __forceinline__ void stage_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  compiler_fence();
+  __builtin_amdgcn_s_waitcnt(vm_lgkm0_imm(N));
+  __builtin_amdgcn_s_barrier();
+  compiler_fence();
+}
+
+// Four LDS stage buffers declared as separate objects (see the kernels):
+// with one array the compiler cannot tell an LDS copy into one buffer from a
+// read of another, and drains every in-flight copy before each LDS read.
+struct LdsRing4 {
+  uint8_t* b[4];
+};
+
 __device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-z)); }
 
 }  // namespace qgg
