@@ -38,12 +38,17 @@ constexpr int kARowB = kKR * 2;           // A bytes per tile row per stage
 template <int MB>
 constexpr int a_stage_bytes() { return 32 * MB * kARowB > 4096 ? 32 * MB * kARowB : 4096; }
 // B tile: 32 rows of 256 BF16 columns; the 16-byte piece P of row r is
-// stored at piece position P ^ swz_b(r), which keeps both the transposing
-// reads (4 rows x 32 bytes per 16 lanes) and the row stores (8 rows x 16
-// bytes per 8 lanes) free of bank conflicts.
+// stored at piece position P ^ swz_b(r).  swz_b takes the 16 values 0..15
+// on any 16 consecutive rows, with rows 4q..4q+3 differing in both bit pairs
+// [2:1] and [3:2]; this keeps the transposing reads (4 rows x 32 bytes per
+// 16 lanes, 4 rows x 64 bytes per 32 lanes) and the row stores (8 or 16 rows
+// x 16 bytes) free of bank conflicts whether a bank cycle serves 128 or 256
+// bytes.
 constexpr int kBRowB = 256 * 2;
 constexpr int kBStage = kKR * kBRowB;
-__device__ __forceinline__ int swz_b(int r) { return 2 * (r & 3) + ((r >> 2) & 1); }
+__device__ __forceinline__ int swz_b(int r) {
+  return ((0xCA60 >> (4 * (r & 3))) & 15) ^ ((r >> 2) & 1) ^ (((r >> 3) & 1) << 1);
+}
 // weight stages in flight per thread (BF16 stages are 4x larger)
 template <int SRC>
 constexpr int tn_ring_depth() { return SRC == kSrcBF16 ? 2 : 4; }
@@ -225,8 +230,8 @@ __device__ __forceinline__ void gemm_tn_item(const GemmArgs& g, const LdsRing4& 
   for (int k = 0; k < 4; ++k) bwoff[k] = jr * kBRowB + (((4 * sg + k) ^ swz_b(jr)) << 4);
   // B operand reads: lane 16 G + i of the wavefront points at row
   // 16 s + 8 (G >> 1) + 4 up + i / 4 (up: the upper four of the eight rows),
-  // column 64 wave + 32 nb + 16 (G & 1) + 4 (i & 3); that row's swizzle is
-  // 2 (i / 4) + up
+  // column 64 wave + 32 nb + 16 (G & 1) + 4 (i & 3) (the row's swizzle does
+  // not depend on s)
   const int bg = lane >> 4, bi = lane & 15;
   int broff[2][2];
 #pragma unroll
@@ -234,8 +239,8 @@ __device__ __forceinline__ void gemm_tn_item(const GemmArgs& g, const LdsRing4& 
 #pragma unroll
     for (int up = 0; up < 2; ++up) {
       const int piece = 8 * wave + 4 * nb + 2 * (bg & 1) + ((bi & 3) >> 1);
-      broff[nb][up] = (8 * (bg >> 1) + 4 * up + (bi >> 2)) * kBRowB +
-                      ((piece ^ (2 * (bi >> 2) + up)) << 4) + 8 * (bi & 1);
+      const int row = 8 * (bg >> 1) + 4 * up + (bi >> 2);
+      broff[nb][up] = row * kBRowB + ((piece ^ swz_b(row)) << 4) + 8 * (bi & 1);
     }
 
   const int wbase = c0 + wave * 64;
@@ -281,21 +286,29 @@ __device__ __forceinline__ void gemm_tn_item(const GemmArgs& g, const LdsRing4& 
     copy_a(st + kNBufA - 1, std::integral_constant<int, (ABUF + kNBufA - 1) % kNBufA>{});
     const uint8_t* at = As.b[ABUF];
     const uint8_t* bt = Bs[BBUF];
+    // all operand reads of the stage first, so their LDS latency overlaps
+    // instead of stalling every MFMA pair
+    bf16x8_t bop[2][2], aop[2][NMB];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      bf16x8_t b[2];
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
         const uint2 lo = lds_tr4(bt + 16 * s * kBRowB + broff[nb][0]);
         const uint2 hi = lds_tr4(bt + 16 * s * kBRowB + broff[nb][1]);
-        b[nb] = __builtin_bit_cast(bf16x8_t, u32x4_t{lo.x, lo.y, hi.x, hi.y});
+        bop[s][nb] = __builtin_bit_cast(bf16x8_t, u32x4_t{lo.x, lo.y, hi.x, hi.y});
       }
 #pragma unroll
+      for (int mb = 0; mb < NMB; ++mb)
+        aop[s][mb] = *reinterpret_cast<const bf16x8_t*>(at + mb * 32 * kARowB + aoff[s]);
+    }
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+#pragma unroll
       for (int mb = 0; mb < NMB; ++mb) {
-        const bf16x8_t a =
-            *reinterpret_cast<const bf16x8_t*>(at + mb * 32 * kARowB + aoff[s]);
-        acc[mb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b[0], acc[mb][0], 0, 0, 0);
-        acc[mb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b[1], acc[mb][1], 0, 0, 0);
+        acc[mb][0] =
+            __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop[s][mb], bop[s][0], acc[mb][0], 0, 0, 0);
+        acc[mb][1] =
+            __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop[s][mb], bop[s][1], acc[mb][1], 0, 0, 0);
       }
     }
     store_bt<SRC>(ring[SLOT], Bs[BBUF ^ 1], bwoff);
