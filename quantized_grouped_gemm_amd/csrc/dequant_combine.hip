@@ -129,35 +129,43 @@ __global__ __launch_bounds__(256) void k_repack(const uint8_t* __restrict__ pack
 }
 
 // out[t][:] = sum over j ascending of w_j * rows[inv_perm[t*k+j]][:], fp32
-// accumulation, BF16 out.  One workgroup per token, 8 columns per thread step.
+// accumulation, BF16 out.  Grid (T, d / 2048): each thread owns 8 columns of
+// one token and issues its k row loads together.
 __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ rows, int d,
                                                  const int32_t* __restrict__ inv_perm,
                                                  const float* __restrict__ gates, int k,
                                                  uint16_t* __restrict__ out) {
   const int64_t t = blockIdx.x;
-  int32_t src[32];
-  float w[32];
-  for (int j = 0; j < k; ++j) {
-    src[j] = inv_perm[t * k + j];
-    w[j] = gates ? gates[t * k + j] : 1.0f;
-  }
-  for (int c = threadIdx.x; c < d / 8; c += blockDim.x) {
-    float acc[8];
+  const int c = blockIdx.y * 256 + threadIdx.x;   // 8-column chunk
+  if (c >= d / 8) return;
+  float acc[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = 0.f;
-    for (int j = 0; j < k; ++j) {
-      if (src[j] < 0) continue;
-      const u32x4_t v = reinterpret_cast<const u32x4_t*>(rows + (int64_t)src[j] * d)[c];
+  for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+  constexpr int kB = 8;   // loads in flight per batch
+  for (int j0 = 0; j0 < k; j0 += kB) {
+    u32x4_t v[kB];
+    float w[kB];
+#pragma unroll
+    for (int b = 0; b < kB; ++b) {
+      const int j = j0 + b;
+      const int src = j < k ? inv_perm[t * k + j] : -1;
+      w[b] = src < 0 ? 0.f : (gates ? gates[t * k + j] : 1.0f);
+      v[b] = src < 0 ? u32x4_t{0u, 0u, 0u, 0u}
+                     : reinterpret_cast<const u32x4_t*>(rows + (int64_t)src * d)[c];
+    }
+#pragma unroll
+    for (int b = 0; b < kB; ++b) {
+      if (j0 + b >= k) break;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        acc[2 * i] = __builtin_fmaf(w[j], bf16_to_f32(v[i] & 0xFFFFu), acc[2 * i]);
-        acc[2 * i + 1] = __builtin_fmaf(w[j], bf16_to_f32(v[i] >> 16), acc[2 * i + 1]);
+        acc[2 * i] = __builtin_fmaf(w[b], bf16_to_f32(v[b][i] & 0xFFFFu), acc[2 * i]);
+        acc[2 * i + 1] = __builtin_fmaf(w[b], bf16_to_f32(v[b][i] >> 16), acc[2 * i + 1]);
       }
     }
-    u32x4_t o = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
-                 pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])};
-    reinterpret_cast<u32x4_t*>(out + t * d)[c] = o;
   }
+  u32x4_t o = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+               pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])};
+  reinterpret_cast<u32x4_t*>(out + t * d)[c] = o;
 }
 
 }  // namespace
@@ -194,7 +202,8 @@ hipError_t launch_repack(int fmt, const uint8_t* packed, const void* scales, int
 hipError_t launch_combine(const uint16_t* rows, int d, const int32_t* inv_perm,
                           const float* gates, int T, int k, uint16_t* out, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_combine, dim3(T), dim3(256), 0, s, rows, d, inv_perm, gates, k, out);
+  hipLaunchKernelGGL(k_combine, dim3(T, (d / 8 + 255) / 256), dim3(256), 0, s, rows, d, inv_perm,
+                     gates, k, out);
   return hipGetLastError();
 }
 

@@ -336,10 +336,12 @@ qgg_status moe_ffn_fwd(const qgg_qweight* w_gate_up, const qgg_qweight* w_down,
   const PermPtrs pp = to_ptrs(p);
 
   QGG_HIP(launch_route(logits, T, E, k, topk_ids, topk_gates, err_flag, stream));
-  QGG_HIP(launch_permute(topk_ids, P, E, pp, err_flag, pws, stream));
-  if (P == 0) return QGG_OK;
-  QGG_HIP(launch_tile_plan(pp, 32 * pl.mb, variant == QGG_CHUNKED ? C : 0, pl.tiles,
-                           pl.chunk_first, stream));
+  if (P == 0) {
+    QGG_HIP(launch_permute(topk_ids, P, E, pp, err_flag, pws, stream));
+    return QGG_OK;
+  }
+  QGG_HIP(launch_permute_plan(topk_ids, P, E, pp, err_flag, pws, 32 * pl.mb,
+                              variant == QGG_CHUNKED ? C : 0, pl.tiles, pl.chunk_first, stream));
 
   GemmArgs gu = base_args(w_gate_up, pl);
   gu.a = x;

@@ -60,6 +60,10 @@ hipError_t launch_gather(const uint16_t* x, int d, const PermPtrs& pp, int E, in
                          uint16_t* out, hipStream_t s);
 hipError_t launch_tile_plan(const PermPtrs& pp, int MT, int C, int4* tiles, int32_t* chunk_first,
                             hipStream_t s);
+// permutation followed by the M-tile plan (MT > 0); one launch when P is small
+hipError_t launch_permute_plan(const int32_t* ids, int64_t P, int E, const PermPtrs& pp,
+                               int32_t* err, void* ws, int MT, int C, int4* tiles,
+                               int32_t* chunk_first, hipStream_t s);
 
 // y = a . W^T per tile (reduce over K); output columns are W rows.
 hipError_t launch_gemm_nt(const GemmArgs& g, int MB, hipStream_t s);

@@ -3,15 +3,48 @@
 // Orbit page, section 时刻细节 ("Active-expert-chunked dequantization"): each
 // token activates only the experts its router selects, and the selected
 // experts are grouped before the grouped GEMM.  The grouping here is a stable
-// counting sort of the (token, expert) pairs by expert id built from
-// wavefront prefix sums; every step is deterministic (no order-dependent
-// atomics: LDS atomics are used only for counts).
+// counting sort of the (token, expert) pairs by expert id: counts, an
+// exclusive scan, then placement by ordered wavefront ballots (a pair's rank
+// inside its expert is a population count); every step is deterministic (no
+// order-dependent atomics: LDS atomics are used only for counts).
 #include "qgg_device.hpp"
 #include "qgg_internal.hpp"
+
+#include <type_traits>
 
 namespace qgg {
 
 // ---------------------------------------------------------------- route
+// Wavefront maximum of a 64-bit key through DPP row/quad moves (no LDS round
+// trips); the result is read from lane 63.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t k) {
+  auto step = [&](auto ctrl_c, auto rmask_c) {
+    constexpr int kCtrl = decltype(ctrl_c)::value;
+    constexpr int kRow = decltype(rmask_c)::value;
+    const uint32_t lo = (uint32_t)k, hi = (uint32_t)(k >> 32);
+    const uint32_t olo = __builtin_amdgcn_update_dpp(lo, lo, kCtrl, kRow, 0xF, false);
+    const uint32_t ohi = __builtin_amdgcn_update_dpp(hi, hi, kCtrl, kRow, 0xF, false);
+    const uint64_t o = ((uint64_t)ohi << 32) | olo;
+    k = o > k ? o : k;
+  };
+  using std::integral_constant;
+  step(integral_constant<int, 0xB1>{}, integral_constant<int, 0xF>{});   // quad_perm 1,0,3,2
+  step(integral_constant<int, 0x4E>{}, integral_constant<int, 0xF>{});   // quad_perm 2,3,0,1
+  step(integral_constant<int, 0x141>{}, integral_constant<int, 0xF>{});  // row_half_mirror
+  step(integral_constant<int, 0x140>{}, integral_constant<int, 0xF>{});  // row_mirror
+  step(integral_constant<int, 0x142>{}, integral_constant<int, 0xA>{});  // row_bcast:15
+  step(integral_constant<int, 0x143>{}, integral_constant<int, 0xC>{});  // row_bcast:31
+  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)k, 63);
+  const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(k >> 32), 63);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// fp32 -> uint32 with the same order (larger float, larger key)
+__device__ __forceinline__ uint32_t order_key(float v) {
+  const uint32_t u = __float_as_uint(v);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
 // One wavefront per token.  Each lane holds up to 16 logits (E <= 1024); k
 // rounds of a wavefront arg-max under the key (logit desc, id asc) pick the
 // experts; gates are the softmax over the kept logits.
@@ -36,50 +69,45 @@ __global__ __launch_bounds__(256) void k_route(const float* __restrict__ logits,
         x = -INFINITY;
       }
     }
-    v[i] = x;
+    v[i] = x + 0.0f;   // -0 -> +0: equal logits tie on the expert id
   }
   if (__any(bad) && lane == 0 && err) atomicOr(err, 1);
   uint32_t taken = 0;  // bit i: v[i] already selected
   float m = 0.f, sum = 0.f;
+  int my_id = 0;       // lane j keeps pick j (k <= 32)
+  float my_w = 0.f;
   for (int j = 0; j < k; ++j) {
-    float bv = -INFINITY;
-    int bi = 0x7FFFFFFF;
+    // this lane's best untaken entry; key 0 = none (a valid entry, even
+    // -inf, has a nonzero key)
+    uint64_t key = 0;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int e = lane + 64 * i;
-      if (e < E && !((taken >> i) & 1u) && (v[i] > bv || bi == 0x7FFFFFFF)) {
-        bv = v[i];
-        bi = e;
-      }
+      const uint64_t ki = ((uint64_t)order_key(v[i]) << 32) | (uint32_t)~e;
+      if (e < E && !((taken >> i) & 1u) && ki > key) key = ki;
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(bv, off, 64);
-      const int oi = __shfl_xor(bi, off, 64);
-      if (ov > bv || (ov == bv && oi < bi)) {
-        bv = ov;
-        bi = oi;
-      }
-    }
+    key = wave_max_u64(key);
+    const int bi = (int)~(uint32_t)key;
+    const uint32_t ok = (uint32_t)(key >> 32);
+    const float best = __uint_as_float((ok & 0x80000000u) ? (ok & 0x7FFFFFFFu) : ~ok);
     if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
-    if (j == 0) m = bv;
-    const float w = expf(bv - m);
+    if (j == 0) m = best;
+    const float w = expf(best - m);
     sum += w;
-    if (lane == 0) {
-      ids[(int64_t)t * k + j] = bi;
-      gates[(int64_t)t * k + j] = w;
+    if (lane == j) {
+      my_id = bi;
+      my_w = w;
     }
   }
-  if (lane == 0) {
-    for (int j = 0; j < k; ++j) gates[(int64_t)t * k + j] = gates[(int64_t)t * k + j] / sum;
+  if (lane < k) {
+    ids[(int64_t)t * k + lane] = my_id;
+    gates[(int64_t)t * k + lane] = my_w / sum;
   }
 }
 
 // -------------------------------------------------------------- permute
-// Pairs are split into segments of kSeg (one workgroup each) and each segment
-// into 16 wave sub-segments of kSeg/16.
+// Pairs are split into segments of kSeg (one counting workgroup each).
 constexpr int kSeg = 4096;
-constexpr int kSub = kSeg / 16;
 
 __device__ __forceinline__ int load_id(const int32_t* ids, int64_t p, int64_t P, int E,
                                        int32_t* err) {
@@ -92,30 +120,83 @@ __device__ __forceinline__ int load_id(const int32_t* ids, int64_t p, int64_t P,
   return e;
 }
 
-// blk[b][e] = number of pairs of segment b routed to expert e.
-__global__ __launch_bounds__(1024) void k_perm_count(const int32_t* __restrict__ ids, int64_t P,
-                                                     int E, int32_t* __restrict__ blk,
-                                                     int32_t* __restrict__ err) {
-  extern __shared__ int lds_cnt[];
+// blk[b][e] = number of pairs of segment b routed to expert e (LDS: E ints).
+__device__ __forceinline__ void perm_count_body(const int32_t* __restrict__ ids, int64_t P, int E,
+                                                int32_t* __restrict__ blk,
+                                                int32_t* __restrict__ err, int* lds_cnt, int b,
+                                                int32_t* __restrict__ inv_perm = nullptr) {
   for (int e = threadIdx.x; e < E; e += blockDim.x) lds_cnt[e] = 0;
   __syncthreads();
-  const int64_t base = (int64_t)blockIdx.x * kSeg;
+  const int64_t base = (int64_t)b * kSeg;
   for (int i = threadIdx.x; i < kSeg; i += blockDim.x) {
     const int e = load_id(ids, base + i, P, E, err);
     if (e >= 0) atomicAdd(&lds_cnt[e], 1);
+    else if (inv_perm && base + i < P) inv_perm[base + i] = -1;
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < E; e += blockDim.x) blk[(int64_t)blockIdx.x * E + e] = lds_cnt[e];
+  for (int e = threadIdx.x; e < E; e += blockDim.x) blk[(int64_t)b * E + e] = lds_cnt[e];
+}
+
+__global__ __launch_bounds__(1024) void k_perm_count(const int32_t* __restrict__ ids, int64_t P,
+                                                     int E, int32_t* __restrict__ blk,
+                                                     int32_t* __restrict__ err,
+                                                     int32_t* __restrict__ inv_perm) {
+  extern __shared__ int lds_cnt[];
+  perm_count_body(ids, P, E, blk, err, lds_cnt, blockIdx.x, inv_perm);
+}
+
+// perm / inv_perm for many pairs: one wavefront per (segment b, expert e)
+// walks the segment's pair ids in order (eight 64-pair ballots in flight) and
+// places its pairs from blk[b][e] (the first sorted row of the segment's
+// pairs of e, after the scan) + the population count of earlier hits; pairs
+// with invalid ids were marked by the count step.
+__global__ __launch_bounds__(256) void k_perm_place(const int32_t* __restrict__ ids, int64_t P,
+                                                    int E, const int32_t* __restrict__ blk,
+                                                    const int32_t* __restrict__ counts,
+                                                    const int32_t* __restrict__ offsets,
+                                                    int32_t* __restrict__ perm,
+                                                    int32_t* __restrict__ inv_perm) {
+  const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int b = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  if (e >= E) return;
+  int run = blk[(int64_t)b * E + e];
+  const int end = (int64_t)(b + 1) * kSeg < P ? blk[(int64_t)(b + 1) * E + e]
+                                              : offsets[e] + counts[e];
+  if (run == end) return;                      // no pair of e in this segment
+  const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
+  const int64_t p0 = (int64_t)b * kSeg;
+  constexpr int kU = 8;
+  for (int c0 = 0; c0 < kSeg; c0 += 64 * kU) {
+    int id[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int64_t p = p0 + c0 + 64 * u + lane;
+      id[u] = p < P ? ids[p] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const bool hit = id[u] == e;
+      const uint64_t mask = __ballot(hit);
+      if (hit) {
+        const int64_t p = p0 + c0 + 64 * u + lane;
+        const int pos = run + __popcll(mask & below);
+        perm[pos] = (int32_t)p;
+        inv_perm[p] = pos;
+      }
+      run += __popcll(mask);
+    }
+    if (run == end) return;
+  }
 }
 
 // counts, offsets (exclusive prefix), active list, n_active; blk[b][e] is
 // replaced by the first sorted row of segment b's pairs of expert e.
-__global__ __launch_bounds__(1024) void k_perm_scan(int nblk, int E, int32_t* __restrict__ blk,
-                                                    int32_t* __restrict__ counts,
-                                                    int32_t* __restrict__ offsets,
-                                                    int32_t* __restrict__ active,
-                                                    int32_t* __restrict__ n_active) {
-  __shared__ int scratch[16];
+__device__ __forceinline__ void perm_scan_body(int nblk, int E, int32_t* __restrict__ blk,
+                                               int32_t* __restrict__ counts,
+                                               int32_t* __restrict__ offsets,
+                                               int32_t* __restrict__ active,
+                                               int32_t* __restrict__ n_active, int* scratch) {
   const int e = threadIdx.x;  // E <= 1024 = blockDim.x
   int run = 0;
   if (e < E) {
@@ -141,63 +222,13 @@ __global__ __launch_bounds__(1024) void k_perm_scan(int nblk, int E, int32_t* __
   if (e == 0) *n_active = nact;
 }
 
-// perm / inv_perm.  Within a wave step of 64 pairs the rank of a pair among
-// equal experts comes from a broadcast scan of the step's ids in LDS; across
-// steps a per-wave, per-expert cursor in LDS carries the running position.
-__global__ __launch_bounds__(1024) void k_perm_scatter(const int32_t* __restrict__ ids, int64_t P,
-                                                       int E, const int32_t* __restrict__ blk,
-                                                       int32_t* __restrict__ perm,
-                                                       int32_t* __restrict__ inv_perm) {
-  extern __shared__ int lds[];
-  int* cur = lds;                 // [16][E] per-wave cursors
-  int* sid = lds + 16 * E;        // [16][64] ids of the current step
-  const int wave = threadIdx.x / 64;
-  const int lane = threadIdx.x & 63;
-  for (int i = threadIdx.x; i < 16 * E; i += blockDim.x) cur[i] = 0;
-  __syncthreads();
-  const int64_t sub0 = (int64_t)blockIdx.x * kSeg + (int64_t)wave * kSub;
-  for (int s = 0; s < kSub; s += 64) {
-    const int e = load_id(ids, sub0 + s + lane, P, E, nullptr);
-    if (e >= 0) atomicAdd(&cur[wave * E + e], 1);
-  }
-  __syncthreads();
-  for (int e = threadIdx.x; e < E; e += blockDim.x) {
-    int run = blk[(int64_t)blockIdx.x * E + e];
-    for (int w = 0; w < 16; ++w) {
-      const int c = cur[w * E + e];
-      cur[w * E + e] = run;
-      run += c;
-    }
-  }
-  __syncthreads();
-  int* mine = sid + wave * 64;
-  for (int s = 0; s < kSub; s += 64) {
-    const int64_t p = sub0 + s + lane;
-    const int e = load_id(ids, p, P, E, nullptr);
-    mine[lane] = e >= 0 ? e : -1 - lane;  // invalid slots never match
-    __syncthreads();
-    int rank = 0;
-    bool last = true;
-    const int me = mine[lane];
-#pragma unroll 8
-    for (int i = 0; i < 64; ++i) {
-      const int o = mine[i];
-      rank += (i < lane && o == me) ? 1 : 0;
-      last = last && !(i > lane && o == me);
-    }
-    int base = 0;
-    if (e >= 0) base = cur[wave * E + e];
-    __syncthreads();
-    if (e >= 0) {
-      const int pos = base + rank;
-      perm[pos] = (int32_t)p;
-      inv_perm[p] = pos;
-      if (last) cur[wave * E + e] = pos + 1;
-    } else if (p < P) {
-      inv_perm[p] = -1;
-    }
-    __syncthreads();
-  }
+__global__ __launch_bounds__(1024) void k_perm_scan(int nblk, int E, int32_t* __restrict__ blk,
+                                                    int32_t* __restrict__ counts,
+                                                    int32_t* __restrict__ offsets,
+                                                    int32_t* __restrict__ active,
+                                                    int32_t* __restrict__ n_active) {
+  __shared__ int scratch[16];
+  perm_scan_body(nblk, E, blk, counts, offsets, active, n_active, scratch);
 }
 
 // x_perm[i][:] = x[perm[i] / k][:], one wavefront per row, 16-byte moves.
@@ -218,13 +249,12 @@ __global__ __launch_bounds__(256) void k_gather_rows(const uint16_t* __restrict_
 // rows.  tiles[j] = {expert, first sorted row, rows, active index};
 // chunk_first[c] = first tile of chunk c (chunks of C active experts), and
 // chunk_first[nchunks] = number of tiles.
-__global__ __launch_bounds__(1024) void k_tile_plan(const int32_t* __restrict__ counts,
-                                                    const int32_t* __restrict__ offsets,
-                                                    const int32_t* __restrict__ active,
-                                                    const int32_t* __restrict__ n_active, int MT,
-                                                    int C, int4* __restrict__ tiles,
-                                                    int32_t* __restrict__ chunk_first) {
-  __shared__ int scratch[16];
+__device__ __forceinline__ void tile_plan_body(const int32_t* __restrict__ counts,
+                                               const int32_t* __restrict__ offsets,
+                                               const int32_t* __restrict__ active,
+                                               const int32_t* __restrict__ n_active, int MT,
+                                               int C, int4* __restrict__ tiles,
+                                               int32_t* __restrict__ chunk_first, int* scratch) {
   const int a = threadIdx.x;
   const int A = *n_active;
   const int e = a < A ? active[a] : -1;
@@ -248,6 +278,74 @@ __global__ __launch_bounds__(1024) void k_tile_plan(const int32_t* __restrict__ 
   }
 }
 
+__global__ __launch_bounds__(1024) void k_tile_plan(const int32_t* __restrict__ counts,
+                                                    const int32_t* __restrict__ offsets,
+                                                    const int32_t* __restrict__ active,
+                                                    const int32_t* __restrict__ n_active, int MT,
+                                                    int C, int4* __restrict__ tiles,
+                                                    int32_t* __restrict__ chunk_first) {
+  __shared__ int scratch[16];
+  tile_plan_body(counts, offsets, active, n_active, MT, C, tiles, chunk_first, scratch);
+}
+
+// Permutation of at most kTiny pairs in one workgroup without rank loops:
+// counts by LDS atomics, then wavefront w places the pairs of active experts
+// w, w + 16, ...: every wavefront holds all ids in registers (64 pairs per
+// register), so one ballot per 64 pairs finds an expert's pairs in order and
+// a pair's rank inside its expert is a population count over the lower lanes
+// plus the running count of earlier ballots.
+constexpr int kTiny = 1024;
+
+__global__ __launch_bounds__(1024) void k_perm_tiny(const int32_t* __restrict__ ids, int64_t P,
+                                                    int E, int32_t* __restrict__ blk,
+                                                    PermPtrs pp, int32_t* __restrict__ err,
+                                                    int MT, int C, int4* __restrict__ tiles,
+                                                    int32_t* __restrict__ chunk_first) {
+  extern __shared__ int cnt[];       // [E]
+  __shared__ int scratch[16];
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int np = (int)P;
+  for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[e] = 0;
+  int r[kTiny / 64];                 // r[c] = id of pair 64 c + lane (-1: none)
+#pragma unroll
+  for (int c = 0; c < kTiny / 64; ++c) r[c] = load_id(ids, 64 * c + lane, P, E, nullptr);
+  __syncthreads();
+  {
+    const int i = threadIdx.x;       // this thread's pair (for counts and errors)
+    const int e = load_id(ids, i, P, E, err);
+    if (e >= 0) atomicAdd(&cnt[e], 1);
+    else if (i < np) pp.inv_perm[i] = -1;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += blockDim.x) blk[e] = cnt[e];
+  __syncthreads();
+  perm_scan_body(1, E, blk, pp.counts, pp.offsets, pp.active, pp.n_active, scratch);
+  __syncthreads();
+  const uint64_t below = lane ? (~0ull >> (64 - lane)) : 0ull;
+  const int nact = *pp.n_active;
+  for (int a = wave; a < nact; a += 16) {
+    const int e = pp.active[a];
+    int run = pp.offsets[e];
+#pragma unroll
+    for (int c = 0; c < kTiny / 64; ++c) {
+      const bool hit = r[c] == e;
+      const uint64_t mask = __ballot(hit);
+      if (hit) {
+        const int pos = run + __popcll(mask & below);
+        pp.perm[pos] = 64 * c + lane;
+        pp.inv_perm[64 * c + lane] = pos;
+      }
+      run += __popcll(mask);
+    }
+  }
+  if (MT > 0) {
+    __syncthreads();
+    tile_plan_body(pp.counts, pp.offsets, pp.active, pp.n_active, MT, C, tiles, chunk_first,
+                   scratch);
+  }
+}
+
 // ------------------------------------------------------------- launchers
 
 hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* gates,
@@ -263,28 +361,30 @@ size_t permute_ws_bytes(int64_t P, int E) {
   return (size_t)std::max<int64_t>(nblk, 1) * E * sizeof(int32_t);
 }
 
-hipError_t launch_permute(const int32_t* ids, int64_t P, int E, const PermPtrs& pp, int32_t* err,
-                          void* ws, hipStream_t s) {
+hipError_t launch_permute_plan(const int32_t* ids, int64_t P, int E, const PermPtrs& pp,
+                               int32_t* err, void* ws, int MT, int C, int4* tiles,
+                               int32_t* chunk_first, hipStream_t s) {
+  if (P <= kTiny) {
+    hipLaunchKernelGGL(k_perm_tiny, dim3(1), dim3(1024), E * sizeof(int), s, ids, P, E,
+                       static_cast<int32_t*>(ws), pp, err, MT, C, tiles, chunk_first);
+    return hipGetLastError();
+  }
   const int nblk = (int)((P + kSeg - 1) / kSeg);
   int32_t* blk = static_cast<int32_t*>(ws);
-  if (nblk > 0) {
-    hipLaunchKernelGGL(k_perm_count, dim3(nblk), dim3(1024), E * sizeof(int), s, ids, P, E, blk,
-                       err);
-  }
+  hipLaunchKernelGGL(k_perm_count, dim3(nblk), dim3(1024), E * sizeof(int), s, ids, P, E, blk,
+                     err, pp.inv_perm);
   hipLaunchKernelGGL(k_perm_scan, dim3(1), dim3(1024), 0, s, nblk, E, blk, pp.counts, pp.offsets,
                      pp.active, pp.n_active);
-  if (nblk > 0) {
-    const size_t lds = (16 * E + 16 * 64) * sizeof(int);
-    if (lds > 65536) {
-      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_perm_scatter),
-                                               hipFuncAttributeMaxDynamicSharedMemorySize,
-                                               (int)lds);
-      if (e != hipSuccess) return e;
-    }
-    hipLaunchKernelGGL(k_perm_scatter, dim3(nblk), dim3(1024), lds, s, ids, P, E, blk, pp.perm,
-                       pp.inv_perm);
-  }
-  return hipGetLastError();
+  hipLaunchKernelGGL(k_perm_place, dim3((E + 3) / 4, nblk), dim3(256), 0, s, ids, P, E, blk,
+                     pp.counts, pp.offsets, pp.perm, pp.inv_perm);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess || MT <= 0) return e;
+  return launch_tile_plan(pp, MT, C, tiles, chunk_first, s);
+}
+
+hipError_t launch_permute(const int32_t* ids, int64_t P, int E, const PermPtrs& pp, int32_t* err,
+                          void* ws, hipStream_t s) {
+  return launch_permute_plan(ids, P, E, pp, err, ws, 0, 0, nullptr, nullptr, s);
 }
 
 hipError_t launch_gather(const uint16_t* x, int d, const PermPtrs& pp, int E, int k, int64_t P,
