@@ -58,8 +58,10 @@ constexpr int tn_b_loads() { return SRC == kSrcBF16 ? 4 : 2; }
 
 // A chunk slot of tile row r: its four 16-byte K chunks are permuted (chunk
 // kc at slot kc ^ swz_a(r)) so that operand reads of 32 consecutive rows hit
-// distinct banks.
-__device__ __forceinline__ int swz_a(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
+// distinct banks (chosen by measuring SQ_LDS_BANK_CONFLICT for candidate
+// permutations of this read pattern on the chip; an unswizzled layout costs
+// 3x the LDS cycles).
+__device__ __forceinline__ int swz_a(int r) { return (r ^ (r >> 2)) & 3; }
 
 __device__ __forceinline__ uint16_t bf16_hw_t(float v) {
   return __builtin_bit_cast(uint16_t, (__bf16)v);
@@ -177,7 +179,8 @@ __device__ __forceinline__ uint2 lds_tr4(const uint8_t* p) {
 // buffer bounds) and only the stores are guarded.
 template <int SRC, int MB, int EPI, int AMODE, int NMB>
 __device__ __forceinline__ void gemm_tn_item(const GemmArgs& g, const LdsRing4& As,
-                                             uint8_t (*Bs)[kBStage], int4 tile, int c0) {
+                                             uint8_t (*Bs)[kBStage], float* Gl, int4 tile,
+                                             int c0) {
   constexpr int kRing = tn_ring_depth<SRC>();
   constexpr int kBL = tn_b_loads<SRC>();
   constexpr int kNCA = (128 * NMB + 255) / 256;   // A copies per thread per stage
@@ -245,6 +248,12 @@ __device__ __forceinline__ void gemm_tn_item(const GemmArgs& g, const LdsRing4& 
 
   const int wbase = c0 + wave * 64;
   const bool active = wbase < g.K;
+  // SwiGLU-backward epilogue: the gate of tile row tid, loaded now and put
+  // in LDS after the K loop, so the epilogue does not wait on perm -> gates
+  float gval = 0.f;
+  if constexpr (EPI == kEpiSwiGLUBwd) {
+    if (tid < 32 * NMB) gval = g.gates[g.perm[row0 + (tid < nrows ? tid : 0)]];
+  }
 
   f32x16_t acc[NMB][2];
 #pragma unroll
@@ -333,39 +342,88 @@ __device__ __forceinline__ void gemm_tn_item(const GemmArgs& g, const LdsRing4& 
     kstage(st + 1, I1{});
   }
   __builtin_amdgcn_s_waitcnt(vm_lgkm0_imm(0));
+  if constexpr (EPI == kEpiSwiGLUBwd) {
+    if (tid < 32 * NMB) Gl[tid] = gval;
+    stage_barrier<0>();
+  }
 
-  if (!active) return;
+  // Epilogue through LDS, 16 tile rows per round: the wavefronts write their
+  // fp32 accumulators (C layout: lane = column, 16 rows per lane) into a
+  // 16 x 256 tile in Bs[0] (16-byte chunks XOR-permuted by row bit 2), then
+  // every thread finishes 16 consecutive columns of one row with 16-byte
+  // loads of the saved activations and 16-byte stores.
+  (void)active;
+  float* tile_f = reinterpret_cast<float*>(Bs[0]);
+  auto tidx = [](int row, int c) { return row * 256 + (((c >> 2) ^ (((row >> 2) & 1) << 3)) << 2) + (c & 3); };
+  const int erow = tid >> 4;            // this thread's row in a round
+  const int eseg = tid & 15;            // its 16 columns: c0 + 16 eseg ..
+  const int ecol = c0 + 16 * eseg;
 #pragma unroll
   for (int mb = 0; mb < NMB; ++mb) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int ih = 0; ih < 2; ++ih) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int r = mb * 32 + 8 * i + 4 * half + j;
-        if (r < nrows) {
-          const int64_t orow = row0 + r;
-          float gate = 1.f;
-          if constexpr (EPI == kEpiSwiGLUBwd) gate = g.gates[g.perm[orow]];
+      for (int ii = 0; ii < 2; ++ii)
 #pragma unroll
-          for (int nb = 0; nb < 2; ++nb) {
-            const int c = wbase + nb * 32 + col;
-            const float v = acc[mb][nb][i * 4 + j];
-            if constexpr (EPI == kEpiSwiGLUBwd) {
-              // v = (dY . W_down)[c]; dA = g * v; h_saved holds [gate | up]
-              const float da = gate * v;
-              const int64_t hb = orow * 2 * (int64_t)g.inter;
-              const float hg = bf16_to_f32(g.h[hb + c]);
-              const float hu = bf16_to_f32(g.h[hb + g.inter + c]);
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb)
+            tile_f[tidx(8 * ii + 4 * half + j, wave * 64 + nb * 32 + col)] =
+                acc[mb][nb][(2 * ih + ii) * 4 + j];
+      stage_barrier<63>();
+      const int r = mb * 32 + 16 * ih + erow;
+      if (r < nrows && ecol < g.K) {
+        const int64_t orow = row0 + r;
+        float v[16];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4_t x = *reinterpret_cast<const f32x4_t*>(&tile_f[tidx(erow, 16 * eseg + 4 * q)]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[4 * q + e] = x[e];
+        }
+        if constexpr (EPI == kEpiSwiGLUBwd) {
+          // v = (dY . W_down)[c]; dA = g * v; h_saved holds [gate | up]
+          const float gate = Gl[r];
+          const int64_t hb = orow * 2 * (int64_t)g.inter + ecol;
+          const u32x4_t* hgp = reinterpret_cast<const u32x4_t*>(g.h + hb);
+          const u32x4_t* hup = reinterpret_cast<const u32x4_t*>(g.h + hb + g.inter);
+          const u32x4_t hg2[2] = {hgp[0], hgp[1]}, hu2[2] = {hup[0], hup[1]};
+          uint32_t og[8], ou[8];
+#pragma unroll
+          for (int e = 0; e < 16; e += 2) {
+            float rg[2], ru[2];
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+              const uint32_t wg = hg2[(e + h2) >> 3][((e + h2) & 7) >> 1];
+              const uint32_t wu = hu2[(e + h2) >> 3][((e + h2) & 7) >> 1];
+              const float hg = bf16_to_f32(((e + h2) & 1) ? (wg >> 16) : (wg & 0xFFFFu));
+              const float hu = bf16_to_f32(((e + h2) & 1) ? (wu >> 16) : (wu & 0xFFFFu));
+              const float da = gate * v[e + h2];
               const float sg = 1.0f / (1.0f + __expf(-hg));
               const float dsilu = sg * (1.0f + hg * (1.0f - sg));
-              g.y[orow * g.ldy + c] = bf16_hw_t(da * hu * dsilu);
-              g.y[orow * g.ldy + g.inter + c] = bf16_hw_t(da * hg * sg);
-            } else {
-              g.y[orow * g.ldy + c] = bf16_hw_t(v);
+              rg[h2] = da * hu * dsilu;
+              ru[h2] = da * hg * sg;
             }
+            og[e >> 1] = (uint32_t)bf16_hw_t(rg[0]) | ((uint32_t)bf16_hw_t(rg[1]) << 16);
+            ou[e >> 1] = (uint32_t)bf16_hw_t(ru[0]) | ((uint32_t)bf16_hw_t(ru[1]) << 16);
           }
+          u32x4_t* yg = reinterpret_cast<u32x4_t*>(g.y + orow * g.ldy + ecol);
+          u32x4_t* yu = reinterpret_cast<u32x4_t*>(g.y + orow * g.ldy + g.inter + ecol);
+          yg[0] = u32x4_t{og[0], og[1], og[2], og[3]};
+          yg[1] = u32x4_t{og[4], og[5], og[6], og[7]};
+          yu[0] = u32x4_t{ou[0], ou[1], ou[2], ou[3]};
+          yu[1] = u32x4_t{ou[4], ou[5], ou[6], ou[7]};
+        } else {
+          uint32_t o[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            o[e] = (uint32_t)bf16_hw_t(v[2 * e]) | ((uint32_t)bf16_hw_t(v[2 * e + 1]) << 16);
+          u32x4_t* yp = reinterpret_cast<u32x4_t*>(g.y + orow * g.ldy + ecol);
+          yp[0] = u32x4_t{o[0], o[1], o[2], o[3]};
+          yp[1] = u32x4_t{o[4], o[5], o[6], o[7]};
         }
       }
+      stage_barrier<63>();
     }
   }
 }
@@ -379,6 +437,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_tn(GemmArgs g) {
   const LdsRing4 As{{A0, A1, A2, A3}};
   static_assert(kNBufA == 4, "four A stage buffers");
   __shared__ __attribute__((aligned(16))) uint8_t Bs[2][kBStage];
+  __shared__ float Gl[32 * MB];   // per-row gates for the SwiGLU-backward epilogue
   const int t_begin = g.range[0];
   const int t_end = g.range[1];
   const int n_tiles_n = (g.K + 255) / 256;      // output columns = W's K index
@@ -392,13 +451,13 @@ __global__ __launch_bounds__(256, 2) void k_gemm_tn(GemmArgs g) {
     const int c0 = (q % n_tiles_n) * 256;
     const int nmb = (tile.z + 31) / 32;
     if (MB == 1 || nmb <= 1) {
-      gemm_tn_item<SRC, MB, EPI, AMODE, 1>(g, As, Bs, tile, c0);
+      gemm_tn_item<SRC, MB, EPI, AMODE, 1>(g, As, Bs, Gl, tile, c0);
     } else if (MB == 2 || nmb == 2) {
-      gemm_tn_item<SRC, MB, EPI, AMODE, (MB >= 2 ? 2 : 1)>(g, As, Bs, tile, c0);
+      gemm_tn_item<SRC, MB, EPI, AMODE, (MB >= 2 ? 2 : 1)>(g, As, Bs, Gl, tile, c0);
     } else if (nmb == 3) {
-      gemm_tn_item<SRC, MB, EPI, AMODE, (MB >= 4 ? 3 : 1)>(g, As, Bs, tile, c0);
+      gemm_tn_item<SRC, MB, EPI, AMODE, (MB >= 4 ? 3 : 1)>(g, As, Bs, Gl, tile, c0);
     } else {
-      gemm_tn_item<SRC, MB, EPI, AMODE, (MB >= 4 ? 4 : 1)>(g, As, Bs, tile, c0);
+      gemm_tn_item<SRC, MB, EPI, AMODE, (MB >= 4 ? 4 : 1)>(g, As, Bs, Gl, tile, c0);
     }
   }
 }
