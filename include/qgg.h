@@ -21,9 +21,12 @@
  *    The library never allocates device memory: scratch and intermediates
  *    come from the caller's `workspace`, sized by qgg_workspace_bytes().
  *  - BF16 tensors are passed as uint16_t bit patterns.  Row-major throughout.
- *  - Calls are asynchronous on `stream` (a hipStream_t; 0 = null stream).
- *    Exception: variant QGG_CHUNKED reads the active-expert count and the
- *    per-chunk tile table back to the host once per call and waits for it.
+ *  - Calls are asynchronous on `stream` (a hipStream_t; 0 = null stream) and
+ *    never synchronize with the host, so a whole call can be captured into a
+ *    HIP graph and replayed.  Variant QGG_CHUNKED launches a fixed number of
+ *    chunk iterations, ceil(min(E, T*k) / C); the active-expert count and the
+ *    per-chunk tile bounds are read on the device, and iterations past the
+ *    last live chunk return at once.  No call issues hipMemset.
  *  - Argument errors are detected on the host before any launch and returned
  *    as a status; nothing aborts.  Data errors found on the device (a
  *    non-finite router logit, an expert id outside [0, E)) set *err_flag to a

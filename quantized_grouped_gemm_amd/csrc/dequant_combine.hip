@@ -40,11 +40,14 @@ __global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ pac
                                                  int count, int tiled_out,
                                                  uint16_t* __restrict__ dst) {
   const int64_t groups_per_expert = (int64_t)N * (K / 32);
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  // the chunk's live experts (the active list is read on the device, so an
+  // empty chunk costs one short launch)
+  const int live = min(count, *n_active - first);
+  const int64_t total = live > 0 ? (int64_t)live * groups_per_expert : 0;
+  for (int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; gid < total;
+       gid += (int64_t)gridDim.x * blockDim.x) {
   const int slot = (int)(gid / groups_per_expert);
-  if (slot >= count) return;
   const int a = first + slot;
-  if (a >= *n_active) return;
   const int64_t e = active[a];
   const int64_t gi = gid % groups_per_expert;
   int64_t n, g;
@@ -100,6 +103,7 @@ __global__ __launch_bounds__(256) void k_dequant(const uint8_t* __restrict__ pac
       u32x4_t v = {out[4 * i], out[4 * i + 1], out[4 * i + 2], out[4 * i + 3]};
       o[i] = v;
     }
+  }
   }
 }
 
@@ -175,7 +179,7 @@ hipError_t launch_dequant(int fmt, const uint8_t* packed, const void* scales, in
                           int count, bool tiled_out, uint16_t* dst, hipStream_t s) {
   const int64_t groups = (int64_t)count * N * (K / 32);
   if (groups <= 0) return hipSuccess;
-  const dim3 grid((unsigned)((groups + 255) / 256));
+  const dim3 grid((unsigned)std::min<int64_t>((groups + 255) / 256, (int64_t)num_cus() * 32));
   if (fmt == 1)
     hipLaunchKernelGGL(k_dequant<1>, grid, dim3(256), 0, s, packed, scales, layout, N, K, active,
                        n_active, first, count, tiled_out ? 1 : 0, dst);

@@ -5,7 +5,6 @@
 
 #include <cstring>
 #include <mutex>
-#include <vector>
 
 #include "qgg.h"
 #include "qgg_internal.hpp"
@@ -119,16 +118,12 @@ GemmArgs base_args(const qgg_qweight* w, const Plan& pl) {
   return g;
 }
 
-// Host copy of n_active and the chunk table, read once per chunked call.
-qgg_status read_chunks(const Plan& pl, const int32_t* n_active_dev, int E, int C,
-                       hipStream_t s, int* n_active, std::vector<int32_t>& first) {
-  QGG_HIP(hipMemcpyAsync(n_active, n_active_dev, sizeof(int32_t), hipMemcpyDeviceToHost, s));
-  first.assign(E + 2, 0);
-  QGG_HIP(hipMemcpyAsync(first.data(), pl.chunk_first, sizeof(int32_t) * (E + 2),
-                         hipMemcpyDeviceToHost, s));
-  QGG_HIP(hipStreamSynchronize(s));
-  (void)C;
-  return QGG_OK;
+// Chunk iterations of a CHUNKED call: enough for every expert that can be
+// active (at most min(E, P)); chunks past the live ones are empty on the
+// device and their launches return at once, so no count is read back.
+int chunk_iterations(int E, int64_t P, int C) {
+  const int64_t most = std::min<int64_t>(E, P);
+  return (int)((most + C - 1) / C);
 }
 
 }  // namespace
@@ -272,7 +267,7 @@ qgg_status dequant_grouped_gemm(const qgg_qweight* w, const uint16_t* a, int fla
   }
   if (P == 0) return QGG_OK;
   const PermPtrs pp = to_ptrs(p);
-  QGG_HIP(launch_tile_plan(pp, 32 * pl.mb, variant == QGG_CHUNKED ? C : 0, pl.tiles,
+  QGG_HIP(launch_tile_plan(pp, E, 32 * pl.mb, variant == QGG_CHUNKED ? C : 0, pl.tiles,
                            pl.chunk_first, stream));
   GemmArgs g = base_args(w, pl);
   g.a = a;
@@ -288,18 +283,14 @@ qgg_status dequant_grouped_gemm(const qgg_qweight* w, const uint16_t* a, int fla
     QGG_HIP(trans ? launch_gemm_tn(g, pl.mb, stream) : launch_gemm_nt(g, pl.mb, stream));
     return QGG_OK;
   }
-  int n_act = 0;
-  std::vector<int32_t> first;
-  qgg_status st = read_chunks(pl, p->n_active, E, C, stream, &n_act, first);
-  if (st != QGG_OK) return st;
-  const int nch = (n_act + C - 1) / C;
+  const int nch = chunk_iterations(E, P, C);
   g.src = kSrcBF16;
   g.wbf16 = sbuf;
   for (int c = 0; c < nch; ++c) {
     QGG_HIP(launch_dequant(w->fmt, w->packed, w->scales, w->layout, N, K, p->active,
                            p->n_active, c * C, C, true, sbuf, stream));
     g.range = pl.chunk_first + c;
-    g.max_tiles = first[c + 1] - first[c];
+    g.max_tiles = (int)pl.cap;
     g.bf16_slot_base = c * C;
     QGG_HIP(trans ? launch_gemm_tn(g, pl.mb, stream) : launch_gemm_nt(g, pl.mb, stream));
   }
@@ -370,16 +361,12 @@ qgg_status moe_ffn_fwd(const qgg_qweight* w_gate_up, const qgg_qweight* w_down,
     QGG_HIP(launch_gemm_nt(gu, pl.mb, stream));
     QGG_HIP(launch_gemm_nt(dn, pl.mb, stream));
   } else {
-    int n_act = 0;
-    std::vector<int32_t> first;
-    qgg_status st = read_chunks(pl, p->n_active, E, C, stream, &n_act, first);
-    if (st != QGG_OK) return st;
-    const int nch = (n_act + C - 1) / C;
+    const int nch = chunk_iterations(E, P, C);
     gu.src = dn.src = kSrcBF16;
     gu.wbf16 = dn.wbf16 = sbuf;
     for (int c = 0; c < nch; ++c) {
       gu.range = dn.range = pl.chunk_first + c;
-      gu.max_tiles = dn.max_tiles = first[c + 1] - first[c];
+      gu.max_tiles = dn.max_tiles = (int)pl.cap;
       gu.bf16_slot_base = dn.bf16_slot_base = c * C;
       QGG_HIP(launch_dequant(w_gate_up->fmt, w_gate_up->packed, w_gate_up->scales,
                              w_gate_up->layout, 2 * inter, d, p->active, p->n_active, c * C, C,
@@ -422,7 +409,7 @@ qgg_status moe_dx_bwd(const qgg_qweight* w_gate_up, const qgg_qweight* w_down,
   uint16_t* dxp = cv.take<uint16_t>((size_t)P * d * 2);
   uint16_t* sbuf = cv.take<uint16_t>(scratch);
   const PermPtrs pp = to_ptrs(p);
-  QGG_HIP(launch_tile_plan(pp, 32 * pl.mb, variant == QGG_CHUNKED ? C : 0, pl.tiles,
+  QGG_HIP(launch_tile_plan(pp, E, 32 * pl.mb, variant == QGG_CHUNKED ? C : 0, pl.tiles,
                            pl.chunk_first, stream));
 
   // dA = (g dY) . W_down, then dH from the SwiGLU derivative (fused epilogue)
@@ -455,16 +442,12 @@ qgg_status moe_dx_bwd(const qgg_qweight* w_gate_up, const qgg_qweight* w_down,
     QGG_HIP(launch_gemm_tn(dn, pl.mb, stream));
     QGG_HIP(launch_gemm_tn(gu, pl.mb, stream));
   } else {
-    int n_act = 0;
-    std::vector<int32_t> first;
-    qgg_status st = read_chunks(pl, p->n_active, E, C, stream, &n_act, first);
-    if (st != QGG_OK) return st;
-    const int nch = (n_act + C - 1) / C;
+    const int nch = chunk_iterations(E, P, C);
     dn.src = gu.src = kSrcBF16;
     dn.wbf16 = gu.wbf16 = sbuf;
     for (int c = 0; c < nch; ++c) {
       dn.range = gu.range = pl.chunk_first + c;
-      dn.max_tiles = gu.max_tiles = first[c + 1] - first[c];
+      dn.max_tiles = gu.max_tiles = (int)pl.cap;
       dn.bf16_slot_base = gu.bf16_slot_base = c * C;
       QGG_HIP(launch_dequant(w_down->fmt, w_down->packed, w_down->scales, w_down->layout, d,
                              inter, p->active, p->n_active, c * C, C, true, sbuf, stream));

@@ -58,8 +58,10 @@ hipError_t launch_permute(const int32_t* ids, int64_t P, int E, const PermPtrs& 
                           void* ws, hipStream_t s);
 hipError_t launch_gather(const uint16_t* x, int d, const PermPtrs& pp, int E, int k, int64_t P,
                          uint16_t* out, hipStream_t s);
-hipError_t launch_tile_plan(const PermPtrs& pp, int MT, int C, int4* tiles, int32_t* chunk_first,
-                            hipStream_t s);
+// M-tile plan; chunk_first gets E + 2 entries (chunks past the last live one
+// are empty)
+hipError_t launch_tile_plan(const PermPtrs& pp, int E, int MT, int C, int4* tiles,
+                            int32_t* chunk_first, hipStream_t s);
 // permutation followed by the M-tile plan (MT > 0); one launch when P is small
 hipError_t launch_permute_plan(const int32_t* ids, int64_t P, int E, const PermPtrs& pp,
                                int32_t* err, void* ws, int MT, int C, int4* tiles,

@@ -254,7 +254,8 @@ __device__ __forceinline__ void tile_plan_body(const int32_t* __restrict__ count
                                                const int32_t* __restrict__ active,
                                                const int32_t* __restrict__ n_active, int MT,
                                                int C, int4* __restrict__ tiles,
-                                               int32_t* __restrict__ chunk_first, int* scratch) {
+                                               int32_t* __restrict__ chunk_first, int* scratch,
+                                               int E) {
   const int a = threadIdx.x;
   const int A = *n_active;
   const int e = a < A ? active[a] : -1;
@@ -271,11 +272,11 @@ __device__ __forceinline__ void tile_plan_body(const int32_t* __restrict__ count
   }
   const int CC = C > 0 ? C : (A > 0 ? A : 1);
   if (a < A && a % CC == 0) chunk_first[a / CC] = first;
-  if (a == 0) {
-    const int nch = (A + CC - 1) / CC;
-    chunk_first[nch] = total;
-    if (nch == 0) chunk_first[0] = 0;
-  }
+  // chunks past the last live one (up to entry E + 1) are empty: their
+  // bounds both read `total`, so a chunk loop of fixed length needs no host
+  // read-back of the active count
+  const int nch = (A + CC - 1) / CC;
+  for (int c = nch + a; c <= E + 1; c += blockDim.x) chunk_first[c] = total;
 }
 
 __global__ __launch_bounds__(1024) void k_tile_plan(const int32_t* __restrict__ counts,
@@ -283,9 +284,9 @@ __global__ __launch_bounds__(1024) void k_tile_plan(const int32_t* __restrict__ 
                                                     const int32_t* __restrict__ active,
                                                     const int32_t* __restrict__ n_active, int MT,
                                                     int C, int4* __restrict__ tiles,
-                                                    int32_t* __restrict__ chunk_first) {
+                                                    int32_t* __restrict__ chunk_first, int E) {
   __shared__ int scratch[16];
-  tile_plan_body(counts, offsets, active, n_active, MT, C, tiles, chunk_first, scratch);
+  tile_plan_body(counts, offsets, active, n_active, MT, C, tiles, chunk_first, scratch, E);
 }
 
 // Permutation of at most kTiny pairs in one workgroup without rank loops:
@@ -342,7 +343,7 @@ __global__ __launch_bounds__(1024) void k_perm_tiny(const int32_t* __restrict__ 
   if (MT > 0) {
     __syncthreads();
     tile_plan_body(pp.counts, pp.offsets, pp.active, pp.n_active, MT, C, tiles, chunk_first,
-                   scratch);
+                   scratch, E);
   }
 }
 
@@ -379,7 +380,7 @@ hipError_t launch_permute_plan(const int32_t* ids, int64_t P, int E, const PermP
                      pp.counts, pp.offsets, pp.perm, pp.inv_perm);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess || MT <= 0) return e;
-  return launch_tile_plan(pp, MT, C, tiles, chunk_first, s);
+  return launch_tile_plan(pp, E, MT, C, tiles, chunk_first, s);
 }
 
 hipError_t launch_permute(const int32_t* ids, int64_t P, int E, const PermPtrs& pp, int32_t* err,
@@ -395,10 +396,10 @@ hipError_t launch_gather(const uint16_t* x, int d, const PermPtrs& pp, int E, in
   return hipGetLastError();
 }
 
-hipError_t launch_tile_plan(const PermPtrs& pp, int MT, int C, int4* tiles, int32_t* chunk_first,
-                            hipStream_t s) {
+hipError_t launch_tile_plan(const PermPtrs& pp, int E, int MT, int C, int4* tiles,
+                            int32_t* chunk_first, hipStream_t s) {
   hipLaunchKernelGGL(k_tile_plan, dim3(1), dim3(1024), 0, s, pp.counts, pp.offsets, pp.active,
-                     pp.n_active, MT, C, tiles, chunk_first);
+                     pp.n_active, MT, C, tiles, chunk_first, E);
   return hipGetLastError();
 }
 

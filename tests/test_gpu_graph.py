@@ -1,0 +1,67 @@
+"""HIP-graph capture of whole calls.  The entry points never synchronize with
+the host (the chunked variant runs a fixed-length chunk loop whose bounds are
+read on the device), so moe_ffn_fwd and moe_dx_bwd can be captured once and
+replayed.  Each replay, with unrelated eager work and host synchronizations
+between replays, must reproduce the eager result bit for bit."""
+import numpy as np
+import pytest
+import torch
+
+import quantized_grouped_gemm_amd as qgg
+import synth
+from synth.configs import CONFIGS, scaled
+
+from .gpu_util import DEV, dev_bf16, dev_weights, host_u16, sync
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # Zipf routing: most chunks of 4 experts are empty, the loop still runs
+    # ceil(min(E, T*k) / 4) iterations
+    (scaled(CONFIGS["int4_ffn_decode_zipf"], T=48, d=256, E=40, k=4, N=512, inter=256,
+            chunks=(4,), name="int4_zipf_graph"), qgg.CHUNKED, 4),
+    (scaled(CONFIGS["int4_ffn_decode_zipf"], T=48, d=256, E=40, k=4, N=512, inter=256,
+            chunks=(4,), name="int4_zipf_graph"), qgg.FUSED, 0),
+    (scaled(CONFIGS["mxfp4_ffn_prefill"], T=96, d=256, E=16, k=4, N=512, inter=256, chunks=(3,),
+            name="mxfp4_ffn_graph"), qgg.CHUNKED, 3),
+]
+
+
+@pytest.mark.parametrize("cfg,variant,chunk", CASES,
+                         ids=lambda v: v.name if hasattr(v, "name") else str(v))
+def test_ffn_and_dx_graph_replays_match_eager(cfg, variant, chunk):
+    print(f"case {cfg.name} variant {variant} chunk {chunk}", flush=True)
+    logits = torch.from_numpy(synth.configs.router_logits(cfg)).to(DEV)
+    x = dev_bf16(synth.configs.activations(cfg))
+    dy = dev_bf16(synth.configs.grad_output(cfg))
+    wg = dev_weights(cfg.fmt, *synth.configs.first_weights(cfg), layout=qgg.LAYOUT_MFMA)
+    wd = dev_weights(cfg.fmt, *synth.configs.down_weights(cfg), layout=qgg.LAYOUT_MFMA)
+
+    def step():
+        r = qgg.moe_ffn_fwd(wg, wd, x, logits, cfg.k, variant, chunk, save_h=True)
+        dx = qgg.moe_dx_bwd(wg, wd, dy, r["topk_gates"], r["perm"], r["h"], cfg.k, variant,
+                            chunk)
+        return r["y"], r["h"], dx
+
+    y0, h0, dx0 = (host_u16(t) for t in step())          # eager reference
+    sync()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):                          # warm up on the side stream
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    sync()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        outs = step()
+    for rep in range(3):
+        graph.replay()
+        sync()
+        got = [host_u16(t) for t in outs]
+        np.testing.assert_array_equal(got[0], y0, err_msg=f"y replay {rep}")
+        np.testing.assert_array_equal(got[1], h0, err_msg=f"h replay {rep}")
+        np.testing.assert_array_equal(got[2], dx0, err_msg=f"dx replay {rep}")
+        for t in outs:                                     # eager work between replays
+            t.zero_()
+        step()
+        sync()

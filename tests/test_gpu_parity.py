@@ -28,15 +28,19 @@ def _inputs(cfg: Config):
 
 ROUTE_CASES = [CONFIGS["tiny_mxfp4_proj"], CONFIGS["kimi_int4_gate_up"],
                CONFIGS["mxfp4_ffn_prefill"], CONFIGS["int4_ffn_decode_zipf"],
-               scaled(CONFIGS["tiny_mxfp4_proj"], T=37, E=1000, k=32, name="wide")]
+               scaled(CONFIGS["tiny_mxfp4_proj"], T=37, E=1000, k=32, name="wide"),
+               # <= 1024 pairs: the one-workgroup ballot permutation, wide E
+               scaled(CONFIGS["tiny_mxfp4_proj"], T=31, E=1000, k=32, name="wide_small")]
 
 
 @pytest.mark.parametrize("cfg", ROUTE_CASES, ids=lambda c: c.name)
 def test_route_and_permute_bit_exact(cfg):
     print(f"case {cfg.name} T={cfg.T} E={cfg.E} k={cfg.k}", flush=True)
     logits = synth.configs.router_logits(cfg)
-    if cfg.name == "wide":
+    if cfg.name.startswith("wide"):
         logits[:, 3] = logits[:, 5]          # exact ties
+        logits[::2, 7] = -0.0                # signed zeros tie with +0
+        logits[::2, 9] = 0.0
     ids_ref, gates_ref = oracle.route(logits, cfg.k)
     lt = torch.from_numpy(logits).to(DEV)
     err = torch.zeros(1, dtype=torch.int32, device=DEV)
