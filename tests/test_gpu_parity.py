@@ -173,6 +173,9 @@ PROJ_CASES = [
     scaled(CONFIGS["tiny_mxfp4_proj"], T=200, d=256, E=8, k=2, N=256, name="mxfp4_mb2"),
     scaled(CONFIGS["kimi_int4_gate_up"], T=512, d=256, E=8, k=2, N=256, chunks=(3,),
            name="int4_mb4"),
+    # >200 rows per expert: several 128-row tiles per expert, ragged
+    scaled(CONFIGS["kimi_int4_gate_up"], T=700, d=256, E=6, k=2, N=320, chunks=(4,),
+           name="int4_tall"),
 ]
 
 
@@ -294,6 +297,8 @@ FFN_CASES = [
            name="mxfp4_ffn_small"),
     scaled(CONFIGS["int4_ffn_decode_zipf"], T=64, d=512, E=48, k=8, N=512, inter=256,
            chunks=(8,), name="int4_zipf_decode_small"),
+    scaled(CONFIGS["mxfp4_ffn_prefill"], T=320, d=256, E=4, k=3, N=512, inter=256, chunks=(3,),
+           name="mxfp4_ffn_tall"),
     scaled(CONFIGS["mxfp4_ffn_prefill"], T=300, d=256, E=8, k=2, N=256, inter=128, chunks=(4,),
            name="mxfp4_ffn_mb4"),
 ]
