@@ -54,6 +54,8 @@ def _L():
         lib.oracle_project_t.argtypes = [i32, P, P, i32, i64, i64, P, i64, P, P]
         lib.oracle_ffn.argtypes = [i32, P, P, P, P, i32, i64, i64, P, i32, P, P, i64, P, P, P]
         lib.oracle_dx.argtypes = [i32, P, P, P, P, i32, i64, i64, P, P, i32, P, P, i64, P, P, P]
+        lib.oracle_router_bwd.argtypes = [i32, P, P, P, P, i32, i64, i64, P, P, P, i32, P, i64,
+                                          P, P, P]
         lib.oracle_silu.argtypes = [ctypes.c_double]
         lib.oracle_silu.restype = ctypes.c_double
         lib.oracle_silu_grad.argtypes = [ctypes.c_double]
@@ -181,6 +183,25 @@ def dx(fmt, gu, dn, x, dy, ids, gates, toks, want_da=False):
                           k, _p(np.ascontiguousarray(ids, np.int32)), _p(gates), toks.size,
                           _p(toks), _p(out), _p(da)), "dx")
     return out, da
+
+
+def router_bwd(fmt, gu, dn, x, dy, logits, ids, toks):
+    """(dgates [ntok][k], dlogits [ntok][E]) of L = <dY, y> for the selected
+    tokens, routing choice held fixed; gates re-derived from the logits."""
+    gu_p, gu_s = gu
+    dn_p, dn_s = dn
+    E, N2, d2 = gu_p.shape
+    d, I = 2 * d2, N2 // 2
+    k = ids.shape[1]
+    toks = np.ascontiguousarray(toks, np.int32)
+    logits = np.ascontiguousarray(logits, np.float32)
+    assert logits.shape[1] == E
+    dg = np.zeros((toks.size, k), np.float64)
+    dl = np.zeros((toks.size, E), np.float64)
+    _check(_L().oracle_router_bwd(fmt, _p(gu_p), _p(gu_s), _p(dn_p), _p(dn_s), E, d, I, _p(x),
+                                  _p(dy), _p(logits), k, _p(np.ascontiguousarray(ids, np.int32)),
+                                  toks.size, _p(toks), _p(dg), _p(dl)), "router_bwd")
+    return dg, dl
 
 
 def silu(z: float) -> float:

@@ -28,6 +28,11 @@
  *           gradient.  dO = g * dY[t]; dA = W_down^T dO; dH = [dA * up *
  *           silu'(gate) | dA * silu(gate)]; dXp = W_gu^T dH; dX[t] = sum over
  *           j ascending of dXp[t,j].  Gates are constants.
+ *  router_bwd  The gradient the base hands back to a trainable router (the
+ *           pages freeze the base, not the router): dg[t,j] = <dY[t], o[t,j]>,
+ *           then reverse mode through the gate definition of route.  The
+ *           pages give no formula for this step; it is the chain rule
+ *           applied to the forward above.
  *
  * Weight layout: packed [E][N][K/2] (element k in byte k>>1, low nibble for
  * even k), scales [E][N][K/32] (u8 E8M0 for MXFP4, u16 BF16 bits for INT4).
@@ -415,5 +420,68 @@ int oracle_dx(int fmt, const uint8_t* gu_p, const void* gu_s, const uint8_t* dn_
     }
   }
   free(dxp);
+  return rc;
+}
+
+/* ------------------------------------------------------ router backward */
+
+/* Gradient of L = <dY, y> with respect to the gates and the router logits,
+ * the base and the routing choice held fixed (the top-k selection is
+ * piecewise constant in the logits, so it passes no gradient).
+ *
+ * dg[s][j] = sum over n ascending of dY[t][n] * o[t,j][n], o from the forward
+ * definition above.  The logit gradient runs reverse mode through the gate
+ * definition of oracle_route, step by step: p = softmax over all E logits,
+ * S = sum of the kept p, g_j = p[id_j] / S; so
+ *   dS = -sum_j dg_j p[id_j] / S^2,
+ *   dp_e = (e kept as slot j ? dg_j / S : 0) + (e kept ? dS : 0),
+ *   dl_e = p_e (dp_e - sum_e' p_e' dp_e').
+ * Outputs for the selected tokens: dgates [ntok][k], dlogits [ntok][E]
+ * (either may be NULL). */
+int oracle_router_bwd(int fmt, const uint8_t* gu_p, const void* gu_s, const uint8_t* dn_p,
+                      const void* dn_s, int E, int64_t d, int64_t I, const uint16_t* x,
+                      const uint16_t* dy, const float* logits, int k, const int32_t* ids,
+                      int64_t ntok, const int32_t* toks, double* dgates, double* dlogits) {
+  double* o = (double*)malloc(sizeof(double) * (size_t)(ntok * k * d));
+  double* dg = (double*)malloc(sizeof(double) * (size_t)(ntok * k));
+  double* p = (double*)malloc(sizeof(double) * (size_t)E);
+  double* dp = (double*)malloc(sizeof(double) * (size_t)E);
+  int rc = (!o || !dg || !p || !dp) ? 3 : 0;
+  if (!rc)
+    rc = ffn_pairs(0, fmt, gu_p, gu_s, dn_p, dn_s, E, d, I, x, NULL, k, ids, NULL, ntok, toks, o,
+                   NULL, NULL);
+  for (int64_t s = 0; s < ntok && !rc; ++s) {
+    const int64_t t = toks[s];
+    for (int j = 0; j < k; ++j) {
+      double acc = 0.0;
+      for (int64_t n = 0; n < d; ++n)
+        acc += (double)bf16_to_float(dy[t * d + n]) * o[(s * k + j) * d + n];
+      dg[s * k + j] = acc;
+      if (dgates) dgates[s * k + j] = acc;
+    }
+    if (!dlogits) continue;
+    const float* l = logits + t * E;
+    double m = -INFINITY;
+    for (int e = 0; e < E; ++e) m = fmax(m, (double)l[e]);
+    double z = 0.0;
+    for (int e = 0; e < E; ++e) {
+      p[e] = exp((double)l[e] - m);
+      z += p[e];
+    }
+    for (int e = 0; e < E; ++e) p[e] /= z;
+    double S = 0.0;
+    for (int j = 0; j < k; ++j) S += p[ids[t * k + j]];
+    double dS = 0.0;
+    for (int j = 0; j < k; ++j) dS -= dg[s * k + j] * p[ids[t * k + j]] / (S * S);
+    for (int e = 0; e < E; ++e) dp[e] = 0.0;
+    for (int j = 0; j < k; ++j) dp[ids[t * k + j]] += dg[s * k + j] / S + dS;
+    double pdp = 0.0;
+    for (int e = 0; e < E; ++e) pdp += p[e] * dp[e];
+    for (int e = 0; e < E; ++e) dlogits[s * E + e] = p[e] * (dp[e] - pdp);
+  }
+  free(o);
+  free(dg);
+  free(p);
+  free(dp);
   return rc;
 }

@@ -431,6 +431,76 @@ def test_dx_adjoint_of_down_projection():
         assert abs(np.dot(gates[t, j] * dyf[t], Wd @ a) - np.dot(da[s], a)) < 1e-10
 
 
+# ------------------------------------------------------------ router backward
+
+def _twin_pair_outputs(fmt, gu, dn, xf, ids, t):
+    """o[t, j] for each slot j of token t, by the numpy twin of the forward."""
+    I = gu[0].shape[1] // 2
+    outs = []
+    for e in ids[t]:
+        Wg = _decode_bits(fmt, gu[0][e], gu[1][e]).astype(np.float64)
+        Wd = _decode_bits(fmt, dn[0][e], dn[1][e]).astype(np.float64)
+        h = Wg @ xf[t]
+        outs.append(Wd @ (h[:I] / (1.0 + np.exp(-h[:I])) * h[I:]))
+    return np.array(outs)
+
+
+def _kept_gates(l64, ids_t):
+    p = special.softmax(l64)
+    g = p[ids_t]
+    return g / g.sum()
+
+
+@pytest.mark.parametrize("fmt", [1, 2])
+def test_router_bwd_matches_twin_and_finite_differences(fmt):
+    T, d, I, E, k = 4, 64, 32, 6, 3
+    gu, dn, x, ids, _ = _tiny_ffn_inputs(fmt, T=T, d=d, I=I, E=E, k=k, seed=5)
+    logits = synth.normal_f32(5, 1, (T, E))
+    ids, _ = oracle.route(logits, k)
+    dy = synth.normal_bf16(5, 5, (T, d))
+    toks = np.arange(T, dtype=np.int32)
+    dg, dl = oracle.router_bwd(fmt, gu, dn, x, dy, logits, ids, toks)
+    xf, dyf = oracle.bf16_to_f64(x), oracle.bf16_to_f64(dy)
+    eps = 1e-6
+    for t in range(T):
+        o = _twin_pair_outputs(fmt, gu, dn, xf, ids, t)
+        dg_twin = o @ dyf[t]
+        np.testing.assert_allclose(dg[t], dg_twin, rtol=1e-12, atol=1e-12)
+        l64 = logits[t].astype(np.float64)
+        for e in range(E):
+            lp, lm = l64.copy(), l64.copy()
+            lp[e] += eps
+            lm[e] -= eps
+            # the perturbation is far smaller than any gap at the top-k boundary
+            fd = (_kept_gates(lp, ids[t]) @ dg_twin - _kept_gates(lm, ids[t]) @ dg_twin) / (2 * eps)
+            assert abs(fd - dl[t, e]) <= 1e-7 * max(1.0, abs(fd)), (t, e, fd, dl[t, e])
+        kept = np.zeros(E, bool)
+        kept[ids[t]] = True
+        assert np.all(np.abs(dl[t, ~kept]) <= 1e-14 * np.abs(dl[t]).max())
+        assert abs(dl[t].sum()) <= 1e-13 * np.abs(dl[t]).max()   # shift invariance
+
+
+def test_router_bwd_special_cases():
+    T, d, I, E = 3, 64, 32, 5
+    gu, dn, x, _, _ = _tiny_ffn_inputs(1, T=T, d=d, I=I, E=E, k=1, seed=6)
+    logits = synth.normal_f32(6, 1, (T, E))
+    dy = synth.normal_bf16(6, 5, (T, d))
+    toks = np.arange(T, dtype=np.int32)
+    # k = 1: the gate is identically 1, so no gradient reaches the logits
+    ids, _ = oracle.route(logits, 1)
+    dg, dl = oracle.router_bwd(1, gu, dn, x, dy, logits, ids, toks)
+    assert np.all(np.abs(dl) <= 1e-15 * np.abs(dg).max())
+    # k = E: the gates are the plain softmax; torch's autograd of softmax
+    ids, _ = oracle.route(logits, E)
+    dg, dl = oracle.router_bwd(1, gu, dn, x, dy, logits, ids, toks)
+    for t in range(T):
+        l = torch.tensor(logits[t].astype(np.float64), requires_grad=True)
+        up = torch.zeros(E, dtype=torch.float64)
+        up[torch.from_numpy(ids[t].astype(np.int64))] = torch.from_numpy(dg[t])
+        torch.softmax(l, 0).backward(up)
+        np.testing.assert_allclose(dl[t], l.grad.numpy(), rtol=1e-12, atol=1e-14)
+
+
 # ------------------------------------------------------- storage accounting
 
 def test_storage_accounting_worked_example():
