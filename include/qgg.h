@@ -181,6 +181,31 @@ qgg_status moe_dx_bwd(const qgg_qweight* w_gate_up, const qgg_qweight* w_down,
                       int chunk, void* workspace, size_t ws_bytes, uint16_t* dx,
                       qgg_stream_t stream);
 
+/* moe_router_bwd -- the gradient a trainable router receives through the
+ * frozen base: L = <dY, y> of moe_ffn_fwd differentiated with respect to the
+ * gates and the router logits, the routing choice held fixed (top-k selection
+ * is piecewise constant in the logits).  The Orbit page (section 时刻细节)
+ * freezes the base and trains what sits beside it; the router's own logits
+ * stay in high precision ("超大规模开放权重模型技术解析", section 三).
+ *   dgates[t][j]  = <dY[t], o[pair(t,j)]>, formed as <dY[t] . W_down, a> in
+ *                   the epilogue of the down-projection backward (the same
+ *                   value by the adjoint identity), fp32 partial sums over
+ *                   256-column pieces added in ascending order;
+ *   dlogits[t][e] = g_j (dg_j - sum_i g_i dg_i) when e is token t's j-th
+ *                   kept expert, 0 for every other expert (the backward of
+ *                   the softmax over the kept logits).
+ * Arguments as moe_dx_bwd, plus topk_ids [T][k] (from moe_route) and three
+ * outputs: dx [T][d] BF16 as moe_dx_bwd (nullable: then the gate_up backward
+ * GEMM is skipped), dgates [T][k] fp32 (nullable), dlogits [T][E] fp32
+ * (nullable; every entry written).  At least one of dgates / dlogits must be
+ * given.  Same shape limits, workspace (QGG_CALL_DX_BWD) and errors as
+ * moe_dx_bwd; deterministic. */
+qgg_status moe_router_bwd(const qgg_qweight* w_gate_up, const qgg_qweight* w_down,
+                          const uint16_t* dy, const int32_t* topk_ids, const float* topk_gates,
+                          const qgg_perm* p, const uint16_t* h_saved, int T, int d, int E, int k,
+                          int inter, int variant, int chunk, void* workspace, size_t ws_bytes,
+                          uint16_t* dx, float* dgates, float* dlogits, qgg_stream_t stream);
+
 /* qgg_repack_weights -- copy a QGG_LAYOUT_ROWS weight tensor into the
  * QGG_LAYOUT_MFMA order: packed_out gets E*N*K/2 bytes, scales_out E*N*K/32
  * scale entries (device buffers the caller owns, not aliasing the source).

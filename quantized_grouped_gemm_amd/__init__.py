@@ -6,7 +6,7 @@ the current HIP stream.  PyTorch supplies device memory and streams.  If the
 library is not built, every call raises; there is no fallback.
 
 Names follow the C-ABI in ``include/qgg.h``: ``moe_route``, ``expert_permute``,
-``dequant_grouped_gemm``, ``moe_ffn_fwd``, ``moe_dx_bwd``.
+``dequant_grouped_gemm``, ``moe_ffn_fwd``, ``moe_dx_bwd``, ``moe_router_bwd``.
 """
 from __future__ import annotations
 
@@ -38,7 +38,8 @@ STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too sm
 
 # Every symbol include/qgg.h declares.
 EXPORTS = ("moe_route", "expert_permute", "dequant_grouped_gemm", "moe_ffn_fwd", "moe_dx_bwd",
-           "qgg_repack_weights", "qgg_workspace_bytes", "qgg_status_string", "qgg_version")
+           "moe_router_bwd", "qgg_repack_weights", "qgg_workspace_bytes", "qgg_status_string",
+           "qgg_version")
 
 _lib = None
 
@@ -77,6 +78,9 @@ def lib():
         L.moe_dx_bwd.argtypes = [ctypes.POINTER(_QWeight), ctypes.POINTER(_QWeight), P, P,
                                  ctypes.POINTER(_Perm), P, i32, i32, i32, i32, i32, i32, i32, P,
                                  sz, P, P]
+        L.moe_router_bwd.argtypes = [ctypes.POINTER(_QWeight), ctypes.POINTER(_QWeight), P, P, P,
+                                     ctypes.POINTER(_Perm), P, i32, i32, i32, i32, i32, i32, i32,
+                                     P, sz, P, P, P, P]
         L.qgg_repack_weights.argtypes = [ctypes.POINTER(_QWeight), P, P, P]
         L.qgg_repack_weights.restype = ctypes.c_int
         L.qgg_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32,
@@ -86,7 +90,7 @@ def lib():
         L.qgg_status_string.restype = ctypes.c_char_p
         L.qgg_version.restype = ctypes.c_char_p
         for f in ("moe_route", "expert_permute", "dequant_grouped_gemm", "moe_ffn_fwd",
-                  "moe_dx_bwd"):
+                  "moe_dx_bwd", "moe_router_bwd"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -291,3 +295,26 @@ def moe_dx_bwd(w_gate_up: QWeight, w_down: QWeight, dy, topk_gates, perm: Perm, 
                             ctypes.byref(pc), _ptr(h_saved), T, d, E, k, inter, variant, chunk,
                             _ptr(buf), buf.numel(), _ptr(dx), _stream()), "moe_dx_bwd")
     return dx
+
+
+def moe_router_bwd(w_gate_up: QWeight, w_down: QWeight, dy, topk_ids, topk_gates, perm: Perm,
+                   h_saved, k: int, variant: int = FUSED, chunk: int = 0, want_dx: bool = True,
+                   ws: Workspace | None = None):
+    """{"dx": [T,d] BF16 or None, "dgates": [T,k] fp32, "dlogits": [T,E] fp32}: the
+    router gradient through the frozen base (and the input gradient if want_dx)."""
+    import torch
+    T, d = dy.shape
+    E = w_gate_up.E
+    inter = w_gate_up.N // 2
+    dev = dy.device
+    dx = torch.empty((T, d), dtype=torch.bfloat16, device=dev) if want_dx else None
+    dg = torch.empty((T, k), dtype=torch.float32, device=dev)
+    dl = torch.empty((T, E), dtype=torch.float32, device=dev)
+    nb, _ = workspace_bytes(CALL_DX_BWD, T, d, E, k, inter, variant, chunk)
+    buf = (ws or _default_ws).get(nb, dev)
+    g, dn, pc = w_gate_up.c(), w_down.c(), perm.c()
+    _check(lib().moe_router_bwd(ctypes.byref(g), ctypes.byref(dn), _ptr(dy), _ptr(topk_ids),
+                                _ptr(topk_gates), ctypes.byref(pc), _ptr(h_saved), T, d, E, k,
+                                inter, variant, chunk, _ptr(buf), buf.numel(), _ptr(dx), _ptr(dg),
+                                _ptr(dl), _stream()), "moe_router_bwd")
+    return {"dx": dx, "dgates": dg, "dlogits": dl}

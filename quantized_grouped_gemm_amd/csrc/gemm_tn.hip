@@ -389,6 +389,7 @@ __device__ __forceinline__ void gemm_tn_item(const GemmArgs& g, const LdsRing4& 
           const u32x4_t* hup = reinterpret_cast<const u32x4_t*>(g.h + hb + g.inter);
           const u32x4_t hg2[2] = {hgp[0], hgp[1]}, hu2[2] = {hup[0], hup[1]};
           uint32_t og[8], ou[8];
+          float gp = 0.f;   // this thread's 16 terms of <dY . W_down, a>
 #pragma unroll
           for (int e = 0; e < 16; e += 2) {
             float rg[2], ru[2];
@@ -403,9 +404,17 @@ __device__ __forceinline__ void gemm_tn_item(const GemmArgs& g, const LdsRing4& 
               const float dsilu = sg * (1.0f + hg * (1.0f - sg));
               rg[h2] = da * hu * dsilu;
               ru[h2] = da * hg * sg;
+              gp = fmaf(v[e + h2], hg * sg * hu, gp);
             }
             og[e >> 1] = (uint32_t)bf16_hw_t(rg[0]) | ((uint32_t)bf16_hw_t(rg[1]) << 16);
             ou[e >> 1] = (uint32_t)bf16_hw_t(ru[0]) | ((uint32_t)bf16_hw_t(ru[1]) << 16);
+          }
+          if (g.gpart) {
+            // the 16 threads of a row are 16 consecutive lanes: a fixed
+            // butterfly gives every one the row's sum over the 256 columns
+#pragma unroll
+            for (int m = 1; m < 16; m <<= 1) gp += __shfl_xor(gp, m, 16);
+            if (eseg == 0) g.gpart[orow * (g.inter / 256) + c0 / 256] = gp;
           }
           u32x4_t* yg = reinterpret_cast<u32x4_t*>(g.y + orow * g.ldy + ecol);
           u32x4_t* yu = reinterpret_cast<u32x4_t*>(g.y + orow * g.ldy + g.inter + ecol);

@@ -164,7 +164,7 @@ qgg_status qgg_repack_weights(const qgg_qweight* src, uint8_t* packed_out, void*
 //  PERMUTE  segment counts
 //  GEMM     plan (tiles, chunk table) | BF16 chunk scratch (CHUNKED)
 //  FFN_FWD  segment counts | plan | a [P][inter] | o [P][d] | scratch
-//  DX_BWD   plan | dH [P][2*inter] | dXp [P][d] | scratch
+//  DX_BWD   plan | dH [P][2*inter] | dXp [P][d] | scratch | gate partials [P][inter/256] fp32
 size_t qgg_workspace_bytes(int call, int T, int d, int E, int k, int N_or_inter, int variant,
                            int chunk, size_t* scratch_bytes) {
   if (scratch_bytes) *scratch_bytes = 0;
@@ -200,6 +200,7 @@ size_t qgg_workspace_bytes(int call, int T, int d, int E, int k, int N_or_inter,
       cv.take<char>((size_t)P * d * 2);
       if (variant == QGG_CHUNKED) scratch = (size_t)C * 2 * I * d * 2;
       cv.take<char>(scratch);
+      cv.take<char>((size_t)P * (I / 256 > 0 ? I / 256 : 1) * 4);
       break;
     }
     default:
@@ -381,18 +382,26 @@ qgg_status moe_ffn_fwd(const qgg_qweight* w_gate_up, const qgg_qweight* w_down,
   return QGG_OK;
 }
 
-qgg_status moe_dx_bwd(const qgg_qweight* w_gate_up, const qgg_qweight* w_down,
-                      const uint16_t* dy, const float* topk_gates, const qgg_perm* p,
-                      const uint16_t* h_saved, int T, int d, int E, int k, int inter, int variant,
-                      int chunk, void* workspace, size_t ws_bytes, uint16_t* dx,
-                      qgg_stream_t stream) {
+// Shared body of moe_dx_bwd and moe_router_bwd.  dx == nullptr skips the
+// gate_up backward GEMM and the scatter-sum; dgates / dlogits != nullptr add
+// the router gradient (partials from the SwiGLU-backward epilogue, then one
+// small kernel).
+static qgg_status backward(const qgg_qweight* w_gate_up, const qgg_qweight* w_down,
+                           const uint16_t* dy, const int32_t* topk_ids, const float* topk_gates,
+                           const qgg_perm* p, const uint16_t* h_saved, int T, int d, int E,
+                           int k, int inter, int variant, int chunk, void* workspace,
+                           size_t ws_bytes, uint16_t* dx, float* dgates, float* dlogits,
+                           qgg_stream_t stream) {
   if (!valid_route_dims(T, E, k) || d <= 0 || inter <= 0 || chunk < 0) return QGG_ERR_INVALID_ARG;
   if (!valid_weight(w_gate_up, E, 2 * inter, d) || !valid_weight(w_down, E, d, inter))
     return QGG_ERR_INVALID_ARG;
   if (w_gate_up->fmt != w_down->fmt) return QGG_ERR_INVALID_ARG;
   if (variant != QGG_CHUNKED && variant != QGG_FUSED) return QGG_ERR_INVALID_ARG;
   if (!valid_perm(p)) return QGG_ERR_INVALID_ARG;
-  if (T > 0 && (!dy || !topk_gates || !h_saved || !dx)) return QGG_ERR_INVALID_ARG;
+  const bool router = dgates != nullptr || dlogits != nullptr;
+  if (T > 0 && (!dy || !topk_gates || !h_saved)) return QGG_ERR_INVALID_ARG;
+  if (T > 0 && !dx && !router) return QGG_ERR_INVALID_ARG;
+  if (T > 0 && dlogits && !topk_ids) return QGG_ERR_INVALID_ARG;
   if (d % 256 || inter % 256) return QGG_ERR_UNSUPPORTED;
   const int64_t P = (int64_t)T * k;
   if (!a_fits(T, d) || !a_fits(P, 2 * inter)) return QGG_ERR_UNSUPPORTED;
@@ -408,6 +417,7 @@ qgg_status moe_dx_bwd(const qgg_qweight* w_gate_up, const qgg_qweight* w_down,
   uint16_t* dh = cv.take<uint16_t>((size_t)P * 2 * inter * 2);
   uint16_t* dxp = cv.take<uint16_t>((size_t)P * d * 2);
   uint16_t* sbuf = cv.take<uint16_t>(scratch);
+  float* gpart = cv.take<float>((size_t)P * (inter / 256) * 4);
   const PermPtrs pp = to_ptrs(p);
   QGG_HIP(launch_tile_plan(pp, E, 32 * pl.mb, variant == QGG_CHUNKED ? C : 0, pl.tiles,
                            pl.chunk_first, stream));
@@ -426,6 +436,7 @@ qgg_status moe_dx_bwd(const qgg_qweight* w_gate_up, const qgg_qweight* w_down,
   dn.inter = inter;
   dn.h = const_cast<uint16_t*>(h_saved);
   dn.gates = topk_gates;
+  dn.gpart = router ? gpart : nullptr;
   // dXp = dH . W_gate_up
   GemmArgs gu = base_args(w_gate_up, pl);
   gu.a = dh;
@@ -440,7 +451,7 @@ qgg_status moe_dx_bwd(const qgg_qweight* w_gate_up, const qgg_qweight* w_down,
 
   if (variant == QGG_FUSED) {
     QGG_HIP(launch_gemm_tn(dn, pl.mb, stream));
-    QGG_HIP(launch_gemm_tn(gu, pl.mb, stream));
+    if (dx) QGG_HIP(launch_gemm_tn(gu, pl.mb, stream));
   } else {
     const int nch = chunk_iterations(E, P, C);
     dn.src = gu.src = kSrcBF16;
@@ -452,14 +463,38 @@ qgg_status moe_dx_bwd(const qgg_qweight* w_gate_up, const qgg_qweight* w_down,
       QGG_HIP(launch_dequant(w_down->fmt, w_down->packed, w_down->scales, w_down->layout, d,
                              inter, p->active, p->n_active, c * C, C, true, sbuf, stream));
       QGG_HIP(launch_gemm_tn(dn, pl.mb, stream));
+      if (!dx) continue;
       QGG_HIP(launch_dequant(w_gate_up->fmt, w_gate_up->packed, w_gate_up->scales,
                              w_gate_up->layout, 2 * inter, d, p->active, p->n_active, c * C, C,
                              true, sbuf, stream));
       QGG_HIP(launch_gemm_tn(gu, pl.mb, stream));
     }
   }
-  QGG_HIP(launch_combine(dxp, d, p->inv_perm, nullptr, T, k, dx, stream));
+  if (dx) QGG_HIP(launch_combine(dxp, d, p->inv_perm, nullptr, T, k, dx, stream));
+  if (router)
+    QGG_HIP(launch_router_bwd(gpart, inter / 256, p->inv_perm, topk_ids, topk_gates, T, E, k,
+                              dgates, dlogits, stream));
   return QGG_OK;
+}
+
+qgg_status moe_dx_bwd(const qgg_qweight* w_gate_up, const qgg_qweight* w_down,
+                      const uint16_t* dy, const float* topk_gates, const qgg_perm* p,
+                      const uint16_t* h_saved, int T, int d, int E, int k, int inter, int variant,
+                      int chunk, void* workspace, size_t ws_bytes, uint16_t* dx,
+                      qgg_stream_t stream) {
+  if (T > 0 && !dx) return QGG_ERR_INVALID_ARG;
+  return backward(w_gate_up, w_down, dy, nullptr, topk_gates, p, h_saved, T, d, E, k, inter,
+                  variant, chunk, workspace, ws_bytes, dx, nullptr, nullptr, stream);
+}
+
+qgg_status moe_router_bwd(const qgg_qweight* w_gate_up, const qgg_qweight* w_down,
+                          const uint16_t* dy, const int32_t* topk_ids, const float* topk_gates,
+                          const qgg_perm* p, const uint16_t* h_saved, int T, int d, int E, int k,
+                          int inter, int variant, int chunk, void* workspace, size_t ws_bytes,
+                          uint16_t* dx, float* dgates, float* dlogits, qgg_stream_t stream) {
+  if (T > 0 && !dgates && !dlogits) return QGG_ERR_INVALID_ARG;
+  return backward(w_gate_up, w_down, dy, topk_ids, topk_gates, p, h_saved, T, d, E, k, inter,
+                  variant, chunk, workspace, ws_bytes, dx, dgates, dlogits, stream);
 }
 
 }  // extern "C"

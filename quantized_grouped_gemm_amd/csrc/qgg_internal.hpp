@@ -49,10 +49,19 @@ struct GemmArgs {
   int inter;                     // SwiGLU width
   uint16_t* h;                   // fwd: optional h save [P][2I]; bwd: saved h
   const float* gates;            // bwd SwiGLU epilogue: topk gates [T*k]
+  float* gpart;                  // bwd SwiGLU epilogue, optional: per sorted row and
+                                 // 256-column item, sum over the item of
+                                 // (dY . W_down)[c] * silu(gate)[c] * up[c]; [P][inter/256]
 };
 
 hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* gates,
                         int32_t* err, hipStream_t s);
+// Router gradient from the per-pair partials of <dY . W_down, a> (gpart,
+// [P][nitems] by sorted row): dgates [T][k] and dlogits [T][E] (either
+// nullable; dlogits fully written).
+hipError_t launch_router_bwd(const float* gpart, int nitems, const int32_t* inv_perm,
+                             const int32_t* ids, const float* gates, int T, int E, int k,
+                             float* dgates, float* dlogits, hipStream_t s);
 size_t permute_ws_bytes(int64_t P, int E);
 hipError_t launch_permute(const int32_t* ids, int64_t P, int E, const PermPtrs& pp, int32_t* err,
                           void* ws, hipStream_t s);

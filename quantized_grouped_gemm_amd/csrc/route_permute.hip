@@ -105,6 +105,49 @@ __global__ __launch_bounds__(256) void k_route(const float* __restrict__ logits,
   }
 }
 
+// ------------------------------------------------------- router backward
+// Gradient handed back to the router when the base is frozen and the routing
+// choice is held fixed.  One wavefront per token; lane j < k owns pair
+// (t, j): dg_j = <dY[t], o[t, j]>, summed from the per-item partials the
+// SwiGLU-backward epilogue left in gpart (ascending item).  The gates are
+// the softmax of the kept logits, whose backward is
+// dl_j = g_j (dg_j - sum_i g_i dg_i); experts not kept get 0.
+__global__ __launch_bounds__(256) void k_router_bwd(const float* __restrict__ gpart, int nitems,
+                                                    const int32_t* __restrict__ inv_perm,
+                                                    const int32_t* __restrict__ ids,
+                                                    const float* __restrict__ gates, int T, int E,
+                                                    int k, float* __restrict__ dgates,
+                                                    float* __restrict__ dlogits) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + threadIdx.x / 64;
+  if (t >= T) return;
+  float dg = 0.f, g = 0.f;
+  int id = -1;
+  if (lane < k) {
+    const int64_t q = (int64_t)t * k + lane;
+    const float* row = gpart + (int64_t)inv_perm[q] * nitems;
+    for (int c = 0; c < nitems; ++c) dg += row[c];
+    g = gates[q];
+    id = ids[q];
+    if (dgates) dgates[q] = dg;
+  }
+  if (!dlogits) return;
+  // sum_i g_i dg_i in ascending i, the same value in every lane
+  const int gdg = __float_as_int(g * dg);
+  float sgd = 0.f;
+  for (int i = 0; i < k; ++i) sgd += __int_as_float(__builtin_amdgcn_readlane(gdg, i));
+  const float dl = g * (dg - sgd);
+  const int dli = __float_as_int(dl);
+  float* out = dlogits + (int64_t)t * E;
+  for (int e0 = 0; e0 < E; e0 += 64) {
+    const int e = e0 + lane;
+    float v = 0.f;
+    for (int i = 0; i < k; ++i)
+      if (__builtin_amdgcn_readlane(id, i) == e) v = __int_as_float(__builtin_amdgcn_readlane(dli, i));
+    if (e < E) out[e] = v;
+  }
+}
+
 // -------------------------------------------------------------- permute
 // Pairs are split into segments of kSeg (one counting workgroup each).
 constexpr int kSeg = 4096;
@@ -354,6 +397,15 @@ hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* ids, 
   if (T == 0) return hipSuccess;
   hipLaunchKernelGGL(k_route, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, k, ids, gates,
                      err);
+  return hipGetLastError();
+}
+
+hipError_t launch_router_bwd(const float* gpart, int nitems, const int32_t* inv_perm,
+                             const int32_t* ids, const float* gates, int T, int E, int k,
+                             float* dgates, float* dlogits, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_router_bwd, dim3((T + 3) / 4), dim3(256), 0, s, gpart, nitems, inv_perm,
+                     ids, gates, T, E, k, dgates, dlogits);
   return hipGetLastError();
 }
 

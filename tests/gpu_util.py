@@ -56,3 +56,37 @@ def assert_close(out, ref, tol=TOL, what=""):
 
 def sync():
     torch.cuda.synchronize()
+
+
+def check_router_grads(dg, dl, dg_ref, dl_ref, ids, gates, tol=TOL, what=""):
+    """dgates and dlogits against the oracle.
+
+    dgates: dg_j is a dot product over the intermediate width whose terms take
+    their size from dY, W_down and h, which do not depend on the token; the
+    BF16 rounding of h (relative 2^-9 per term) gives an error that scales
+    with that common term size, not with the particular dg_j, which can be
+    small by cancellation.  So the floor of the relative error is the RMS of
+    dg over the whole tensor (not over one token's k values).
+
+    dlogits: dl_j = g_j (dg_j - sum_i g_i dg_i) cancels when the dg_j are
+    close, so its relative error is not bounded by that of dg.  With
+    |err dg_i| <= tol * m (m = max of the token's |dg_i| and the floor above),
+    |err dl_j| <= g_j (1 + sum_i g_i) tol m = 2 g_j tol m, up to the fp32
+    rounding of the final product.  Entries outside the kept experts must be
+    exactly 0."""
+    dg = np.asarray(dg, np.float64)
+    dl = np.asarray(dl, np.float64)
+    assert np.all(np.isfinite(dg)) and np.all(np.isfinite(dl)), f"{what}: non-finite output"
+    floor = max(float(np.sqrt(np.mean(dg_ref * dg_ref))), 1e-30)
+    e = float(np.max(np.abs(dg - dg_ref) / np.maximum(np.abs(dg_ref), floor)))
+    assert e <= tol, f"{what} dgates: max rel err {e:.3e} > {tol}"
+    T, k = ids.shape
+    rows = np.arange(T)[:, None]
+    kept = np.zeros(dl.shape, bool)
+    kept[rows, ids] = True
+    assert np.all(dl[~kept] == 0.0), f"{what}: nonzero dlogits outside the kept experts"
+    m = np.maximum(np.max(np.abs(dg_ref), axis=1, keepdims=True), floor)
+    bound = 2.0 * np.asarray(gates, np.float64) * tol * m + 1e-6 * np.abs(dl_ref[rows, ids])
+    err = np.abs(dl[rows, ids] - dl_ref[rows, ids])
+    assert np.all(err <= bound), f"{what}: dlogits error {np.max(err / bound):.3f} x bound"
+    return e

@@ -13,7 +13,8 @@ import oracle
 import quantized_grouped_gemm_amd as qgg
 import synth.configs as sc
 
-from .gpu_util import DEV, assert_close, bf16_to_f64, dev_bf16, dev_weights, host_u16, sync
+from .gpu_util import (DEV, assert_close, bf16_to_f64, check_router_grads, dev_bf16,
+                       dev_weights, host_u16, sync)
 
 pytestmark = [pytest.mark.gpu, pytest.mark.timeout(900)]
 
@@ -137,6 +138,26 @@ def test_moe_dx_bwd_full():
     dx_ref, _ = oracle.dx(cfg.fmt, gu, dn, x, dy, ids_ref, gates_ref, toks)
     e = assert_close(bf16_to_f64(dx0[toks]), dx_ref, what="dx")
     print(f"case dx: 32 tokens checked, max rel err {e:.2e}", flush=True)
+    # router gradient, same launch configuration: dx bit-identical to the
+    # plain backward, dgates / dlogits identical across variants, sampled
+    # tokens against the oracle
+    r = qgg.moe_router_bwd(wg, wd, dyd, fwd["topk_ids"], fwd["topk_gates"], fwd["perm"],
+                           fwd["h"], cfg.k, qgg.FUSED, 0)
+    sync()
+    np.testing.assert_array_equal(host_u16(r["dx"]), dx0, err_msg="router_bwd dx")
+    dg0, dl0 = r["dgates"].cpu().numpy(), r["dlogits"].cpu().numpy()
+    del r
+    rc = qgg.moe_router_bwd(wg, wd, dyd, fwd["topk_ids"], fwd["topk_gates"], fwd["perm"],
+                            fwd["h"], cfg.k, qgg.CHUNKED, cfg.chunks[0], want_dx=False)
+    sync()
+    np.testing.assert_array_equal(rc["dgates"].cpu().numpy(), dg0)
+    np.testing.assert_array_equal(rc["dlogits"].cpu().numpy(), dl0)
+    del rc
+    rt = toks[:8]
+    dg_ref, dl_ref = oracle.router_bwd(cfg.fmt, gu, dn, x, dy, logits, ids_ref, rt)
+    gates = fwd["topk_gates"].cpu().numpy()
+    e = check_router_grads(dg0[rt], dl0[rt], dg_ref, dl_ref, ids_ref[rt], gates[rt], what="router")
+    print(f"case router: {rt.size} tokens checked, dgates max rel err {e:.2e}", flush=True)
     del wg, wd, fwd, dyd
     _FFN_CACHE.clear()
     _free()

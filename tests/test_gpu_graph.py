@@ -1,7 +1,7 @@
 """HIP-graph capture of whole calls.  The entry points never synchronize with
 the host (the chunked variant runs a fixed-length chunk loop whose bounds are
-read on the device), so moe_ffn_fwd and moe_dx_bwd can be captured once and
-replayed.  Each replay, with unrelated eager work and host synchronizations
+read on the device), so moe_ffn_fwd, moe_dx_bwd and moe_router_bwd can be
+captured once and replayed.  Each replay, with unrelated eager work and host synchronizations
 between replays, must reproduce the eager result bit for bit."""
 import numpy as np
 import pytest
@@ -41,9 +41,14 @@ def test_ffn_and_dx_graph_replays_match_eager(cfg, variant, chunk):
         r = qgg.moe_ffn_fwd(wg, wd, x, logits, cfg.k, variant, chunk, save_h=True)
         dx = qgg.moe_dx_bwd(wg, wd, dy, r["topk_gates"], r["perm"], r["h"], cfg.k, variant,
                             chunk)
-        return r["y"], r["h"], dx
+        g = qgg.moe_router_bwd(wg, wd, dy, r["topk_ids"], r["topk_gates"], r["perm"], r["h"],
+                               cfg.k, variant, chunk, want_dx=False)
+        return r["y"], r["h"], dx, g["dgates"], g["dlogits"]
 
-    y0, h0, dx0 = (host_u16(t) for t in step())          # eager reference
+    def host(outs):
+        return [host_u16(t) for t in outs[:3]] + [t.cpu().numpy() for t in outs[3:]]
+
+    ref = host(step())                                     # eager reference
     sync()
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -57,10 +62,9 @@ def test_ffn_and_dx_graph_replays_match_eager(cfg, variant, chunk):
     for rep in range(3):
         graph.replay()
         sync()
-        got = [host_u16(t) for t in outs]
-        np.testing.assert_array_equal(got[0], y0, err_msg=f"y replay {rep}")
-        np.testing.assert_array_equal(got[1], h0, err_msg=f"h replay {rep}")
-        np.testing.assert_array_equal(got[2], dx0, err_msg=f"dx replay {rep}")
+        got = host(outs)
+        for name, a, b in zip(("y", "h", "dx", "dgates", "dlogits"), got, ref):
+            np.testing.assert_array_equal(a, b, err_msg=f"{name} replay {rep}")
         for t in outs:                                     # eager work between replays
             t.zero_()
         step()

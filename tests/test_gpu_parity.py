@@ -11,8 +11,8 @@ import quantized_grouped_gemm_amd as qgg
 import synth
 from synth.configs import CONFIGS, STREAM, Config, scaled
 
-from .gpu_util import (DEV, LAYOUTS, assert_close, bf16_to_f64, dev_bf16, dev_weights, host_u16,
-                       sync)
+from .gpu_util import (DEV, LAYOUTS, assert_close, bf16_to_f64, check_router_grads, dev_bf16,
+                       dev_weights, host_u16, sync)
 
 pytestmark = pytest.mark.gpu
 
@@ -374,6 +374,51 @@ def test_moe_dx_bwd_parity(cfg):
         assert_close(bf16_to_f64(outs[-1]), dx_ref, what=f"{cfg.name} dx v{variant} c{chunk}")
     for o in outs[1:]:
         np.testing.assert_array_equal(o, outs[0])
+
+
+ROUTER_CASES = DX_CASES + [
+    scaled(CONFIGS["mxfp4_dx_bwd"], T=64, d=256, E=6, k=1, N=512, inter=256, chunks=(4,),
+           name="mxfp4_router_k1"),
+]
+
+
+@pytest.mark.parametrize("cfg", ROUTER_CASES, ids=lambda c: c.name)
+def test_moe_router_bwd_parity(cfg):
+    print(f"case {cfg.name}", flush=True)
+    logits = synth.configs.router_logits(cfg)
+    x = synth.configs.activations(cfg)
+    dy = synth.configs.grad_output(cfg)
+    gu, dn = _ffn_weights(cfg)
+    ids_ref, gates_ref = oracle.route(logits, cfg.k)
+    toks = np.arange(cfg.T, dtype=np.int32)
+    dg_ref, dl_ref = oracle.router_bwd(cfg.fmt, gu, dn, x, dy, logits, ids_ref, toks)
+    wg, wd = dev_weights(cfg.fmt, *gu), dev_weights(cfg.fmt, *dn)
+    fwd = qgg.moe_ffn_fwd(wg, wd, dev_bf16(x), torch.from_numpy(logits).to(DEV), cfg.k,
+                          qgg.FUSED, 0, save_h=True)
+    dyd = dev_bf16(dy)
+    dx_plain = host_u16(qgg.moe_dx_bwd(wg, wd, dyd, fwd["topk_gates"], fwd["perm"], fwd["h"],
+                                       cfg.k, qgg.FUSED, 0))
+    gates = fwd["topk_gates"].cpu().numpy()
+    outs = []
+    runs = [(lo, v, c, want_dx) for lo in LAYOUTS for v, c in
+            [(qgg.FUSED, 0), (qgg.CHUNKED, cfg.chunks[0])] for want_dx in (True, False)]
+    for layout, variant, chunk, want_dx in runs:
+        wg = dev_weights(cfg.fmt, *gu, layout=layout)
+        wd = dev_weights(cfg.fmt, *dn, layout=layout)
+        r = qgg.moe_router_bwd(wg, wd, dyd, fwd["topk_ids"], fwd["topk_gates"], fwd["perm"],
+                               fwd["h"], cfg.k, variant, chunk, want_dx=want_dx)
+        sync()
+        what = f"{cfg.name} v{variant} c{chunk} dx{int(want_dx)}"
+        dg, dl = r["dgates"].cpu().numpy(), r["dlogits"].cpu().numpy()
+        check_router_grads(dg, dl, dg_ref, dl_ref, ids_ref, gates, what=what)
+        if cfg.k == 1:
+            assert np.all(dl == 0.0), f"{what}: k = 1 leaves the gate constant"
+        if want_dx:
+            np.testing.assert_array_equal(host_u16(r["dx"]), dx_plain, err_msg=what)
+        outs.append((dg, dl))
+    for dg, dl in outs[1:]:
+        np.testing.assert_array_equal(dg, outs[0][0])
+        np.testing.assert_array_equal(dl, outs[0][1])
 
 
 def test_repeat_runs_bit_identical_and_outputs_fully_written():
