@@ -280,18 +280,14 @@ __device__ __forceinline__ void gemm_nt_item(const GemmArgs& g,
       return *reinterpret_cast<const bf16x8_t*>(at + mb * 32 * kStageRowB +
                                                 aoff[s ^ ((mb & 1) << 2)]);
     };
-    // A operands: double-buffered across the four K sub-steps when the
-    // tile is short; loaded just in time when registers are scarce
-    constexpr bool kDbl = NMB <= 3;
-    bf16x8_t acur[NMB], anxt[NMB];
+    // A operands: each block's operand for the next K sub-step is read as
+    // soon as its MFMAs for this sub-step have issued, so the read lands
+    // behind the other blocks' MFMAs with one register set per block
+    bf16x8_t acur[NMB];
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb) acur[mb] = a_op(mb, 0);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      if (kDbl && s < 3) {
-#pragma unroll
-        for (int mb = 0; mb < NMB; ++mb) anxt[mb] = a_op(mb, s + 1);
-      }
       const bf16x8_t b0 = b_operand<SRC>(slot[0], sc0, s);
       const bf16x8_t b1 = b_operand<SRC>(slot[1], sc1, s);
       if (s == 3) {
@@ -301,13 +297,9 @@ __device__ __forceinline__ void gemm_nt_item(const GemmArgs& g,
       }
 #pragma unroll
       for (int mb = 0; mb < NMB; ++mb) {
-        if (!kDbl && s > 0) acur[mb] = a_op(mb, s);
         acc[mb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(acur[mb], b0, acc[mb][0], 0, 0, 0);
         acc[mb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(acur[mb], b1, acc[mb][1], 0, 0, 0);
-      }
-      if (kDbl && s < 3) {
-#pragma unroll
-        for (int mb = 0; mb < NMB; ++mb) acur[mb] = anxt[mb];
+        if (s < 3) acur[mb] = a_op(mb, s + 1);
       }
     }
     if constexpr (SRC != kSrcBF16) {
