@@ -295,11 +295,11 @@ __device__ __forceinline__ void gemm_tn_item(const GemmArgs& g, const LdsRing4& 
     copy_a(st + kNBufA - 1, std::integral_constant<int, (ABUF + kNBufA - 1) % kNBufA>{});
     const uint8_t* at = As.b[ABUF];
     const uint8_t* bt = Bs[BBUF];
-    // all operand reads of the stage first, so their LDS latency overlaps
-    // instead of stalling every MFMA pair
+    // operand reads in the order the MFMAs consume them: sub-step 0's,
+    // then its first MFMA pair, then sub-step 1's reads behind the
+    // remaining sub-step 0 MFMAs
     bf16x8_t bop[2][2], aop[2][NMB];
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
+    auto read_ops = [&](int s) {
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
         const uint2 lo = lds_tr4(bt + 16 * s * kBRowB + broff[nb][0]);
@@ -309,17 +309,19 @@ __device__ __forceinline__ void gemm_tn_item(const GemmArgs& g, const LdsRing4& 
 #pragma unroll
       for (int mb = 0; mb < NMB; ++mb)
         aop[s][mb] = *reinterpret_cast<const bf16x8_t*>(at + mb * 32 * kARowB + aoff[s]);
-    }
+    };
+    auto mfma_pair = [&](int s, int mb) {
+      acc[mb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop[s][mb], bop[s][0], acc[mb][0], 0, 0, 0);
+      acc[mb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop[s][mb], bop[s][1], acc[mb][1], 0, 0, 0);
+    };
+    read_ops(0);
+    mfma_pair(0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    read_ops(1);
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
+    for (int mb = 1; mb < NMB; ++mb) mfma_pair(0, mb);
 #pragma unroll
-      for (int mb = 0; mb < NMB; ++mb) {
-        acc[mb][0] =
-            __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop[s][mb], bop[s][0], acc[mb][0], 0, 0, 0);
-        acc[mb][1] =
-            __builtin_amdgcn_mfma_f32_32x32x16_bf16(aop[s][mb], bop[s][1], acc[mb][1], 0, 0, 0);
-      }
-    }
+    for (int mb = 0; mb < NMB; ++mb) mfma_pair(1, mb);
     store_bt<SRC>(ring[SLOT], Bs[BBUF ^ 1], bwoff);
     {
       const int nx = st + 1 + kRing;

@@ -93,9 +93,9 @@ __device__ __forceinline__ void dq8_mxfp4(uint32_t w, float scale, uint32_t out[
 // bf16_rne(q * s).  s512 = 512 s and neg8s = -8 s are exact powers-of-two
 // multiples of s (finite for every scale below 2^118).
 __device__ __forceinline__ void dq8_int4(uint32_t w, float s512, float neg8s, uint32_t out[4]) {
-  const uint32_t b = w ^ 0x88888888u;
-  const uint32_t lo = b & 0x0F0F0F0Fu;          // elements 0, 2, 4, 6
-  const uint32_t hi = (b >> 4) & 0x0F0F0F0Fu;   // elements 1, 3, 5, 7
+  // (x ^ 8) & 15 per byte: one three-input bitwise op for each half
+  const uint32_t lo = (w ^ 0x08080808u) & 0x0F0F0F0Fu;          // elements 0, 2, 4, 6
+  const uint32_t hi = ((w >> 4) ^ 0x08080808u) & 0x0F0F0F0Fu;   // elements 1, 3, 5, 7
   const f32x2_t e02 = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, false);
   const f32x2_t e46 = __builtin_amdgcn_cvt_pk_f32_fp8((int)lo, true);
   const f32x2_t e13 = __builtin_amdgcn_cvt_pk_f32_fp8((int)hi, false);
