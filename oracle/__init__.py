@@ -56,6 +56,8 @@ def _L():
         lib.oracle_dx.argtypes = [i32, P, P, P, P, i32, i64, i64, P, P, i32, P, P, i64, P, P, P]
         lib.oracle_router_bwd.argtypes = [i32, P, P, P, P, i32, i64, i64, P, P, P, i32, P, i64,
                                           P, P, P]
+        lib.oracle_lora_project.argtypes = [i32, P, P, i32, i64, i64, P, i64, P, P, i32,
+                                            ctypes.c_double, P, P, P, P]
         lib.oracle_silu.argtypes = [ctypes.c_double]
         lib.oracle_silu.restype = ctypes.c_double
         lib.oracle_silu_grad.argtypes = [ctypes.c_double]
@@ -183,6 +185,24 @@ def dx(fmt, gu, dn, x, dy, ids, gates, toks, want_da=False):
                           k, _p(np.ascontiguousarray(ids, np.int32)), _p(gates), toks.size,
                           _p(toks), _p(out), _p(da)), "dx")
     return out, da
+
+
+def lora_project(fmt, packed, scales, x, tok, expert, A, B, alpha, want_u=False):
+    """double y [npairs][N] = x W^T + alpha (x A^T) B^T per pair (A BF16 [E][r][K],
+    B BF16 [E][N][r]); with want_u also alpha * (x A^T) [npairs][r]."""
+    E, N, K2 = packed.shape
+    rank = A.shape[1]
+    assert A.shape == (E, rank, 2 * K2) and B.shape == (E, N, rank)
+    tok = np.ascontiguousarray(tok, np.int32)
+    expert = np.ascontiguousarray(expert, np.int32)
+    y = np.zeros((tok.size, N), np.float64)
+    u = np.zeros((tok.size, rank), np.float64) if want_u else None
+    _check(_L().oracle_lora_project(fmt, _p(packed), _p(scales), E, N, 2 * K2, _p(x), tok.size,
+                                    _p(tok), _p(expert), rank, float(alpha),
+                                    _p(np.ascontiguousarray(A, np.uint16)),
+                                    _p(np.ascontiguousarray(B, np.uint16)), _p(y), _p(u)),
+           "lora_project")
+    return (y, u) if want_u else y
 
 
 def router_bwd(fmt, gu, dn, x, dy, logits, ids, toks):

@@ -28,6 +28,8 @@
  *           gradient.  dO = g * dY[t]; dA = W_down^T dO; dH = [dA * up *
  *           silu'(gate) | dA * silu(gate)]; dXp = W_gu^T dH; dX[t] = sum over
  *           j ascending of dXp[t,j].  Gates are constants.
+ *  lora     Orbit page, opening section: a BF16 adapter on the frozen base.
+ *           LoRA form y = x W_e^T + alpha (x A_e^T) B_e^T, in double.
  *  router_bwd  The gradient the base hands back to a trainable router (the
  *           pages freeze the base, not the router): dg[t,j] = <dY[t], o[t,j]>,
  *           then reverse mode through the gate definition of route.  The
@@ -484,4 +486,49 @@ int oracle_router_bwd(int fmt, const uint8_t* gu_p, const void* gu_s, const uint
   free(p);
   free(dp);
   return rc;
+}
+
+/* ------------------------------------------------------ adapter (LoRA) */
+
+/* Orbit page, opening section: the base is frozen in its low-precision
+ * format and one BF16 adapter on top of it is what trains; the Orbit
+ * repository's issue #1 names LoRA as that adapter's common form.  LoRA form
+ * of one expert projection:
+ *   y[i][n] = sum_k x[t][k] W_e[n][k] + alpha * sum_j u[i][j] B_e[n][j],
+ *   u[i][j] = sum_k x[t][k] A_e[j][k]
+ * with t = tok[i], e = expert[i]; A is BF16 [E][rank][K], B BF16 [E][N][rank].
+ * Everything in double; u (nullable) receives alpha * u, as [npairs][rank]. */
+int oracle_lora_project(int fmt, const uint8_t* packed, const void* scales, int E, int64_t N,
+                        int64_t K, const uint16_t* x, int64_t npairs, const int32_t* tok,
+                        const int32_t* expert, int rank, double alpha, const uint16_t* A,
+                        const uint16_t* B, double* y, double* u_out) {
+  if (rank <= 0) return 1;
+  int rc = oracle_project(fmt, packed, scales, E, N, K, x, npairs, tok, expert, y);
+  if (rc) return rc;
+  double* xr = (double*)malloc(sizeof(double) * (size_t)K);
+  double* u = (double*)malloc(sizeof(double) * (size_t)rank);
+  if (!xr || !u) {
+    free(xr);
+    free(u);
+    return 3;
+  }
+  for (int64_t i = 0; i < npairs; ++i) {
+    const int64_t e = expert[i];
+    oracle_bf16_to_f64(x + (int64_t)tok[i] * K, K, xr);
+    for (int j = 0; j < rank; ++j) {
+      double acc = 0.0;
+      for (int64_t k = 0; k < K; ++k)
+        acc += xr[k] * (double)bf16_to_float(A[(e * rank + j) * K + k]);
+      u[j] = acc;
+      if (u_out) u_out[i * rank + j] = alpha * acc;
+    }
+    for (int64_t n = 0; n < N; ++n) {
+      double acc = 0.0;
+      for (int j = 0; j < rank; ++j) acc += u[j] * (double)bf16_to_float(B[(e * N + n) * rank + j]);
+      y[i * N + n] += alpha * acc;
+    }
+  }
+  free(xr);
+  free(u);
+  return 0;
 }

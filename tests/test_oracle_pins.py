@@ -431,6 +431,62 @@ def test_dx_adjoint_of_down_projection():
         assert abs(np.dot(gates[t, j] * dyf[t], Wd @ a) - np.dot(da[s], a)) < 1e-10
 
 
+# ------------------------------------------------------------- LoRA adapter
+
+def _bf16_bits_to_f64(u16):
+    return (np.asarray(u16, np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def _lora_inputs(fmt, P=7, T=5, K=128, N=64, E=3, rank=16, seed=7):
+    packed, scales = synth.qweights(seed, 3, fmt, E, N, K, std=0.2)
+    x = synth.normal_bf16(seed, 2, (T, K))
+    A = synth.normal_bf16(seed, 7, (E, rank, K), std=0.05)
+    B = synth.normal_bf16(seed, 8, (E, N, rank), std=0.05)
+    rng = np.random.default_rng(seed)
+    tok = rng.integers(0, T, P).astype(np.int32)
+    expert = rng.integers(0, E, P).astype(np.int32)
+    return packed, scales, x, A, B, tok, expert
+
+
+@pytest.mark.parametrize("fmt", [1, 2])
+def test_lora_project_matches_numpy_twin(fmt):
+    packed, scales, x, A, B, tok, expert = _lora_inputs(fmt)
+    alpha = 0.75
+    y, u = oracle.lora_project(fmt, packed, scales, x, tok, expert, A, B, alpha, want_u=True)
+    xf = _bf16_bits_to_f64(x)
+    for i in range(tok.size):
+        e = expert[i]
+        W = _decode_bits(fmt, packed[e], scales[e]).astype(np.float64)
+        Ae, Be = _bf16_bits_to_f64(A[e]), _bf16_bits_to_f64(B[e])
+        ui = Ae @ xf[tok[i]]
+        np.testing.assert_allclose(u[i], alpha * ui, rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(y[i], W @ xf[tok[i]] + alpha * (Be @ ui), rtol=1e-12, atol=1e-13)
+
+
+def test_lora_project_special_cases():
+    fmt = 2
+    packed, scales, x, A, B, tok, expert = _lora_inputs(fmt)
+    base = oracle.project(fmt, packed, scales, x, tok, expert)
+    # no adapter contribution: alpha = 0, or B = 0
+    assert np.array_equal(oracle.lora_project(fmt, packed, scales, x, tok, expert, A, B, 0.0), base)
+    assert np.array_equal(
+        oracle.lora_project(fmt, packed, scales, x, tok, expert, A, np.zeros_like(B), 2.0), base)
+    # rank-one adapter A = e_k0, B = e_n0 (per expert): column n0 gains alpha x[k0]
+    E, rank, K = A.shape
+    N = B.shape[1]
+    A1 = np.zeros_like(A)
+    B1 = np.zeros_like(B)
+    k0, n0 = 37, 11
+    A1[:, 0, k0] = 0x3F80          # BF16 1.0
+    B1[:, n0, 0] = 0x3F80
+    y = oracle.lora_project(fmt, packed, scales, x, tok, expert, A1, B1, 0.5)
+    d = y - base
+    xf = _bf16_bits_to_f64(x)
+    np.testing.assert_array_equal(d[:, n0], 0.5 * xf[tok, k0])
+    d[:, n0] = 0
+    assert np.all(d == 0)
+
+
 # ------------------------------------------------------------ router backward
 
 def _twin_pair_outputs(fmt, gu, dn, xf, ids, t):
