@@ -157,6 +157,33 @@ qgg_status dequant_grouped_gemm(const qgg_qweight* w, const uint16_t* a, int fla
                                 void* workspace, size_t ws_bytes, uint16_t* y,
                                 qgg_stream_t stream);
 
+/* LoRA adapter of one grouped projection (device arrays, BF16 bits):
+ * A [E][rank][K] (down), B [E][N][rank] (up); y gains alpha * (a A_e^T) B_e^T.
+ * rank is a multiple of 16 in [16, 128]. */
+typedef struct {
+  int32_t rank;
+  float alpha;
+  const uint16_t* A;
+  const uint16_t* B;
+} qgg_lora;
+
+/* lora_grouped_gemm -- dequant_grouped_gemm with a BF16 LoRA adapter on the
+ * frozen quantized base: y[i][:] = a_row(i) . W_e^T + u[i] . B_e^T with
+ * u[i][:] = alpha * a_row(i) . A_e^T.  Orbit page, opening section: the base
+ * stays frozen in its low-precision format and one BF16 adapter on top of it
+ * is what trains (the Orbit repository's issue #1 names LoRA as that
+ * adapter's common form).  u is formed first (fp32 accumulate, stored BF16 in
+ * u_out [P][rank], sorted order: the activation the adapter's backward
+ * needs); the up projection runs as extra MFMA steps on the same fp32
+ * accumulators as the base product, so y is rounded to BF16 once.  Arguments
+ * otherwise as dequant_grouped_gemm (same workspace); QGG_TRANSPOSE_W and
+ * QGG_DEQUANT_ONLY are rejected (QGG_ERR_INVALID_ARG), a rank outside the
+ * limits returns QGG_ERR_UNSUPPORTED. */
+qgg_status lora_grouped_gemm(const qgg_qweight* w, const qgg_lora* lora, const uint16_t* a,
+                             int flags, const qgg_perm* p, int T, int k, int variant, int chunk,
+                             void* workspace, size_t ws_bytes, uint16_t* u_out, uint16_t* y,
+                             qgg_stream_t stream);
+
 /* moe_ffn_fwd -- the SwiGLU expert FFN for a routed batch: route, permute,
  * h = x . W_gu^T (rows [0,inter) of W_gu are gate, [inter, 2*inter) up),
  * a = silu(gate) * up, o = a . W_down^T, y[t] = sum_j g[t,j] * o[pair(t,j)]

@@ -6,7 +6,8 @@ the current HIP stream.  PyTorch supplies device memory and streams.  If the
 library is not built, every call raises; there is no fallback.
 
 Names follow the C-ABI in ``include/qgg.h``: ``moe_route``, ``expert_permute``,
-``dequant_grouped_gemm``, ``moe_ffn_fwd``, ``moe_dx_bwd``, ``moe_router_bwd``.
+``dequant_grouped_gemm``, ``lora_grouped_gemm``, ``moe_ffn_fwd``, ``moe_dx_bwd``,
+``moe_router_bwd``.
 """
 from __future__ import annotations
 
@@ -37,9 +38,9 @@ CALL_DX_BWD = 4
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too small", 4: "HIP error"}
 
 # Every symbol include/qgg.h declares.
-EXPORTS = ("moe_route", "expert_permute", "dequant_grouped_gemm", "moe_ffn_fwd", "moe_dx_bwd",
-           "moe_router_bwd", "qgg_repack_weights", "qgg_workspace_bytes", "qgg_status_string",
-           "qgg_version")
+EXPORTS = ("moe_route", "expert_permute", "dequant_grouped_gemm", "lora_grouped_gemm",
+           "moe_ffn_fwd", "moe_dx_bwd", "moe_router_bwd", "qgg_repack_weights",
+           "qgg_workspace_bytes", "qgg_status_string", "qgg_version")
 
 _lib = None
 
@@ -52,6 +53,11 @@ class _QWeight(ctypes.Structure):
     _fields_ = [("fmt", ctypes.c_int32), ("E", ctypes.c_int32), ("N", ctypes.c_int32),
                 ("K", ctypes.c_int32), ("packed", ctypes.c_void_p), ("scales", ctypes.c_void_p),
                 ("layout", ctypes.c_int32)]
+
+
+class _Lora(ctypes.Structure):
+    _fields_ = [("rank", ctypes.c_int32), ("alpha", ctypes.c_float), ("A", ctypes.c_void_p),
+                ("B", ctypes.c_void_p)]
 
 
 class _Perm(ctypes.Structure):
@@ -72,6 +78,8 @@ def lib():
         L.expert_permute.argtypes = [P, i32, i32, i32, ctypes.POINTER(_Perm), P, i32, P, P, P, sz, P]
         L.dequant_grouped_gemm.argtypes = [ctypes.POINTER(_QWeight), P, i32, ctypes.POINTER(_Perm),
                                            i32, i32, i32, i32, P, sz, P, P]
+        L.lora_grouped_gemm.argtypes = [ctypes.POINTER(_QWeight), ctypes.POINTER(_Lora), P, i32,
+                                        ctypes.POINTER(_Perm), i32, i32, i32, i32, P, sz, P, P, P]
         L.moe_ffn_fwd.argtypes = [ctypes.POINTER(_QWeight), ctypes.POINTER(_QWeight), P, P, i32,
                                   i32, i32, i32, i32, i32, i32, P, P, ctypes.POINTER(_Perm), P, P,
                                   P, sz, P, P]
@@ -89,8 +97,8 @@ def lib():
         L.qgg_status_string.argtypes = [i32]
         L.qgg_status_string.restype = ctypes.c_char_p
         L.qgg_version.restype = ctypes.c_char_p
-        for f in ("moe_route", "expert_permute", "dequant_grouped_gemm", "moe_ffn_fwd",
-                  "moe_dx_bwd", "moe_router_bwd"):
+        for f in ("moe_route", "expert_permute", "dequant_grouped_gemm", "lora_grouped_gemm",
+                  "moe_ffn_fwd", "moe_dx_bwd", "moe_router_bwd"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -253,6 +261,27 @@ def dequant_grouped_gemm(w: QWeight, a, perm: Perm, T: int, k: int, variant: int
                                       variant, chunk, _ptr(buf), buf.numel(), _ptr(y), _stream()),
            "dequant_grouped_gemm")
     return y if y is not None else buf
+
+
+def lora_grouped_gemm(w: QWeight, A, B, alpha: float, a, perm: Perm, T: int, k: int,
+                      variant: int = FUSED, chunk: int = 0, flags: int = A_TOKENS,
+                      ws: Workspace | None = None):
+    """(y [P, N], u [P, rank]) BF16 in sorted order: the projection with a LoRA adapter,
+    A [E, rank, K] and B [E, N, rank] BF16 device tensors."""
+    import torch
+    dev = w.packed.device
+    P = T * k
+    rank = A.shape[1]
+    y = torch.empty((P, w.N), dtype=torch.bfloat16, device=dev)
+    u = torch.empty((P, rank), dtype=torch.bfloat16, device=dev)
+    nb, _ = workspace_bytes(CALL_GEMM, T, w.K, w.E, k, w.N, variant, chunk)
+    buf = (ws or _default_ws).get(nb, dev)
+    wc, pc = w.c(), perm.c()
+    lc = _Lora(rank, float(alpha), A.data_ptr(), B.data_ptr())
+    _check(lib().lora_grouped_gemm(ctypes.byref(wc), ctypes.byref(lc), _ptr(a), flags,
+                                   ctypes.byref(pc), T, k, variant, chunk, _ptr(buf), buf.numel(),
+                                   _ptr(u), _ptr(y), _stream()), "lora_grouped_gemm")
+    return y, u
 
 
 def moe_ffn_fwd(w_gate_up: QWeight, w_down: QWeight, x, logits, k: int, variant: int = FUSED,

@@ -333,6 +333,32 @@ __device__ __forceinline__ void gemm_nt_item(const GemmArgs& g,
   __builtin_amdgcn_s_waitcnt(vm_lgkm0_imm(0));
 
   if (!active) return;
+  if constexpr (EPI == kEpiStore) {
+    // LoRA up projection as extra K steps on the same accumulators: A rows
+    // from u (this lane's row of each block, clamped into the tile), B rows
+    // from the expert's adapter B (this wave's two output columns)
+    if (g.lora_rank > 0) {
+      const int rk = g.lora_rank;
+      const uint16_t* b0p = g.lora_b + ((int64_t)expert * g.N + wrow0) * rk + 8 * half;
+      const uint16_t* b1p = g.lora_b + ((int64_t)expert * g.N + wrow1) * rk + 8 * half;
+      const uint16_t* up[NMB];
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb) {
+        const int r = mb * 32 + col < nrows ? mb * 32 + col : nrows - 1;
+        up[mb] = g.lora_u + (int64_t)(row0 + r) * rk + 8 * half;
+      }
+      for (int j = 0; j < rk; j += 16) {
+        const bf16x8_t b0 = *reinterpret_cast<const bf16x8_t*>(b0p + j);
+        const bf16x8_t b1 = *reinterpret_cast<const bf16x8_t*>(b1p + j);
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb) {
+          const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(up[mb] + j);
+          acc[mb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b0, acc[mb][0], 0, 0, 0);
+          acc[mb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b1, acc[mb][1], 0, 0, 0);
+        }
+      }
+    }
+  }
   // epilogue: lane holds column `col` of rows 8i + 4*half + j of each block
 #pragma unroll
   for (int mb = 0; mb < NMB; ++mb) {

@@ -3,6 +3,7 @@
 // the caller's.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstring>
 #include <mutex>
 
@@ -234,10 +235,11 @@ qgg_status expert_permute(const int32_t* topk_ids, int T, int k, int E, const qg
   return QGG_OK;
 }
 
-qgg_status dequant_grouped_gemm(const qgg_qweight* w, const uint16_t* a, int flags,
-                                const qgg_perm* p, int T, int k, int variant, int chunk,
-                                void* workspace, size_t ws_bytes, uint16_t* y,
-                                qgg_stream_t stream) {
+// Shared body of dequant_grouped_gemm and lora_grouped_gemm (lora may be null).
+static qgg_status grouped_gemm(const qgg_qweight* w, const qgg_lora* lora, const uint16_t* a,
+                               int flags, const qgg_perm* p, int T, int k, int variant, int chunk,
+                               void* workspace, size_t ws_bytes, uint16_t* u_out, uint16_t* y,
+                               qgg_stream_t stream) {
   if (!w || !valid_perm(p) || !valid_fmt(w->fmt) || !valid_layout(w->layout))
     return QGG_ERR_INVALID_ARG;
   const int E = w->E, N = w->N, K = w->K;
@@ -280,6 +282,13 @@ qgg_status dequant_grouped_gemm(const qgg_qweight* w, const uint16_t* a, int fla
   g.y = y;
   g.ldy = trans ? K : N;
   g.epi = kEpiStore;
+  if (lora) {
+    QGG_HIP(launch_lora_u(a, K, p->perm, k, g.amode, pl.tiles, pl.chunk_first + E + 1,
+                          (int)pl.cap, pl.mb, lora->A, lora->rank, lora->alpha, u_out, stream));
+    g.lora_rank = lora->rank;
+    g.lora_u = u_out;
+    g.lora_b = lora->B;
+  }
   if (variant == QGG_FUSED) {
     QGG_HIP(trans ? launch_gemm_tn(g, pl.mb, stream) : launch_gemm_nt(g, pl.mb, stream));
     return QGG_OK;
@@ -296,6 +305,27 @@ qgg_status dequant_grouped_gemm(const qgg_qweight* w, const uint16_t* a, int fla
     QGG_HIP(trans ? launch_gemm_tn(g, pl.mb, stream) : launch_gemm_nt(g, pl.mb, stream));
   }
   return QGG_OK;
+}
+
+qgg_status dequant_grouped_gemm(const qgg_qweight* w, const uint16_t* a, int flags,
+                                const qgg_perm* p, int T, int k, int variant, int chunk,
+                                void* workspace, size_t ws_bytes, uint16_t* y,
+                                qgg_stream_t stream) {
+  return grouped_gemm(w, nullptr, a, flags, p, T, k, variant, chunk, workspace, ws_bytes, nullptr,
+                      y, stream);
+}
+
+qgg_status lora_grouped_gemm(const qgg_qweight* w, const qgg_lora* lora, const uint16_t* a,
+                             int flags, const qgg_perm* p, int T, int k, int variant, int chunk,
+                             void* workspace, size_t ws_bytes, uint16_t* u_out, uint16_t* y,
+                             qgg_stream_t stream) {
+  if (!lora || !w) return QGG_ERR_INVALID_ARG;
+  if (lora->rank < 16 || lora->rank > 128 || lora->rank % 16) return QGG_ERR_UNSUPPORTED;
+  if (!std::isfinite(lora->alpha)) return QGG_ERR_INVALID_ARG;
+  if (flags & (QGG_TRANSPOSE_W | QGG_DEQUANT_ONLY)) return QGG_ERR_INVALID_ARG;
+  if (T > 0 && (!lora->A || !lora->B || !u_out)) return QGG_ERR_INVALID_ARG;
+  return grouped_gemm(w, lora, a, flags, p, T, k, variant, chunk, workspace, ws_bytes, u_out, y,
+                      stream);
 }
 
 qgg_status moe_ffn_fwd(const qgg_qweight* w_gate_up, const qgg_qweight* w_down,

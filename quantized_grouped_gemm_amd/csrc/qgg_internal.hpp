@@ -49,6 +49,12 @@ struct GemmArgs {
   int inter;                     // SwiGLU width
   uint16_t* h;                   // fwd: optional h save [P][2I]; bwd: saved h
   const float* gates;            // bwd SwiGLU epilogue: topk gates [T*k]
+  // optional LoRA up projection folded into the forward (kEpiStore) GEMM:
+  // y += u . B_e^T with u [rows][lora_rank] (sorted order, BF16, already
+  // scaled by alpha) and B [E][N][lora_rank] BF16; lora_rank % 16 == 0
+  int lora_rank;
+  const uint16_t* lora_u;
+  const uint16_t* lora_b;
   float* gpart;                  // bwd SwiGLU epilogue, optional: per sorted row and
                                  // 256-column item, sum over the item of
                                  // (dY . W_down)[c] * silu(gate)[c] * up[c]; [P][inter/256]
@@ -62,6 +68,12 @@ hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* ids, 
 hipError_t launch_router_bwd(const float* gpart, int nitems, const int32_t* inv_perm,
                              const int32_t* ids, const float* gates, int T, int E, int k,
                              float* dgates, float* dlogits, hipStream_t s);
+// u[i][j] = alpha * sum_k a[row(i)][k] A_e[j][k] for the sorted rows of the
+// tiles [0, *ntiles) (row(i) = perm[i] / topk for kATokens); A [E][rank][K] BF16,
+// u [P][rank] BF16; K % 64 == 0, rank <= 128.
+hipError_t launch_lora_u(const uint16_t* x, int K, const int32_t* perm, int topk, int amode,
+                         const int4* tiles, const int32_t* ntiles, int max_tiles, int MB,
+                         const uint16_t* A, int rank, float alpha, uint16_t* u, hipStream_t s);
 size_t permute_ws_bytes(int64_t P, int E);
 hipError_t launch_permute(const int32_t* ids, int64_t P, int E, const PermPtrs& pp, int32_t* err,
                           void* ws, hipStream_t s);

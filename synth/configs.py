@@ -12,7 +12,8 @@ from dataclasses import dataclass, field
 import numpy as np
 
 # Philox stream ids, one per tensor role.
-STREAM = {"logits": 1, "x": 2, "w_gate_up": 3, "w_down": 4, "dy": 5, "zipf": 6}
+STREAM = {"logits": 1, "x": 2, "w_gate_up": 3, "w_down": 4, "dy": 5, "zipf": 6, "lora_a": 7,
+          "lora_b": 8}
 
 
 @dataclass(frozen=True)

@@ -11,6 +11,7 @@ import torch
 
 import oracle
 import quantized_grouped_gemm_amd as qgg
+import synth
 import synth.configs as sc
 
 from .gpu_util import (DEV, assert_close, bf16_to_f64, check_router_grads, dev_bf16,
@@ -67,6 +68,46 @@ def test_kimi_int4_gate_up_full():
     e = assert_close(bf16_to_f64(got), ref, what="kimi int4 gate_up")
     print(f"case kimi: {rows.size} rows checked, max rel err {e:.2e}", flush=True)
     del w, xd, y_f, y_c, packed, scales
+    _free()
+
+
+def test_kimi_int4_gate_up_lora_full():
+    """The bench workload with a rank-32 BF16 LoRA adapter on every expert."""
+    cfg = sc.CONFIGS["kimi_int4_gate_up"]
+    rank, alpha = 32, 0.5
+    print(f"case {cfg.name} + LoRA rank {rank}: generating inputs", flush=True)
+    logits, x = sc.router_logits(cfg), sc.activations(cfg)
+    packed, scales = sc.first_weights(cfg)
+    A = synth.normal_bf16(cfg.seed, sc.STREAM["lora_a"], (cfg.E, rank, cfg.d), std=0.02)
+    B = synth.normal_bf16(cfg.seed, sc.STREAM["lora_b"], (cfg.E, cfg.N, rank), std=0.02)
+    w = qgg.repack(dev_weights(cfg.fmt, packed, scales))
+    xd, Ad, Bd = dev_bf16(x), dev_bf16(A), dev_bf16(B)
+    ids, _ = qgg.moe_route(torch.from_numpy(logits).to(DEV), cfg.k)
+    p, _ = qgg.expert_permute(ids, cfg.E)
+    y_f, u_f = qgg.lora_grouped_gemm(w, Ad, Bd, alpha, xd, p, cfg.T, cfg.k, qgg.FUSED, 0)
+    y_c, u_c = qgg.lora_grouped_gemm(w, Ad, Bd, alpha, xd, p, cfg.T, cfg.k, qgg.CHUNKED,
+                                     cfg.chunks[0])
+    sync()
+    assert torch.equal(y_f.view(torch.int16), y_c.view(torch.int16))
+    assert torch.equal(u_f.view(torch.int16), u_c.view(torch.int16))
+    del y_c, u_c
+    print("case kimi lora: GPU done, checking", flush=True)
+    ids_ref, _, pref = _check_routing(cfg, logits, ids, p)
+    rng = np.random.default_rng(3)
+    rows = []
+    for e in pref["active"][:pref["n_active"]]:
+        seg = np.arange(pref["offsets"][e], pref["offsets"][e + 1])
+        rows.append(rng.choice(seg, min(2, seg.size), replace=False))
+    rows = np.sort(np.concatenate(rows))
+    pairs = pref["perm"][rows]
+    y_ref, u_ref = oracle.lora_project(cfg.fmt, packed, scales, x,
+                                       (pairs // cfg.k).astype(np.int32),
+                                       ids_ref.reshape(-1)[pairs], A, B, alpha, want_u=True)
+    sel = torch.from_numpy(rows).to(DEV)
+    assert_close(bf16_to_f64(host_u16(u_f[sel])), u_ref, what="kimi lora u")
+    e = assert_close(bf16_to_f64(host_u16(y_f[sel])), y_ref, what="kimi lora y")
+    print(f"case kimi lora: {rows.size} rows checked, max rel err {e:.2e}", flush=True)
+    del w, xd, Ad, Bd, y_f, u_f, packed, scales
     _free()
 
 

@@ -212,6 +212,48 @@ def test_grouped_gemm_parity_and_chunk_invariance(cfg):
         np.testing.assert_array_equal(v, base, err_msg=f"layout/variant/chunk {key} differs")
 
 
+LORA_CASES = [(PROJ_CASES[0], 16), (PROJ_CASES[1], 48), (PROJ_CASES[3], 32),
+              (PROJ_CASES[4], 128)]
+
+
+@pytest.mark.parametrize("cfg,rank", LORA_CASES, ids=lambda v: v.name if hasattr(v, "name") else str(v))
+def test_lora_grouped_gemm_parity(cfg, rank):
+    print(f"case {cfg.name} rank {rank}", flush=True)
+    logits, x, w = _inputs(cfg)
+    A = synth.normal_bf16(cfg.seed, STREAM["lora_a"], (cfg.E, rank, cfg.d), std=0.05)
+    B = synth.normal_bf16(cfg.seed, STREAM["lora_b"], (cfg.E, cfg.N, rank), std=0.05)
+    alpha = 0.5
+    ids_ref, _ = oracle.route(logits, cfg.k)
+    tok = np.arange(cfg.T * cfg.k, dtype=np.int32) // cfg.k
+    y_ref, u_ref = oracle.lora_project(cfg.fmt, w[0], w[1], x, tok, ids_ref.reshape(-1), A, B,
+                                       alpha, want_u=True)
+    ids, _ = qgg.moe_route(torch.from_numpy(logits).to(DEV), cfg.k)
+    p, _ = qgg.expert_permute(ids, cfg.E)
+    xd, Ad, Bd = dev_bf16(x), dev_bf16(A), dev_bf16(B)
+    inv = p.inv_perm.cpu().numpy()
+    outs = {}
+    for layout in LAYOUTS:
+        wd = dev_weights(cfg.fmt, *w, layout=layout)
+        for variant, chunk in [(qgg.FUSED, 0), (qgg.CHUNKED, cfg.chunks[0])]:
+            y, u = qgg.lora_grouped_gemm(wd, Ad, Bd, alpha, xd, p, cfg.T, cfg.k, variant, chunk)
+            sync()
+            what = f"{cfg.name} r{rank} layout{layout} v{variant} c{chunk}"
+            yh, uh = host_u16(y), host_u16(u)
+            assert_close(bf16_to_f64(uh[inv]), u_ref, what=what + " u")
+            assert_close(bf16_to_f64(yh[inv]), y_ref, what=what + " y")
+            outs[(layout, variant, chunk)] = (yh, uh)
+        if layout == qgg.LAYOUT_MFMA:
+            # alpha = 0: the adapter steps add exact zeros to the base product
+            y0, _ = qgg.lora_grouped_gemm(wd, Ad, Bd, 0.0, xd, p, cfg.T, cfg.k, qgg.FUSED, 0)
+            yb = qgg.dequant_grouped_gemm(wd, xd, p, cfg.T, cfg.k, qgg.FUSED, 0)
+            sync()
+            np.testing.assert_array_equal(host_u16(y0), host_u16(yb))
+    first = next(iter(outs.values()))
+    for key, (yh, uh) in outs.items():
+        np.testing.assert_array_equal(yh, first[0], err_msg=f"y {key} differs")
+        np.testing.assert_array_equal(uh, first[1], err_msg=f"u {key} differs")
+
+
 def test_grouped_gemm_one_hot_rows_return_weight_columns():
     # Rows of x that are one-hot pick single weight columns, so the output is
     # the dequantized weights themselves (exactly representable in BF16).
