@@ -58,6 +58,8 @@ def _L():
                                           P, P, P]
         lib.oracle_lora_project.argtypes = [i32, P, P, i32, i64, i64, P, i64, P, P, i32,
                                             ctypes.c_double, P, P, P, P]
+        lib.oracle_lora_bwd.argtypes = [i32, i64, i64, P, P, i64, P, P, i32, ctypes.c_double,
+                                        P, P, P, P, P]
         lib.oracle_silu.argtypes = [ctypes.c_double]
         lib.oracle_silu.restype = ctypes.c_double
         lib.oracle_silu_grad.argtypes = [ctypes.c_double]
@@ -203,6 +205,25 @@ def lora_project(fmt, packed, scales, x, tok, expert, A, B, alpha, want_u=False)
                                     _p(np.ascontiguousarray(B, np.uint16)), _p(y), _p(u)),
            "lora_project")
     return (y, u) if want_u else y
+
+
+def lora_bwd(x, dy, tok, expert, A, B, alpha):
+    """(dx [npairs][K], dA [E][r][K], dB [E][N][r]) in double: the adapter term's
+    gradients for L = <dY, y> (dy BF16 [npairs][N])."""
+    E, rank, K = A.shape
+    N = B.shape[1]
+    tok = np.ascontiguousarray(tok, np.int32)
+    expert = np.ascontiguousarray(expert, np.int32)
+    dx = np.zeros((tok.size, K), np.float64)
+    dA = np.zeros((E, rank, K), np.float64)
+    dB = np.zeros((E, N, rank), np.float64)
+    _check(_L().oracle_lora_bwd(E, N, K, _p(np.ascontiguousarray(x, np.uint16)),
+                                _p(np.ascontiguousarray(dy, np.uint16)), tok.size, _p(tok),
+                                _p(expert), rank, float(alpha),
+                                _p(np.ascontiguousarray(A, np.uint16)),
+                                _p(np.ascontiguousarray(B, np.uint16)), _p(dx), _p(dA), _p(dB)),
+           "lora_bwd")
+    return dx, dA, dB
 
 
 def router_bwd(fmt, gu, dn, x, dy, logits, ids, toks):

@@ -29,7 +29,8 @@
  *           silu'(gate) | dA * silu(gate)]; dXp = W_gu^T dH; dX[t] = sum over
  *           j ascending of dXp[t,j].  Gates are constants.
  *  lora     Orbit page, opening section: a BF16 adapter on the frozen base.
- *           LoRA form y = x W_e^T + alpha (x A_e^T) B_e^T, in double.
+ *           LoRA form y = x W_e^T + alpha (x A_e^T) B_e^T, in double; its
+ *           backward gives the adapter's weight gradients and its part of dx.
  *  router_bwd  The gradient the base hands back to a trainable router (the
  *           pages freeze the base, not the router): dg[t,j] = <dY[t], o[t,j]>,
  *           then reverse mode through the gate definition of route.  The
@@ -530,5 +531,61 @@ int oracle_lora_project(int fmt, const uint8_t* packed, const void* scales, int 
   }
   free(xr);
   free(u);
+  return 0;
+}
+
+/* Backward of oracle_lora_project's adapter term for L = <dY, y>, base frozen
+ * (chain rule through y = x W^T + alpha (x A^T) B^T; the pages give no
+ * formula for this step).  Per pair i (t = tok[i], e = expert[i]):
+ *   u_i = alpha x_t A_e^T,  du_i = dY_i B_e,  dx_i = alpha du_i A_e,
+ *   dA_e = alpha sum_i du_i (x) x_t,  dB_e = sum_i dY_i (x) u_i.
+ * dy BF16 [npairs][N]; outputs double: dx [npairs][K], dA [E][rank][K],
+ * dB [E][N][rank] (each nullable; dA, dB are overwritten, zero for experts no
+ * pair uses). */
+int oracle_lora_bwd(int E, int64_t N, int64_t K, const uint16_t* x, const uint16_t* dy,
+                    int64_t npairs, const int32_t* tok, const int32_t* expert, int rank,
+                    double alpha, const uint16_t* A, const uint16_t* B, double* dx, double* dA,
+                    double* dB) {
+  if (rank <= 0) return 1;
+  double* xr = (double*)malloc(sizeof(double) * (size_t)K);
+  double* u = (double*)malloc(sizeof(double) * (size_t)rank);
+  double* du = (double*)malloc(sizeof(double) * (size_t)rank);
+  if (!xr || !u || !du) {
+    free(xr);
+    free(u);
+    free(du);
+    return 3;
+  }
+  if (dA) memset(dA, 0, sizeof(double) * (size_t)(E * rank * K));
+  if (dB) memset(dB, 0, sizeof(double) * (size_t)(E * N * rank));
+  for (int64_t i = 0; i < npairs; ++i) {
+    const int64_t e = expert[i];
+    oracle_bf16_to_f64(x + (int64_t)tok[i] * K, K, xr);
+    for (int j = 0; j < rank; ++j) {
+      double su = 0.0, sd = 0.0;
+      for (int64_t k = 0; k < K; ++k) su += xr[k] * (double)bf16_to_float(A[(e * rank + j) * K + k]);
+      for (int64_t n = 0; n < N; ++n)
+        sd += (double)bf16_to_float(dy[i * N + n]) * (double)bf16_to_float(B[(e * N + n) * rank + j]);
+      u[j] = alpha * su;
+      du[j] = sd;
+    }
+    if (dx)
+      for (int64_t k = 0; k < K; ++k) {
+        double acc = 0.0;
+        for (int j = 0; j < rank; ++j) acc += du[j] * (double)bf16_to_float(A[(e * rank + j) * K + k]);
+        dx[i * K + k] = alpha * acc;
+      }
+    if (dA)
+      for (int j = 0; j < rank; ++j)
+        for (int64_t k = 0; k < K; ++k) dA[(e * rank + j) * K + k] += alpha * du[j] * xr[k];
+    if (dB)
+      for (int64_t n = 0; n < N; ++n) {
+        const double g = (double)bf16_to_float(dy[i * N + n]);
+        for (int j = 0; j < rank; ++j) dB[(e * N + n) * rank + j] += g * u[j];
+      }
+  }
+  free(xr);
+  free(u);
+  free(du);
   return 0;
 }

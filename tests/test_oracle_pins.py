@@ -487,6 +487,40 @@ def test_lora_project_special_cases():
     assert np.all(d == 0)
 
 
+def _lora_term_loss(xp, dyf, expert, Af, Bf, alpha):
+    """<dY, alpha (x A^T) B^T> summed over pairs, in float64 (xp: per-pair rows)."""
+    return sum(dyf[i] @ (alpha * (Bf[e] @ (Af[e] @ xp[i]))) for i, e in enumerate(expert))
+
+
+def test_lora_bwd_matches_finite_differences():
+    packed, scales, x, A, B, tok, expert = _lora_inputs(1, P=9, E=12, rank=16)
+    N = B.shape[1]
+    dy = synth.normal_bf16(7, 5, (tok.size, N))
+    alpha = 0.75
+    dx, dA, dB = oracle.lora_bwd(x, dy, tok, expert, A, B, alpha)
+    xp = _bf16_bits_to_f64(x)[tok]
+    dyf, Af, Bf = _bf16_bits_to_f64(dy), _bf16_bits_to_f64(A), _bf16_bits_to_f64(B)
+    rng = np.random.default_rng(11)
+    eps = 1e-3
+    for name, grad in (("x", dx), ("A", dA), ("B", dB)):
+        for _ in range(3):
+            V = rng.standard_normal(grad.shape)
+            args = {"x": xp, "A": Af, "B": Bf}
+            lp = dict(args)
+            lm = dict(args)
+            lp[name] = args[name] + eps * V
+            lm[name] = args[name] - eps * V
+            fd = (_lora_term_loss(lp["x"], dyf, expert, lp["A"], lp["B"], alpha)
+                  - _lora_term_loss(lm["x"], dyf, expert, lm["A"], lm["B"], alpha)) / (2 * eps)
+            an = float(np.sum(grad * V))
+            assert abs(fd - an) <= 1e-9 * max(1.0, abs(an)), (name, fd, an)
+    # experts no pair uses get zero adapter gradients
+    unused = sorted(set(range(A.shape[0])) - set(expert.tolist()))
+    assert unused
+    for e in unused:
+        assert np.all(dA[e] == 0) and np.all(dB[e] == 0)
+
+
 # ------------------------------------------------------------ router backward
 
 def _twin_pair_outputs(fmt, gu, dn, xf, ids, t):
