@@ -82,6 +82,7 @@ typedef int qgg_status;
 #define QGG_CALL_GEMM 2
 #define QGG_CALL_FFN_FWD 3
 #define QGG_CALL_DX_BWD 4
+#define QGG_CALL_LORA_BWD 5   /* N_or_inter = adapter rank */
 
 /* Storage layouts of the packed weights and scales (the bytes are the same,
  * only their order differs):
@@ -183,6 +184,26 @@ qgg_status lora_grouped_gemm(const qgg_qweight* w, const qgg_lora* lora, const u
                              int flags, const qgg_perm* p, int T, int k, int variant, int chunk,
                              void* workspace, size_t ws_bytes, uint16_t* u_out, uint16_t* y,
                              qgg_stream_t stream);
+
+/* lora_grouped_gemm_bwd -- the adapter's backward for L = <dY, y> of
+ * lora_grouped_gemm, the base frozen (Orbit page, 时刻细节: no gradient is
+ * formed for the frozen base; the adapter is what trains).  With du_i =
+ * dY_i . B_e (fp32, workspace):
+ *   dx[i][:]  = alpha du_i . A_e         BF16 [P][K], sorted order: the
+ *               adapter's part of the input gradient (the base part is
+ *               dequant_grouped_gemm with QGG_TRANSPOSE_W on the same dY);
+ *   dA[e]     = alpha sum_i du_i (x) a_row(i)    fp32 [E][rank][K];
+ *   dB[e]     = sum_i dY_i (x) u_i               fp32 [E][N][rank];
+ * sums over the rows i of expert e in sorted order; experts with no rows get
+ * zeros.  dy [P][N] BF16 sorted; u [P][rank] BF16 as lora_grouped_gemm wrote
+ * it; a and flags (QGG_A_TOKENS or 0) as in the forward.  Any of dx, dA, dB
+ * may be NULL (not all).  workspace: qgg_workspace_bytes(QGG_CALL_LORA_BWD,
+ * T, K, E, k, rank, ...).  Deterministic. */
+qgg_status lora_grouped_gemm_bwd(const qgg_lora* lora, int E, int N, int K, const uint16_t* a,
+                                 int flags, const uint16_t* dy, const uint16_t* u,
+                                 const qgg_perm* p, int T, int k, void* workspace,
+                                 size_t ws_bytes, uint16_t* dx, float* dA, float* dB,
+                                 qgg_stream_t stream);
 
 /* moe_ffn_fwd -- the SwiGLU expert FFN for a routed batch: route, permute,
  * h = x . W_gu^T (rows [0,inter) of W_gu are gate, [inter, 2*inter) up),

@@ -34,13 +34,14 @@ CALL_PERMUTE = 1
 CALL_GEMM = 2
 CALL_FFN_FWD = 3
 CALL_DX_BWD = 4
+CALL_LORA_BWD = 5
 
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too small", 4: "HIP error"}
 
 # Every symbol include/qgg.h declares.
 EXPORTS = ("moe_route", "expert_permute", "dequant_grouped_gemm", "lora_grouped_gemm",
-           "moe_ffn_fwd", "moe_dx_bwd", "moe_router_bwd", "qgg_repack_weights",
-           "qgg_workspace_bytes", "qgg_status_string", "qgg_version")
+           "lora_grouped_gemm_bwd", "moe_ffn_fwd", "moe_dx_bwd", "moe_router_bwd",
+           "qgg_repack_weights", "qgg_workspace_bytes", "qgg_status_string", "qgg_version")
 
 _lib = None
 
@@ -80,6 +81,8 @@ def lib():
                                            i32, i32, i32, i32, P, sz, P, P]
         L.lora_grouped_gemm.argtypes = [ctypes.POINTER(_QWeight), ctypes.POINTER(_Lora), P, i32,
                                         ctypes.POINTER(_Perm), i32, i32, i32, i32, P, sz, P, P, P]
+        L.lora_grouped_gemm_bwd.argtypes = [ctypes.POINTER(_Lora), i32, i32, i32, P, i32, P, P,
+                                            ctypes.POINTER(_Perm), i32, i32, P, sz, P, P, P, P]
         L.moe_ffn_fwd.argtypes = [ctypes.POINTER(_QWeight), ctypes.POINTER(_QWeight), P, P, i32,
                                   i32, i32, i32, i32, i32, i32, P, P, ctypes.POINTER(_Perm), P, P,
                                   P, sz, P, P]
@@ -98,7 +101,7 @@ def lib():
         L.qgg_status_string.restype = ctypes.c_char_p
         L.qgg_version.restype = ctypes.c_char_p
         for f in ("moe_route", "expert_permute", "dequant_grouped_gemm", "lora_grouped_gemm",
-                  "moe_ffn_fwd", "moe_dx_bwd", "moe_router_bwd"):
+                  "lora_grouped_gemm_bwd", "moe_ffn_fwd", "moe_dx_bwd", "moe_router_bwd"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -282,6 +285,30 @@ def lora_grouped_gemm(w: QWeight, A, B, alpha: float, a, perm: Perm, T: int, k: 
                                    ctypes.byref(pc), T, k, variant, chunk, _ptr(buf), buf.numel(),
                                    _ptr(u), _ptr(y), _stream()), "lora_grouped_gemm")
     return y, u
+
+
+def lora_grouped_gemm_bwd(A, B, alpha: float, a, dy, u, perm: Perm, T: int, k: int,
+                          flags: int = A_TOKENS, want=("dx", "dA", "dB"),
+                          ws: Workspace | None = None):
+    """{"dx": [P, K] BF16, "dA": [E, rank, K] fp32, "dB": [E, N, rank] fp32} (those in
+    `want`): the adapter's backward for the upstream gradient dy [P, N] (sorted)."""
+    import torch
+    E, rank, K = A.shape
+    N = B.shape[1]
+    dev = dy.device
+    P = T * k
+    dx = torch.empty((P, K), dtype=torch.bfloat16, device=dev) if "dx" in want else None
+    dA = torch.empty((E, rank, K), dtype=torch.float32, device=dev) if "dA" in want else None
+    dB = torch.empty((E, N, rank), dtype=torch.float32, device=dev) if "dB" in want else None
+    nb, _ = workspace_bytes(CALL_LORA_BWD, T, K, E, k, rank, FUSED, 0)
+    buf = (ws or _default_ws).get(nb, dev)
+    pc = perm.c()
+    lc = _Lora(rank, float(alpha), A.data_ptr(), B.data_ptr())
+    _check(lib().lora_grouped_gemm_bwd(ctypes.byref(lc), E, N, K, _ptr(a), flags, _ptr(dy),
+                                       _ptr(u), ctypes.byref(pc), T, k, _ptr(buf), buf.numel(),
+                                       _ptr(dx), _ptr(dA), _ptr(dB), _stream()),
+           "lora_grouped_gemm_bwd")
+    return {"dx": dx, "dA": dA, "dB": dB}
 
 
 def moe_ffn_fwd(w_gate_up: QWeight, w_down: QWeight, x, logits, k: int, variant: int = FUSED,

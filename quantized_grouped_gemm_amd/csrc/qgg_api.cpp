@@ -166,6 +166,7 @@ qgg_status qgg_repack_weights(const qgg_qweight* src, uint8_t* packed_out, void*
 //  GEMM     plan (tiles, chunk table) | BF16 chunk scratch (CHUNKED)
 //  FFN_FWD  segment counts | plan | a [P][inter] | o [P][d] | scratch
 //  DX_BWD   plan | dH [P][2*inter] | dXp [P][d] | scratch | gate partials [P][inter/256] fp32
+//  LORA_BWD plan | du [P][rank] fp32
 size_t qgg_workspace_bytes(int call, int T, int d, int E, int k, int N_or_inter, int variant,
                            int chunk, size_t* scratch_bytes) {
   if (scratch_bytes) *scratch_bytes = 0;
@@ -194,6 +195,10 @@ size_t qgg_workspace_bytes(int call, int T, int d, int E, int k, int N_or_inter,
       cv.take<char>(scratch);
       break;
     }
+    case QGG_CALL_LORA_BWD:   // N_or_inter = adapter rank
+      carve_plan(cv, P, E, pl);
+      cv.take<char>((size_t)P * N_or_inter * 4);
+      break;
     case QGG_CALL_DX_BWD: {
       const int64_t I = N_or_inter;
       carve_plan(cv, P, E, pl);
@@ -326,6 +331,40 @@ qgg_status lora_grouped_gemm(const qgg_qweight* w, const qgg_lora* lora, const u
   if (T > 0 && (!lora->A || !lora->B || !u_out)) return QGG_ERR_INVALID_ARG;
   return grouped_gemm(w, lora, a, flags, p, T, k, variant, chunk, workspace, ws_bytes, u_out, y,
                       stream);
+}
+
+qgg_status lora_grouped_gemm_bwd(const qgg_lora* lora, int E, int N, int K, const uint16_t* a,
+                                 int flags, const uint16_t* dy, const uint16_t* u,
+                                 const qgg_perm* p, int T, int k, void* workspace,
+                                 size_t ws_bytes, uint16_t* dx, float* dA, float* dB,
+                                 qgg_stream_t stream) {
+  if (!lora || !valid_perm(p) || !valid_route_dims(T, E, k) || N <= 0 || K <= 0)
+    return QGG_ERR_INVALID_ARG;
+  if (lora->rank < 16 || lora->rank > 128 || lora->rank % 16) return QGG_ERR_UNSUPPORTED;
+  if (!std::isfinite(lora->alpha)) return QGG_ERR_INVALID_ARG;
+  if (flags & ~QGG_A_TOKENS) return QGG_ERR_INVALID_ARG;
+  if (K % 128 || N % 64) return QGG_ERR_UNSUPPORTED;
+  if (!dx && !dA && !dB) return QGG_ERR_INVALID_ARG;
+  if (!lora->A || !lora->B) return QGG_ERR_INVALID_ARG;
+  if (T > 0 && (!dy || (dB && !u) || (dA && !a))) return QGG_ERR_INVALID_ARG;
+  const int64_t P = (int64_t)T * k;
+  const size_t need =
+      qgg_workspace_bytes(QGG_CALL_LORA_BWD, T, K, E, k, lora->rank, QGG_FUSED, 0, nullptr);
+  if (!workspace || ws_bytes < need) return QGG_ERR_WORKSPACE_TOO_SMALL;
+  Carver cv(workspace);
+  Plan pl;
+  carve_plan(cv, P, E, pl);
+  float* du = cv.take<float>((size_t)P * lora->rank * 4);
+  const PermPtrs pp = to_ptrs(p);
+  if (P > 0)
+    QGG_HIP(launch_tile_plan(pp, E, 32 * pl.mb, 0, pl.tiles, pl.chunk_first, stream));
+  // with no routed rows every adapter gradient is zero: the kernels still
+  // run (empty row ranges) so dA and dB are written in full
+  QGG_HIP(launch_lora_bwd(a, K, N, E, p->perm, k, (flags & QGG_A_TOKENS) ? kATokens : kASorted,
+                          p->offsets, pl.tiles, pl.chunk_first + E + 1, P > 0 ? (int)pl.cap : 0,
+                          pl.mb, lora->A, lora->B, lora->rank, lora->alpha, dy, u, du, dx, dA, dB,
+                          stream));
+  return QGG_OK;
 }
 
 qgg_status moe_ffn_fwd(const qgg_qweight* w_gate_up, const qgg_qweight* w_down,

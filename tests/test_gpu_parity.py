@@ -213,7 +213,10 @@ def test_grouped_gemm_parity_and_chunk_invariance(cfg):
 
 
 LORA_CASES = [(PROJ_CASES[0], 16), (PROJ_CASES[1], 48), (PROJ_CASES[3], 32),
-              (PROJ_CASES[4], 128)]
+              (PROJ_CASES[4], 128),
+              # most experts get no rows: their adapter gradients must be zero
+              (scaled(CONFIGS["kimi_int4_gate_up"], T=8, d=256, E=40, k=2, N=256, chunks=(4,),
+                      name="int4_sparse"), 32)]
 
 
 @pytest.mark.parametrize("cfg,rank", LORA_CASES, ids=lambda v: v.name if hasattr(v, "name") else str(v))
@@ -252,6 +255,40 @@ def test_lora_grouped_gemm_parity(cfg, rank):
     for key, (yh, uh) in outs.items():
         np.testing.assert_array_equal(yh, first[0], err_msg=f"y {key} differs")
         np.testing.assert_array_equal(uh, first[1], err_msg=f"u {key} differs")
+
+
+@pytest.mark.parametrize("cfg,rank", LORA_CASES, ids=lambda v: v.name if hasattr(v, "name") else str(v))
+def test_lora_grouped_gemm_bwd_parity(cfg, rank):
+    print(f"case {cfg.name} rank {rank} backward", flush=True)
+    logits, x, w = _inputs(cfg)
+    A = synth.normal_bf16(cfg.seed, STREAM["lora_a"], (cfg.E, rank, cfg.d), std=0.05)
+    B = synth.normal_bf16(cfg.seed, STREAM["lora_b"], (cfg.E, cfg.N, rank), std=0.05)
+    P = cfg.T * cfg.k
+    dy_pairs = synth.normal_bf16(cfg.seed, STREAM["dy"], (P, cfg.N))
+    alpha = 0.5
+    ids_ref, _ = oracle.route(logits, cfg.k)
+    tok = np.arange(P, dtype=np.int32) // cfg.k
+    dx_ref, dA_ref, dB_ref = oracle.lora_bwd(x, dy_pairs, tok, ids_ref.reshape(-1), A, B, alpha)
+    ids, _ = qgg.moe_route(torch.from_numpy(logits).to(DEV), cfg.k)
+    p, _ = qgg.expert_permute(ids, cfg.E)
+    perm, inv = p.perm.cpu().numpy(), p.inv_perm.cpu().numpy()
+    xd, Ad, Bd = dev_bf16(x), dev_bf16(A), dev_bf16(B)
+    wd = dev_weights(cfg.fmt, *w, layout=qgg.LAYOUT_MFMA)
+    _, u = qgg.lora_grouped_gemm(wd, Ad, Bd, alpha, xd, p, cfg.T, cfg.k, qgg.FUSED, 0)
+    dyd = dev_bf16(dy_pairs[perm])                      # sorted order
+    g1 = qgg.lora_grouped_gemm_bwd(Ad, Bd, alpha, xd, dyd, u, p, cfg.T, cfg.k)
+    g2 = qgg.lora_grouped_gemm_bwd(Ad, Bd, alpha, xd, dyd, u, p, cfg.T, cfg.k, want=("dB",))
+    sync()
+    what = f"{cfg.name} r{rank}"
+    dx = bf16_to_f64(host_u16(g1["dx"]))[inv]
+    dA, dB = g1["dA"].cpu().numpy(), g1["dB"].cpu().numpy()
+    assert_close(dx, dx_ref, what=what + " dx")
+    assert_close(dA.reshape(-1, cfg.d), dA_ref.reshape(-1, cfg.d), what=what + " dA")
+    assert_close(dB.reshape(-1, rank), dB_ref.reshape(-1, rank), what=what + " dB")
+    used = np.zeros(cfg.E, bool)
+    used[ids_ref.reshape(-1)] = True
+    assert np.all(dA[~used] == 0) and np.all(dB[~used] == 0)
+    np.testing.assert_array_equal(g2["dB"].cpu().numpy(), dB)
 
 
 def test_grouped_gemm_one_hot_rows_return_weight_columns():
