@@ -82,7 +82,7 @@ typedef int qgg_status;
 #define QGG_CALL_GEMM 2
 #define QGG_CALL_FFN_FWD 3
 #define QGG_CALL_DX_BWD 4
-#define QGG_CALL_LORA_BWD 5   /* N_or_inter = adapter rank */
+#define QGG_CALL_LORA_BWD 5   /* d = N, N_or_inter = adapter rank */
 
 /* Storage layouts of the packed weights and scales (the bytes are the same,
  * only their order differs):
@@ -198,7 +198,8 @@ qgg_status lora_grouped_gemm(const qgg_qweight* w, const qgg_lora* lora, const u
  * zeros.  dy [P][N] BF16 sorted; u [P][rank] BF16 as lora_grouped_gemm wrote
  * it; a and flags (QGG_A_TOKENS or 0) as in the forward.  Any of dx, dA, dB
  * may be NULL (not all).  workspace: qgg_workspace_bytes(QGG_CALL_LORA_BWD,
- * T, K, E, k, rank, ...).  Deterministic. */
+ * T, N, E, k, rank, ...) (it holds du and a transposed copy of B).
+ * Deterministic. */
 qgg_status lora_grouped_gemm_bwd(const qgg_lora* lora, int E, int N, int K, const uint16_t* a,
                                  int flags, const uint16_t* dy, const uint16_t* u,
                                  const qgg_perm* p, int T, int k, void* workspace,

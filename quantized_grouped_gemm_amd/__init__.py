@@ -300,7 +300,7 @@ def lora_grouped_gemm_bwd(A, B, alpha: float, a, dy, u, perm: Perm, T: int, k: i
     dx = torch.empty((P, K), dtype=torch.bfloat16, device=dev) if "dx" in want else None
     dA = torch.empty((E, rank, K), dtype=torch.float32, device=dev) if "dA" in want else None
     dB = torch.empty((E, N, rank), dtype=torch.float32, device=dev) if "dB" in want else None
-    nb, _ = workspace_bytes(CALL_LORA_BWD, T, K, E, k, rank, FUSED, 0)
+    nb, _ = workspace_bytes(CALL_LORA_BWD, T, N, E, k, rank, FUSED, 0)
     buf = (ws or _default_ws).get(nb, dev)
     pc = perm.c()
     lc = _Lora(rank, float(alpha), A.data_ptr(), B.data_ptr())

@@ -15,17 +15,19 @@
 #include "qgg_device.hpp"
 #include "qgg_internal.hpp"
 
+#include <type_traits>
+
 namespace qgg {
 
 namespace {
 
-template <int NCB>
+template <int NCB, typename OUT>
 __global__ __launch_bounds__(64) void k_lora_u(const uint16_t* __restrict__ x, int K,
                                                const int32_t* __restrict__ perm, int topk,
                                                int amode, const int4* __restrict__ tiles,
                                                const int32_t* __restrict__ ntiles, int MB,
                                                const uint16_t* __restrict__ A, int rank,
-                                               float alpha, uint16_t* __restrict__ u) {
+                                               float alpha, OUT* __restrict__ u) {
   const int t = blockIdx.x / MB;
   const int mb = blockIdx.x % MB;
   if (t >= *ntiles) return;
@@ -74,8 +76,13 @@ __global__ __launch_bounds__(64) void k_lora_u(const uint16_t* __restrict__ x, i
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const int rr = mb * 32 + 8 * i + 4 * half + jj;
-        if (rr < nrows) u[(int64_t)(row0 + rr) * rank + j] =
-              __builtin_bit_cast(uint16_t, (__bf16)(alpha * acc[cb][4 * i + jj]));
+        if (rr < nrows) {
+          const float v = alpha * acc[cb][4 * i + jj];
+          if constexpr (std::is_same<OUT, float>::value)
+            u[(int64_t)(row0 + rr) * rank + j] = v;
+          else
+            u[(int64_t)(row0 + rr) * rank + j] = __builtin_bit_cast(uint16_t, (__bf16)v);
+        }
       }
   }
 }
@@ -83,64 +90,37 @@ __global__ __launch_bounds__(64) void k_lora_u(const uint16_t* __restrict__ x, i
 // ---------------------------------------------------------------- backward
 // Gradients of L = <dY, y> through the adapter term alpha (x A^T) B^T, the
 // base frozen: du = dY B_e, dx = alpha du A_e, dA_e = alpha sum_i du_i (x) x_i,
-// dB_e = sum_i dY_i (x) u_i.  Plain fp32 FMA kernels with LDS staging (the
-// adapter is a rank-r update: these are 2 P r (N + 2K) + 2 P N r flops next to
-// the base's 2 P N K); every sum runs in a fixed order, so results are
+// dB_e = sum_i dY_i (x) u_i.  du is the same row-times-matrix product as u
+// (k_lora_u on MFMA, with B_e transposed once to [rank][N]); the other three
+// are fp32 FMA kernels whose broadcast operand sits in LDS as float4 rows, two
+// output columns per thread.  Every sum runs in a fixed order, so results are
 // deterministic.
 
-// du [P][rank] fp32 for one 32-row block of a tile; thread (row = t / 8,
-// column group t % 8) owns columns g, g + 8, ...
-template <int RQ>
-__global__ __launch_bounds__(256) void k_lora_du(const uint16_t* __restrict__ dy, int N,
-                                                 const int4* __restrict__ tiles,
-                                                 const int32_t* __restrict__ ntiles, int MB,
-                                                 const uint16_t* __restrict__ B, int rank,
-                                                 float* __restrict__ du) {
-  __shared__ __attribute__((aligned(16))) uint16_t dys[32][64 + 8];
-  __shared__ __attribute__((aligned(16))) uint16_t bs[64][128 + 8];
-  const int t = blockIdx.x / MB, mb = blockIdx.x % MB;
-  if (t >= *ntiles) return;
-  const int4 tile = tiles[t];
-  const int expert = tile.x, row0 = tile.y, nrows = tile.z;
-  if (mb * 32 >= nrows) return;
-  const int tid = threadIdx.x;
-  const int row = tid >> 3, cg = tid & 7;
-  const int lrow = min(mb * 32 + row, nrows - 1);
-  const int rp = rank / 8;                    // 16-byte pieces per B row
-  float acc[RQ];
-#pragma unroll
-  for (int q = 0; q < RQ; ++q) acc[q] = 0.f;
-  for (int n0 = 0; n0 < N; n0 += 64) {
-    *reinterpret_cast<u32x4_t*>(&dys[row][8 * cg]) =
-        *reinterpret_cast<const u32x4_t*>(dy + (int64_t)(row0 + lrow) * N + n0 + 8 * cg);
-    for (int pc = tid; pc < 64 * rp; pc += 256) {
-      const int n = pc / rp, jp = pc % rp;
-      *reinterpret_cast<u32x4_t*>(&bs[n][8 * jp]) = *reinterpret_cast<const u32x4_t*>(
-          B + ((int64_t)expert * N + n0 + n) * rank + 8 * jp);
-    }
-    __syncthreads();
-    for (int n = 0; n < 64; ++n) {
-      const float d = bf16_to_f32(dys[row][n]);
-#pragma unroll
-      for (int q = 0; q < RQ; ++q)
-        if (cg + 8 * q < rank) acc[q] = fmaf(d, bf16_to_f32(bs[n][cg + 8 * q]), acc[q]);
-    }
-    __syncthreads();
+// Bt[e][j][n] = B[e][n][j]: a 64-row slab of one expert through LDS
+__global__ __launch_bounds__(256) void k_lora_bt(const uint16_t* __restrict__ B, int N, int rank,
+                                                 uint16_t* __restrict__ Bt) {
+  __shared__ uint16_t t[64][128 + 2];
+  const int e = blockIdx.x, n0 = blockIdx.y * 64;
+  for (int q = threadIdx.x; q < 64 * rank; q += 256) {
+    const int n = q / rank, j = q % rank;
+    t[n][j] = B[((int64_t)e * N + n0 + n) * rank + j];
   }
-  if (mb * 32 + row < nrows) {
-#pragma unroll
-    for (int q = 0; q < RQ; ++q)
-      if (cg + 8 * q < rank) du[(int64_t)(row0 + mb * 32 + row) * rank + cg + 8 * q] = acc[q];
+  __syncthreads();
+  for (int q = threadIdx.x; q < 64 * rank; q += 256) {
+    const int j = q / 64, n = q % 64;
+    Bt[((int64_t)e * rank + j) * N + n0 + n] = t[n][j];
   }
 }
 
-// dx [P][K] BF16 = alpha du A_e for one 32-row block and 256 columns
+// dx [P][K] BF16 = alpha du A_e for one 32-row block and 512 columns (two
+// per thread); du rows staged transposed, dut[j][r], so a float4 read gives
+// four rows' du_j
 __global__ __launch_bounds__(256) void k_lora_dx(const float* __restrict__ du,
                                                  const int4* __restrict__ tiles,
                                                  const int32_t* __restrict__ ntiles, int MB,
                                                  const uint16_t* __restrict__ A, int rank, int K,
                                                  float alpha, uint16_t* __restrict__ dx) {
-  __shared__ float dus[32][128];
+  __shared__ __attribute__((aligned(16))) float dut[128][32];
   const int t = blockIdx.x / MB, mb = blockIdx.x % MB;
   if (t >= *ntiles) return;
   const int4 tile = tiles[t];
@@ -150,149 +130,172 @@ __global__ __launch_bounds__(256) void k_lora_dx(const float* __restrict__ du,
   const int nr = min(32, nrows - mb * 32);
   for (int q = tid; q < 32 * rank; q += 256) {
     const int r = q / rank, j = q % rank;
-    dus[r][j] = r < nr ? du[(int64_t)(row0 + mb * 32 + r) * rank + j] : 0.f;
+    dut[j][r] = r < nr ? du[(int64_t)(row0 + mb * 32 + r) * rank + j] : 0.f;
   }
   __syncthreads();
-  const int k = blockIdx.y * 256 + tid;
-  if (k >= K) return;
-  float acc[32];
+  const int k0 = blockIdx.y * 512 + tid, k1 = k0 + 256;
+  float a0[32], a1[32];
 #pragma unroll
-  for (int r = 0; r < 32; ++r) acc[r] = 0.f;
-  const uint16_t* a = A + (int64_t)expert * rank * K + k;
-  for (int j = 0; j < rank; ++j) {
-    const float w = bf16_to_f32(a[(int64_t)j * K]);
+  for (int r = 0; r < 32; ++r) a0[r] = a1[r] = 0.f;
+  const uint16_t* a = A + (int64_t)expert * rank * K;
+  const int kc0 = k0 < K ? k0 : K - 1, kc1 = k1 < K ? k1 : K - 1;
+  for (int j0 = 0; j0 < rank; j0 += 16) {
+    // the 16 rows' loads first, so they are in flight together
+    float w0[16], w1[16];
 #pragma unroll
-    for (int r = 0; r < 32; ++r) acc[r] = fmaf(dus[r][j], w, acc[r]);
+    for (int jj = 0; jj < 16; ++jj) {
+      w0[jj] = bf16_to_f32(a[(int64_t)(j0 + jj) * K + kc0]);
+      w1[jj] = bf16_to_f32(a[(int64_t)(j0 + jj) * K + kc1]);
+    }
+#pragma unroll
+    for (int jj = 0; jj < 16; ++jj) {
+#pragma unroll
+      for (int r4 = 0; r4 < 8; ++r4) {
+        const f32x4_t d = *reinterpret_cast<const f32x4_t*>(&dut[j0 + jj][4 * r4]);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          a0[4 * r4 + c] = fmaf(d[c], w0[jj], a0[4 * r4 + c]);
+          a1[4 * r4 + c] = fmaf(d[c], w1[jj], a1[4 * r4 + c]);
+        }
+      }
+    }
   }
 #pragma unroll
-  for (int r = 0; r < 32; ++r)
-    if (r < nr)
-      dx[(int64_t)(row0 + mb * 32 + r) * K + k] = __builtin_bit_cast(uint16_t, (__bf16)(alpha * acc[r]));
+  for (int r = 0; r < 32; ++r) {
+    uint16_t* o = dx + (int64_t)(row0 + mb * 32 + r) * K;
+    if (r < nr && k0 < K) o[k0] = __builtin_bit_cast(uint16_t, (__bf16)(alpha * a0[r]));
+    if (r < nr && k1 < K) o[k1] = __builtin_bit_cast(uint16_t, (__bf16)(alpha * a1[r]));
+  }
 }
 
-// dA [E][rank][K] fp32 = alpha sum over the expert's rows of du_i (x) x_i;
-// thread owns column k, rows staged 32 at a time
-template <int R>
-__global__ __launch_bounds__(256) void k_lora_dA(const float* __restrict__ du,
-                                                 const uint16_t* __restrict__ x, int K,
-                                                 const int32_t* __restrict__ offsets,
-                                                 const int32_t* __restrict__ perm, int topk,
-                                                 int amode, int rank, float alpha,
-                                                 float* __restrict__ dA) {
-  __shared__ float dus[32][128];
+// Weight gradient of one expert, G[j][c] = scale sum_i L[i][j] R[i][c] over
+// the expert's rows i (ascending): L rows [rank] fp32 or BF16 staged in LDS,
+// R rows read per thread at NC columns c, c + 256, ... (out [rank][C] when
+// !TRANS_OUT, [C][rank] when TRANS_OUT).
+template <int R, int NC, typename LT, bool TRANS_OUT>
+__global__ __launch_bounds__(256) void k_lora_wgrad(const LT* __restrict__ L, int rank,
+                                                    const uint16_t* __restrict__ Rm, int C,
+                                                    const int32_t* __restrict__ offsets,
+                                                    const int32_t* __restrict__ perm, int topk,
+                                                    int amode, float scale,
+                                                    float* __restrict__ G) {
+  __shared__ __attribute__((aligned(16))) float ls[32][R];
   __shared__ int64_t src[32];
   const int e = blockIdx.x;
   const int tid = threadIdx.x;
-  const int k = blockIdx.y * 256 + tid;
+  const int cb = blockIdx.y * 256 * NC + tid;
   const int i0 = offsets[e], i1 = offsets[e + 1];
-  float acc[R];
+  float g[NC][R];
 #pragma unroll
-  for (int j = 0; j < R; ++j) acc[j] = 0.f;
+  for (int c = 0; c < NC; ++c)
+#pragma unroll
+    for (int j = 0; j < R; ++j) g[c][j] = 0.f;
   for (int b = i0; b < i1; b += 32) {
     const int nr = min(32, i1 - b);
     __syncthreads();
-    for (int q = tid; q < 32 * rank; q += 256) {
-      const int r = q / rank, j = q % rank;
-      dus[r][j] = r < nr ? du[(int64_t)(b + r) * rank + j] : 0.f;
+    for (int q = tid; q < 32 * R; q += 256) {
+      const int r = q / R, j = q % R;
+      float v = 0.f;
+      if (r < nr && j < rank) {
+        if constexpr (std::is_same<LT, float>::value) v = L[(int64_t)(b + r) * rank + j];
+        else v = bf16_to_f32(L[(int64_t)(b + r) * rank + j]);
+      }
+      ls[r][j] = v;
     }
-    if (tid < 32) src[tid] = tid < nr ? (amode == kATokens ? perm[b + tid] / topk : (int64_t)(b + tid)) : 0;
+    if (tid < 32)
+      src[tid] = tid < nr ? (amode == kATokens ? perm[b + tid] / topk : (int64_t)(b + tid)) : 0;
     __syncthreads();
-    if (k < K) {
-      for (int r = 0; r < nr; ++r) {
-        const float xv = bf16_to_f32(x[src[r] * K + k]);
+    // rows in groups of 8 (padding rows of ls are zero), the group's loads
+    // issued together
+    for (int r0 = 0; r0 < nr; r0 += 8) {
+      float xv[8][NC];
 #pragma unroll
-        for (int j = 0; j < R; ++j)
-          if (j < rank) acc[j] = fmaf(dus[r][j], xv, acc[j]);
+      for (int rr = 0; rr < 8; ++rr) {
+        const uint16_t* row = Rm + src[r0 + rr] * C;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          const int col = cb + 256 * c;
+          xv[rr][c] = bf16_to_f32(row[col < C ? col : C - 1]);
+        }
+      }
+#pragma unroll
+      for (int rr = 0; rr < 8; ++rr) {
+#pragma unroll
+        for (int j4 = 0; j4 < R / 4; ++j4) {
+          const f32x4_t l = *reinterpret_cast<const f32x4_t*>(&ls[r0 + rr][4 * j4]);
+#pragma unroll
+          for (int c = 0; c < NC; ++c)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) g[c][4 * j4 + q] = fmaf(l[q], xv[rr][c], g[c][4 * j4 + q]);
+        }
       }
     }
   }
-  if (k < K) {
 #pragma unroll
-    for (int j = 0; j < R; ++j)
-      if (j < rank) dA[((int64_t)e * rank + j) * K + k] = alpha * acc[j];
+  for (int c = 0; c < NC; ++c) {
+    const int col = cb + 256 * c;
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+      if (j < rank && col < C) {
+        if constexpr (TRANS_OUT) G[((int64_t)e * C + col) * rank + j] = scale * g[c][j];
+        else G[((int64_t)e * rank + j) * C + col] = scale * g[c][j];
+      }
+    }
   }
 }
 
-// dB [E][N][rank] fp32 = sum over the expert's rows of dY_i (x) u_i; thread
-// owns output row n
-template <int R>
-__global__ __launch_bounds__(256) void k_lora_dB(const uint16_t* __restrict__ dy, int N,
-                                                 const uint16_t* __restrict__ u,
-                                                 const int32_t* __restrict__ offsets, int rank,
-                                                 float* __restrict__ dB) {
-  __shared__ float us[32][128];
-  const int e = blockIdx.x;
-  const int tid = threadIdx.x;
-  const int n = blockIdx.y * 256 + tid;
-  const int i0 = offsets[e], i1 = offsets[e + 1];
-  float acc[R];
-#pragma unroll
-  for (int j = 0; j < R; ++j) acc[j] = 0.f;
-  for (int b = i0; b < i1; b += 32) {
-    const int nr = min(32, i1 - b);
-    __syncthreads();
-    for (int q = tid; q < 32 * rank; q += 256) {
-      const int r = q / rank, j = q % rank;
-      us[r][j] = r < nr ? bf16_to_f32(u[(int64_t)(b + r) * rank + j]) : 0.f;
-    }
-    __syncthreads();
-    if (n < N) {
-      for (int r = 0; r < nr; ++r) {
-        const float g = bf16_to_f32(dy[(int64_t)(b + r) * N + n]);
-#pragma unroll
-        for (int j = 0; j < R; ++j)
-          if (j < rank) acc[j] = fmaf(g, us[r][j], acc[j]);
-      }
-    }
-  }
-  if (n < N) {
-    float* o = dB + ((int64_t)e * N + n) * rank;
-#pragma unroll
-    for (int j = 0; j < R; ++j)
-      if (j < rank) o[j] = acc[j];
-  }
+template <typename LT, bool TRANS_OUT>
+void launch_wgrad(const LT* L, int rank, const uint16_t* Rm, int C, int E,
+                  const int32_t* offsets, const int32_t* perm, int topk, int amode, float scale,
+                  float* G, hipStream_t s) {
+  if (rank <= 32)
+    hipLaunchKernelGGL((k_lora_wgrad<32, 2, LT, TRANS_OUT>), dim3((unsigned)E, (C + 511) / 512),
+                       dim3(256), 0, s, L, rank, Rm, C, offsets, perm, topk, amode, scale, G);
+  else if (rank <= 64)
+    hipLaunchKernelGGL((k_lora_wgrad<64, 1, LT, TRANS_OUT>), dim3((unsigned)E, (C + 255) / 256),
+                       dim3(256), 0, s, L, rank, Rm, C, offsets, perm, topk, amode, scale, G);
+  else
+    hipLaunchKernelGGL((k_lora_wgrad<128, 1, LT, TRANS_OUT>), dim3((unsigned)E, (C + 255) / 256),
+                       dim3(256), 0, s, L, rank, Rm, C, offsets, perm, topk, amode, scale, G);
 }
 
 }  // namespace
+
+template <typename OUT>
+static void lora_rows_x_wt(const uint16_t* x, int K, const int32_t* perm, int topk, int amode,
+                           const int4* tiles, const int32_t* ntiles, int max_tiles, int MB,
+                           const uint16_t* W, int rank, float alpha, OUT* out, hipStream_t s) {
+  const dim3 grid((unsigned)(max_tiles * MB));
+  const int ncb = (rank + 31) / 32;
+  if (ncb == 1)
+    hipLaunchKernelGGL((k_lora_u<1, OUT>), grid, dim3(64), 0, s, x, K, perm, topk, amode, tiles, ntiles, MB, W, rank, alpha, out);
+  else if (ncb == 2)
+    hipLaunchKernelGGL((k_lora_u<2, OUT>), grid, dim3(64), 0, s, x, K, perm, topk, amode, tiles, ntiles, MB, W, rank, alpha, out);
+  else if (ncb == 3)
+    hipLaunchKernelGGL((k_lora_u<3, OUT>), grid, dim3(64), 0, s, x, K, perm, topk, amode, tiles, ntiles, MB, W, rank, alpha, out);
+  else
+    hipLaunchKernelGGL((k_lora_u<4, OUT>), grid, dim3(64), 0, s, x, K, perm, topk, amode, tiles, ntiles, MB, W, rank, alpha, out);
+}
 
 hipError_t launch_lora_bwd(const uint16_t* x, int K, int N, int E, const int32_t* perm, int topk,
                            int amode, const int32_t* offsets, const int4* tiles,
                            const int32_t* ntiles, int max_tiles, int MB, const uint16_t* A,
                            const uint16_t* B, int rank, float alpha, const uint16_t* dy,
-                           const uint16_t* u, float* du, uint16_t* dx, float* dA, float* dB,
-                           hipStream_t s) {
+                           const uint16_t* u, uint16_t* bt, float* du, uint16_t* dx, float* dA,
+                           float* dB, hipStream_t s) {
   if (dx || dA) {
+    // du = dY B_e over the sorted rows (zero rows: nothing to form)
+    hipLaunchKernelGGL(k_lora_bt, dim3((unsigned)E, N / 64), dim3(256), 0, s, B, N, rank, bt);
     if (max_tiles > 0) {
-      const dim3 g1((unsigned)(max_tiles * MB));
-      if (rank <= 32)
-        hipLaunchKernelGGL(k_lora_du<4>, g1, dim3(256), 0, s, dy, N, tiles, ntiles, MB, B, rank, du);
-      else if (rank <= 64)
-        hipLaunchKernelGGL(k_lora_du<8>, g1, dim3(256), 0, s, dy, N, tiles, ntiles, MB, B, rank, du);
-      else
-        hipLaunchKernelGGL(k_lora_du<16>, g1, dim3(256), 0, s, dy, N, tiles, ntiles, MB, B, rank, du);
+      lora_rows_x_wt<float>(dy, N, perm, 1, kASorted, tiles, ntiles, max_tiles, MB, bt, rank,
+                            1.0f, du, s);
       if (dx)
-        hipLaunchKernelGGL(k_lora_dx, dim3((unsigned)(max_tiles * MB), (K + 255) / 256), dim3(256), 0,
-                           s, du, tiles, ntiles, MB, A, rank, K, alpha, dx);
+        hipLaunchKernelGGL(k_lora_dx, dim3((unsigned)(max_tiles * MB), (K + 511) / 512),
+                           dim3(256), 0, s, du, tiles, ntiles, MB, A, rank, K, alpha, dx);
     }
-    if (dA) {
-      const dim3 g3((unsigned)E, (K + 255) / 256);
-      if (rank <= 32)
-        hipLaunchKernelGGL(k_lora_dA<32>, g3, dim3(256), 0, s, du, x, K, offsets, perm, topk, amode, rank, alpha, dA);
-      else if (rank <= 64)
-        hipLaunchKernelGGL(k_lora_dA<64>, g3, dim3(256), 0, s, du, x, K, offsets, perm, topk, amode, rank, alpha, dA);
-      else
-        hipLaunchKernelGGL(k_lora_dA<128>, g3, dim3(256), 0, s, du, x, K, offsets, perm, topk, amode, rank, alpha, dA);
-    }
+    if (dA) launch_wgrad<float, false>(du, rank, x, K, E, offsets, perm, topk, amode, alpha, dA, s);
   }
-  if (dB) {
-    const dim3 g4((unsigned)E, (N + 255) / 256);
-    if (rank <= 32)
-      hipLaunchKernelGGL(k_lora_dB<32>, g4, dim3(256), 0, s, dy, N, u, offsets, rank, dB);
-    else if (rank <= 64)
-      hipLaunchKernelGGL(k_lora_dB<64>, g4, dim3(256), 0, s, dy, N, u, offsets, rank, dB);
-    else
-      hipLaunchKernelGGL(k_lora_dB<128>, g4, dim3(256), 0, s, dy, N, u, offsets, rank, dB);
-  }
+  if (dB) launch_wgrad<uint16_t, true>(u, rank, dy, N, E, offsets, perm, 1, kASorted, 1.0f, dB, s);
   return hipGetLastError();
 }
 
@@ -300,16 +303,8 @@ hipError_t launch_lora_u(const uint16_t* x, int K, const int32_t* perm, int topk
                          const int4* tiles, const int32_t* ntiles, int max_tiles, int MB,
                          const uint16_t* A, int rank, float alpha, uint16_t* u, hipStream_t s) {
   if (max_tiles <= 0) return hipSuccess;
-  const dim3 grid((unsigned)(max_tiles * MB));
-  const int ncb = (rank + 31) / 32;
-  if (ncb == 1)
-    hipLaunchKernelGGL(k_lora_u<1>, grid, dim3(64), 0, s, x, K, perm, topk, amode, tiles, ntiles, MB, A, rank, alpha, u);
-  else if (ncb == 2)
-    hipLaunchKernelGGL(k_lora_u<2>, grid, dim3(64), 0, s, x, K, perm, topk, amode, tiles, ntiles, MB, A, rank, alpha, u);
-  else if (ncb == 3)
-    hipLaunchKernelGGL(k_lora_u<3>, grid, dim3(64), 0, s, x, K, perm, topk, amode, tiles, ntiles, MB, A, rank, alpha, u);
-  else
-    hipLaunchKernelGGL(k_lora_u<4>, grid, dim3(64), 0, s, x, K, perm, topk, amode, tiles, ntiles, MB, A, rank, alpha, u);
+  lora_rows_x_wt<uint16_t>(x, K, perm, topk, amode, tiles, ntiles, max_tiles, MB, A, rank, alpha,
+                           u, s);
   return hipGetLastError();
 }
 

@@ -166,7 +166,7 @@ qgg_status qgg_repack_weights(const qgg_qweight* src, uint8_t* packed_out, void*
 //  GEMM     plan (tiles, chunk table) | BF16 chunk scratch (CHUNKED)
 //  FFN_FWD  segment counts | plan | a [P][inter] | o [P][d] | scratch
 //  DX_BWD   plan | dH [P][2*inter] | dXp [P][d] | scratch | gate partials [P][inter/256] fp32
-//  LORA_BWD plan | du [P][rank] fp32
+//  LORA_BWD plan | du [P][rank] fp32 | B transposed [E][rank][N] BF16
 size_t qgg_workspace_bytes(int call, int T, int d, int E, int k, int N_or_inter, int variant,
                            int chunk, size_t* scratch_bytes) {
   if (scratch_bytes) *scratch_bytes = 0;
@@ -195,9 +195,10 @@ size_t qgg_workspace_bytes(int call, int T, int d, int E, int k, int N_or_inter,
       cv.take<char>(scratch);
       break;
     }
-    case QGG_CALL_LORA_BWD:   // N_or_inter = adapter rank
+    case QGG_CALL_LORA_BWD:   // d = N (dY width), N_or_inter = adapter rank
       carve_plan(cv, P, E, pl);
       cv.take<char>((size_t)P * N_or_inter * 4);
+      cv.take<char>((size_t)E * N_or_inter * d * 2);
       break;
     case QGG_CALL_DX_BWD: {
       const int64_t I = N_or_inter;
@@ -349,12 +350,13 @@ qgg_status lora_grouped_gemm_bwd(const qgg_lora* lora, int E, int N, int K, cons
   if (T > 0 && (!dy || (dB && !u) || (dA && !a))) return QGG_ERR_INVALID_ARG;
   const int64_t P = (int64_t)T * k;
   const size_t need =
-      qgg_workspace_bytes(QGG_CALL_LORA_BWD, T, K, E, k, lora->rank, QGG_FUSED, 0, nullptr);
+      qgg_workspace_bytes(QGG_CALL_LORA_BWD, T, N, E, k, lora->rank, QGG_FUSED, 0, nullptr);
   if (!workspace || ws_bytes < need) return QGG_ERR_WORKSPACE_TOO_SMALL;
   Carver cv(workspace);
   Plan pl;
   carve_plan(cv, P, E, pl);
   float* du = cv.take<float>((size_t)P * lora->rank * 4);
+  uint16_t* bt = cv.take<uint16_t>((size_t)E * lora->rank * N * 2);
   const PermPtrs pp = to_ptrs(p);
   if (P > 0)
     QGG_HIP(launch_tile_plan(pp, E, 32 * pl.mb, 0, pl.tiles, pl.chunk_first, stream));
@@ -362,8 +364,8 @@ qgg_status lora_grouped_gemm_bwd(const qgg_lora* lora, int E, int N, int K, cons
   // run (empty row ranges) so dA and dB are written in full
   QGG_HIP(launch_lora_bwd(a, K, N, E, p->perm, k, (flags & QGG_A_TOKENS) ? kATokens : kASorted,
                           p->offsets, pl.tiles, pl.chunk_first + E + 1, P > 0 ? (int)pl.cap : 0,
-                          pl.mb, lora->A, lora->B, lora->rank, lora->alpha, dy, u, du, dx, dA, dB,
-                          stream));
+                          pl.mb, lora->A, lora->B, lora->rank, lora->alpha, dy, u, bt, du, dx, dA,
+                          dB, stream));
   return QGG_OK;
 }
 

@@ -74,14 +74,15 @@ hipError_t launch_router_bwd(const float* gpart, int nitems, const int32_t* inv_
 hipError_t launch_lora_u(const uint16_t* x, int K, const int32_t* perm, int topk, int amode,
                          const int4* tiles, const int32_t* ntiles, int max_tiles, int MB,
                          const uint16_t* A, int rank, float alpha, uint16_t* u, hipStream_t s);
-// Adapter backward (see lora.hip): du [P][rank] fp32 scratch; dx [P][K] BF16,
-// dA [E][rank][K] fp32, dB [E][N][rank] fp32, each nullable.
+// Adapter backward (see lora.hip): bt [E][rank][N] BF16 and du [P][rank] fp32
+// scratch; dx [P][K] BF16, dA [E][rank][K] fp32, dB [E][N][rank] fp32, each
+// nullable.  N % 64 == 0.
 hipError_t launch_lora_bwd(const uint16_t* x, int K, int N, int E, const int32_t* perm, int topk,
                            int amode, const int32_t* offsets, const int4* tiles,
                            const int32_t* ntiles, int max_tiles, int MB, const uint16_t* A,
                            const uint16_t* B, int rank, float alpha, const uint16_t* dy,
-                           const uint16_t* u, float* du, uint16_t* dx, float* dA, float* dB,
-                           hipStream_t s);
+                           const uint16_t* u, uint16_t* bt, float* du, uint16_t* dx, float* dA,
+                           float* dB, hipStream_t s);
 size_t permute_ws_bytes(int64_t P, int E);
 hipError_t launch_permute(const int32_t* ids, int64_t P, int E, const PermPtrs& pp, int32_t* err,
                           void* ws, hipStream_t s);

@@ -107,7 +107,30 @@ def test_kimi_int4_gate_up_lora_full():
     assert_close(bf16_to_f64(host_u16(u_f[sel])), u_ref, what="kimi lora u")
     e = assert_close(bf16_to_f64(host_u16(y_f[sel])), y_ref, what="kimi lora y")
     print(f"case kimi lora: {rows.size} rows checked, max rel err {e:.2e}", flush=True)
-    del w, xd, Ad, Bd, y_f, u_f, packed, scales
+    # adapter backward at the same size: two active experts' gradients and
+    # their rows' dx against the oracle
+    P = cfg.T * cfg.k
+    dy_pairs = synth.normal_bf16(cfg.seed, sc.STREAM["dy"], (P, cfg.N))
+    dyd = dev_bf16(dy_pairs[pref["perm"]])
+    g = qgg.lora_grouped_gemm_bwd(Ad, Bd, alpha, xd, dyd, u_f, p, cfg.T, cfg.k)
+    sync()
+    sel_e = pref["active"][[0, pref["n_active"] // 2]]
+    srows = np.concatenate([np.arange(pref["offsets"][e], pref["offsets"][e + 1]) for e in sel_e])
+    spairs = pref["perm"][srows]
+    remap = np.full(cfg.E, -1, np.int32)
+    remap[sel_e] = np.arange(sel_e.size)
+    dx_ref, dA_ref, dB_ref = oracle.lora_bwd(
+        x, dy_pairs[spairs], (spairs // cfg.k).astype(np.int32),
+        remap[ids_ref.reshape(-1)[spairs]], A[sel_e], B[sel_e], alpha)
+    assert_close(bf16_to_f64(host_u16(g["dx"][torch.from_numpy(srows).to(DEV)])), dx_ref,
+                 what="kimi lora dx")
+    esel = torch.from_numpy(sel_e.astype(np.int64)).to(DEV)
+    assert_close(g["dA"][esel].cpu().numpy().reshape(-1, cfg.d), dA_ref.reshape(-1, cfg.d),
+                 what="kimi lora dA")
+    assert_close(g["dB"][esel].cpu().numpy().reshape(-1, rank), dB_ref.reshape(-1, rank),
+                 what="kimi lora dB")
+    print(f"case kimi lora bwd: experts {sel_e.tolist()}, {srows.size} rows checked", flush=True)
+    del w, xd, Ad, Bd, y_f, u_f, packed, scales, g, dyd
     _free()
 
 
