@@ -8,10 +8,11 @@
 // MFMA steps after its quantized K loop (same fp32 accumulators, one BF16
 // rounding), so only u is formed here.
 //
-// One wavefront per 32-row block of an M-tile: rank / 32 (rounded up) MFMA
-// column blocks of v_mfma_f32_32x32x16_bf16, both operands straight from
-// global memory (a lane's 8 K values of an x row and of an A_e row are 16
-// contiguous bytes), K / 16 steps, four in flight.
+// One workgroup per M-tile, one wavefront per 32-row block: rank / 32
+// (rounded up) MFMA column blocks of v_mfma_f32_32x32x16_bf16, both operands
+// straight from global memory (a lane's 8 K values of an x row and of an A_e
+// row are 16 contiguous bytes); the tile's wavefronts read the same A_e rows
+// at about the same time, so the expert's adapter is fetched once per tile.
 #include "qgg_device.hpp"
 #include "qgg_internal.hpp"
 
@@ -22,19 +23,19 @@ namespace qgg {
 namespace {
 
 template <int NCB, typename OUT>
-__global__ __launch_bounds__(64) void k_lora_u(const uint16_t* __restrict__ x, int K,
-                                               const int32_t* __restrict__ perm, int topk,
-                                               int amode, const int4* __restrict__ tiles,
-                                               const int32_t* __restrict__ ntiles, int MB,
-                                               const uint16_t* __restrict__ A, int rank,
-                                               float alpha, OUT* __restrict__ u) {
-  const int t = blockIdx.x / MB;
-  const int mb = blockIdx.x % MB;
+__global__ __launch_bounds__(256) void k_lora_u(const uint16_t* __restrict__ x, int K,
+                                                const int32_t* __restrict__ perm, int topk,
+                                                int amode, const int4* __restrict__ tiles,
+                                                const int32_t* __restrict__ ntiles,
+                                                const uint16_t* __restrict__ A, int rank,
+                                                float alpha, OUT* __restrict__ u) {
+  const int t = blockIdx.x;
+  const int mb = threadIdx.x >> 6;     // wavefront = 32-row block of the tile
   if (t >= *ntiles) return;
   const int4 tile = tiles[t];
   const int expert = tile.x, row0 = tile.y, nrows = tile.z;
   if (mb * 32 >= nrows) return;
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
   const int col = lane & 31, half = lane >> 5;
   // this lane's A-operand row (clamped into the tile) and its source row of x
   const int r = min(mb * 32 + col, nrows - 1);
@@ -70,13 +71,12 @@ __global__ __launch_bounds__(64) void k_lora_u(const uint16_t* __restrict__ x, i
 #pragma unroll
   for (int cb = 0; cb < NCB; ++cb) {
     const int j = 32 * cb + col;
-    if (j >= rank) continue;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const int rr = mb * 32 + 8 * i + 4 * half + jj;
-        if (rr < nrows) {
+        if (rr < nrows && j < rank) {
           const float v = alpha * acc[cb][4 * i + jj];
           if constexpr (std::is_same<OUT, float>::value)
             u[(int64_t)(row0 + rr) * rank + j] = v;
@@ -265,16 +265,16 @@ template <typename OUT>
 static void lora_rows_x_wt(const uint16_t* x, int K, const int32_t* perm, int topk, int amode,
                            const int4* tiles, const int32_t* ntiles, int max_tiles, int MB,
                            const uint16_t* W, int rank, float alpha, OUT* out, hipStream_t s) {
-  const dim3 grid((unsigned)(max_tiles * MB));
+  const dim3 grid((unsigned)max_tiles);
   const int ncb = (rank + 31) / 32;
   if (ncb == 1)
-    hipLaunchKernelGGL((k_lora_u<1, OUT>), grid, dim3(64), 0, s, x, K, perm, topk, amode, tiles, ntiles, MB, W, rank, alpha, out);
+    hipLaunchKernelGGL((k_lora_u<1, OUT>), grid, dim3(64 * MB), 0, s, x, K, perm, topk, amode, tiles, ntiles, W, rank, alpha, out);
   else if (ncb == 2)
-    hipLaunchKernelGGL((k_lora_u<2, OUT>), grid, dim3(64), 0, s, x, K, perm, topk, amode, tiles, ntiles, MB, W, rank, alpha, out);
+    hipLaunchKernelGGL((k_lora_u<2, OUT>), grid, dim3(64 * MB), 0, s, x, K, perm, topk, amode, tiles, ntiles, W, rank, alpha, out);
   else if (ncb == 3)
-    hipLaunchKernelGGL((k_lora_u<3, OUT>), grid, dim3(64), 0, s, x, K, perm, topk, amode, tiles, ntiles, MB, W, rank, alpha, out);
+    hipLaunchKernelGGL((k_lora_u<3, OUT>), grid, dim3(64 * MB), 0, s, x, K, perm, topk, amode, tiles, ntiles, W, rank, alpha, out);
   else
-    hipLaunchKernelGGL((k_lora_u<4, OUT>), grid, dim3(64), 0, s, x, K, perm, topk, amode, tiles, ntiles, MB, W, rank, alpha, out);
+    hipLaunchKernelGGL((k_lora_u<4, OUT>), grid, dim3(64 * MB), 0, s, x, K, perm, topk, amode, tiles, ntiles, W, rank, alpha, out);
 }
 
 hipError_t launch_lora_bwd(const uint16_t* x, int K, int N, int E, const int32_t* perm, int topk,
