@@ -117,7 +117,8 @@ typedef struct {
  * perm[P]        sorted row -> pair index
  * inv_perm[P]    pair index -> sorted row
  * active[E]      ids of experts with counts > 0, ascending; rest are -1
- * n_active[1]    number of active experts */
+ * n_active[1]    number of active experts
+ * perm and inv_perm may be NULL when P = T*k is 0; the others never. */
 typedef struct {
   int32_t* counts;
   int32_t* offsets;

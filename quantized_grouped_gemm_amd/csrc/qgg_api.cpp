@@ -79,8 +79,11 @@ bool valid_weight(const qgg_qweight* w, int E, int N, int K) {
          w->K == K && w->packed && w->scales;
 }
 
-bool valid_perm(const qgg_perm* p) {
-  return p && p->counts && p->offsets && p->perm && p->inv_perm && p->active && p->n_active;
+// perm and inv_perm hold one entry per routed pair, so an empty batch may
+// pass them as NULL
+bool valid_perm(const qgg_perm* p, int64_t P) {
+  return p && p->counts && p->offsets && p->active && p->n_active &&
+         (P == 0 || (p->perm && p->inv_perm));
 }
 
 bool valid_route_dims(int T, int E, int k) {
@@ -228,7 +231,7 @@ qgg_status moe_route(const float* logits, int T, int E, int k, int32_t* topk_ids
 qgg_status expert_permute(const int32_t* topk_ids, int T, int k, int E, const qgg_perm* p,
                           const uint16_t* x, int d, uint16_t* x_perm, int32_t* err_flag,
                           void* workspace, size_t ws_bytes, qgg_stream_t stream) {
-  if (!valid_route_dims(T, E, k) || !valid_perm(p)) return QGG_ERR_INVALID_ARG;
+  if (!valid_route_dims(T, E, k) || !valid_perm(p, (int64_t)T * k)) return QGG_ERR_INVALID_ARG;
   if (T > 0 && !topk_ids) return QGG_ERR_INVALID_ARG;
   const bool gather = x != nullptr && x_perm != nullptr;
   if (gather && (d <= 0 || d % 8)) return QGG_ERR_INVALID_ARG;
@@ -246,7 +249,7 @@ static qgg_status grouped_gemm(const qgg_qweight* w, const qgg_lora* lora, const
                                int flags, const qgg_perm* p, int T, int k, int variant, int chunk,
                                void* workspace, size_t ws_bytes, uint16_t* u_out, uint16_t* y,
                                qgg_stream_t stream) {
-  if (!w || !valid_perm(p) || !valid_fmt(w->fmt) || !valid_layout(w->layout))
+  if (!w || !valid_perm(p, (int64_t)T * k) || !valid_fmt(w->fmt) || !valid_layout(w->layout))
     return QGG_ERR_INVALID_ARG;
   const int E = w->E, N = w->N, K = w->K;
   if (!valid_route_dims(T, E, k) || N <= 0 || K <= 0 || chunk < 0) return QGG_ERR_INVALID_ARG;
@@ -339,7 +342,7 @@ qgg_status lora_grouped_gemm_bwd(const qgg_lora* lora, int E, int N, int K, cons
                                  const qgg_perm* p, int T, int k, void* workspace,
                                  size_t ws_bytes, uint16_t* dx, float* dA, float* dB,
                                  qgg_stream_t stream) {
-  if (!lora || !valid_perm(p) || !valid_route_dims(T, E, k) || N <= 0 || K <= 0)
+  if (!lora || !valid_perm(p, (int64_t)T * k) || !valid_route_dims(T, E, k) || N <= 0 || K <= 0)
     return QGG_ERR_INVALID_ARG;
   if (lora->rank < 16 || lora->rank > 128 || lora->rank % 16) return QGG_ERR_UNSUPPORTED;
   if (!std::isfinite(lora->alpha)) return QGG_ERR_INVALID_ARG;
@@ -379,7 +382,7 @@ qgg_status moe_ffn_fwd(const qgg_qweight* w_gate_up, const qgg_qweight* w_down,
     return QGG_ERR_INVALID_ARG;
   if (w_gate_up->fmt != w_down->fmt) return QGG_ERR_INVALID_ARG;
   if (variant != QGG_CHUNKED && variant != QGG_FUSED) return QGG_ERR_INVALID_ARG;
-  if (!valid_perm(p)) return QGG_ERR_INVALID_ARG;
+  if (!valid_perm(p, (int64_t)T * k)) return QGG_ERR_INVALID_ARG;
   if (T > 0 && (!x || !logits || !topk_ids || !topk_gates || !y)) return QGG_ERR_INVALID_ARG;
   if (d % 128 || inter % 128) return QGG_ERR_UNSUPPORTED;
   const int64_t P = (int64_t)T * k;
@@ -468,7 +471,7 @@ static qgg_status backward(const qgg_qweight* w_gate_up, const qgg_qweight* w_do
     return QGG_ERR_INVALID_ARG;
   if (w_gate_up->fmt != w_down->fmt) return QGG_ERR_INVALID_ARG;
   if (variant != QGG_CHUNKED && variant != QGG_FUSED) return QGG_ERR_INVALID_ARG;
-  if (!valid_perm(p)) return QGG_ERR_INVALID_ARG;
+  if (!valid_perm(p, (int64_t)T * k)) return QGG_ERR_INVALID_ARG;
   const bool router = dgates != nullptr || dlogits != nullptr;
   if (T > 0 && (!dy || !topk_gates || !h_saved)) return QGG_ERR_INVALID_ARG;
   if (T > 0 && !dx && !router) return QGG_ERR_INVALID_ARG;

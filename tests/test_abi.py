@@ -109,6 +109,61 @@ def test_host_side_argument_errors():
                         256, 8, 2, 256, 1, 0, fake, 16, fake, None) == 3
 
 
+def test_host_side_errors_router_and_adapter():
+    L = _lib_or_skip()
+    fake = ctypes.c_void_p(0x1000)
+    p = qgg._Perm(*([0x1000] * 6))
+    gu = qgg._QWeight(1, 8, 512, 256, 0x1000, 0x1000)
+    dn = qgg._QWeight(1, 8, 256, 256, 0x1000, 0x1000)
+    # router backward: needs an output, ids for dlogits, and a big enough workspace
+    assert L.moe_router_bwd(ctypes.byref(gu), ctypes.byref(dn), fake, fake, fake, ctypes.byref(p),
+                            fake, 4, 256, 8, 2, 256, 1, 0, fake, 1 << 30, fake, None, None,
+                            None) == 1
+    assert L.moe_router_bwd(ctypes.byref(gu), ctypes.byref(dn), fake, None, fake, ctypes.byref(p),
+                            fake, 4, 256, 8, 2, 256, 1, 0, fake, 1 << 30, None, None, fake,
+                            None) == 1
+    assert L.moe_router_bwd(ctypes.byref(gu), ctypes.byref(dn), fake, fake, fake, ctypes.byref(p),
+                            fake, 4, 256, 8, 2, 256, 1, 0, fake, 16, None, fake, fake, None) == 3
+    # adapter forward: rank limits, alpha, flags, workspace
+    w = qgg._QWeight(2, 8, 512, 256, 0x1000, 0x1000)
+    for rank, alpha, flags, want in ((8, 1.0, 1, 2), (24, 1.0, 1, 2), (160, 1.0, 1, 2),
+                                     (32, float("nan"), 1, 1), (32, 1.0, 3, 1), (32, 1.0, 5, 1)):
+        lo = qgg._Lora(rank, alpha, 0x1000, 0x1000)
+        assert L.lora_grouped_gemm(ctypes.byref(w), ctypes.byref(lo), fake, flags,
+                                   ctypes.byref(p), 4, 2, 1, 0, fake, 1 << 20, fake, fake,
+                                   None) == want, (rank, alpha, flags)
+    lo = qgg._Lora(32, 1.0, 0x1000, 0x1000)
+    assert L.lora_grouped_gemm(ctypes.byref(w), ctypes.byref(lo), fake, 1, ctypes.byref(p), 4, 2,
+                               1, 0, fake, 1 << 20, None, fake, None) == 1
+    assert L.lora_grouped_gemm(ctypes.byref(w), ctypes.byref(lo), fake, 1, ctypes.byref(p), 4, 2,
+                               1, 0, fake, 16, fake, fake, None) == 3
+    # adapter backward: rank, at least one output, u for dB, workspace
+    assert L.lora_grouped_gemm_bwd(ctypes.byref(qgg._Lora(40, 1.0, 0x1000, 0x1000)), 8, 512, 256,
+                                   fake, 1, fake, fake, ctypes.byref(p), 4, 2, fake, 1 << 30,
+                                   fake, None, None, None) == 2
+    assert L.lora_grouped_gemm_bwd(ctypes.byref(lo), 8, 512, 256, fake, 1, fake, fake,
+                                   ctypes.byref(p), 4, 2, fake, 1 << 30, None, None, None,
+                                   None) == 1
+    assert L.lora_grouped_gemm_bwd(ctypes.byref(lo), 8, 512, 256, fake, 1, fake, None,
+                                   ctypes.byref(p), 4, 2, fake, 1 << 30, None, None, fake,
+                                   None) == 1
+    assert L.lora_grouped_gemm_bwd(ctypes.byref(lo), 8, 512, 256, fake, 1, fake, fake,
+                                   ctypes.byref(p), 4, 2, fake, 16, fake, fake, fake, None) == 3
+
+
+def test_workspace_formulas_backward():
+    _lib_or_skip()
+    T, d, E, k, I = 8192, 7168, 256, 8, 2048
+    P = T * k
+    # the router partials (P x I/256 fp32) sit after the backward's other buffers
+    fused, _ = qgg.workspace_bytes(qgg.CALL_DX_BWD, T, d, E, k, I, qgg.FUSED, 0)
+    assert fused >= P * 2 * I * 2 + P * d * 2 + P * (I // 256) * 4
+    # adapter backward: du (P x rank fp32) and B transposed (E x rank x N BF16)
+    N, rank = 4096, 32
+    lb, _ = qgg.workspace_bytes(qgg.CALL_LORA_BWD, 4096, N, 384, 8, rank, qgg.FUSED, 0)
+    assert lb >= 4096 * 8 * rank * 4 + 384 * rank * N * 2
+
+
 def test_missing_library_raises(monkeypatch, tmp_path):
     monkeypatch.setattr(qgg, "LIB_PATH", str(tmp_path / "nope.so"))
     monkeypatch.setattr(qgg, "_lib", None)

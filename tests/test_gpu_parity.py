@@ -500,6 +500,38 @@ def test_moe_router_bwd_parity(cfg):
         np.testing.assert_array_equal(dl, outs[0][1])
 
 
+def test_empty_batch_every_entry_point():
+    """T = 0: every call succeeds; the adapter gradients come back as exact zeros."""
+    print("case empty batch", flush=True)
+    E, d, inter, k, rank = 6, 256, 256, 2, 16
+    logits = torch.zeros((0, E), dtype=torch.float32, device=DEV)
+    x = torch.zeros((0, d), dtype=torch.bfloat16, device=DEV)
+    ids, gates = qgg.moe_route(logits, k)
+    p, _ = qgg.expert_permute(ids, E)
+    sync()
+    assert p.counts.cpu().numpy().tolist() == [0] * E and int(p.n_active.item()) == 0
+    gu = dev_weights(2, *synth.qweights(0, 3, 2, E, 2 * inter, d), layout=qgg.LAYOUT_MFMA)
+    dn = dev_weights(2, *synth.qweights(0, 4, 2, E, d, inter), layout=qgg.LAYOUT_MFMA)
+    y = qgg.dequant_grouped_gemm(gu, x, p, 0, k)
+    assert y.shape == (0, 2 * inter)
+    for variant, chunk in [(qgg.FUSED, 0), (qgg.CHUNKED, 2)]:
+        r = qgg.moe_ffn_fwd(gu, dn, x, logits, k, variant, chunk, save_h=True)
+        assert r["y"].shape == (0, d)
+        dx = qgg.moe_dx_bwd(gu, dn, x, r["topk_gates"], r["perm"], r["h"], k, variant, chunk)
+        g = qgg.moe_router_bwd(gu, dn, x, r["topk_ids"], r["topk_gates"], r["perm"], r["h"], k,
+                               variant, chunk)
+        assert dx.shape == (0, d) and g["dlogits"].shape == (0, E)
+    A = dev_bf16(synth.normal_bf16(0, STREAM["lora_a"], (E, rank, d)))
+    B = dev_bf16(synth.normal_bf16(0, STREAM["lora_b"], (E, 2 * inter, rank)))
+    yl, u = qgg.lora_grouped_gemm(gu, A, B, 0.5, x, p, 0, k)
+    dy = torch.zeros((0, 2 * inter), dtype=torch.bfloat16, device=DEV)
+    gl = qgg.lora_grouped_gemm_bwd(A, B, 0.5, x, dy, u, p, 0, k)
+    sync()
+    assert yl.shape == (0, 2 * inter) and gl["dx"].shape == (0, d)
+    assert torch.count_nonzero(gl["dA"]).item() == 0
+    assert torch.count_nonzero(gl["dB"]).item() == 0
+
+
 def test_repeat_runs_bit_identical_and_outputs_fully_written():
     cfg = FFN_CASES[0]
     logits = synth.configs.router_logits(cfg)
