@@ -91,7 +91,8 @@ def run(args):
     import synth.configs as sc
 
     cfg = sc.CONFIGS[args.config]
-    assert cfg.kind == "proj", "the bench times the single-projection workload"
+    if cfg.kind != "proj":
+        return run_ffn(args, cfg)
     dev = torch.device("cuda:0")
     t_gen = time.perf_counter()
     logits = sc.router_logits(cfg)
@@ -213,6 +214,69 @@ def run(args):
             "kind": "oracle",
             "sample": f"all {rows} routed rows of the first {n_exp} active experts "
                       f"(oracle: decode + fp64 dot products), {dt:.1f} s"}
+    print(json.dumps(out), flush=True)
+
+
+def run_ffn(args, cfg):
+    """The expert-FFN workloads (not the default line): moe_ffn_fwd for an "ffn"
+    configuration, moe_dx_bwd (after one forward that saves h) for a "bwd" one,
+    FUSED, whole-call time.  The roofline is the call's flops against the dense
+    BF16 MFMA peak; per-kernel figures come from a rocprofv3 trace of this
+    command."""
+    import torch
+    import quantized_grouped_gemm_amd as qgg
+    import synth.configs as sc
+
+    dev = torch.device("cuda:0")
+
+    def up_w(pk_sc):
+        pk, scl = pk_sc
+        scl = scl.view(np.int16) if scl.dtype == np.uint16 else scl
+        return qgg.repack(qgg.QWeight(cfg.fmt, torch.from_numpy(pk).to(dev),
+                                      torch.from_numpy(scl).to(dev)))
+
+    def up_bf16(a):
+        return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    lt = torch.from_numpy(sc.router_logits(cfg)).to(dev)
+    x = up_bf16(sc.activations(cfg))
+    wg, wd = up_w(sc.first_weights(cfg)), up_w(sc.down_weights(cfg))
+    ws = qgg.Workspace()
+    if cfg.kind == "ffn":
+        def call():
+            return qgg.moe_ffn_fwd(wg, wd, x, lt, cfg.k, qgg.FUSED, 0, ws=ws)
+    else:
+        fwd = qgg.moe_ffn_fwd(wg, wd, x, lt, cfg.k, qgg.FUSED, 0, save_h=True)
+        dy = up_bf16(sc.grad_output(cfg))
+
+        def call():
+            return qgg.moe_dx_bwd(wg, wd, dy, fwd["topk_gates"], fwd["perm"], fwd["h"], cfg.k,
+                                  qgg.FUSED, 0, ws=ws)
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        call()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / args.steps * 1e3
+    P = cfg.T * cfg.k
+    flops = 2.0 * P * (2 * cfg.inter * cfg.d + cfg.d * cfg.inter)
+    tf = flops / (ms / 1e3) / 1e12
+    from quantized_grouped_gemm_amd import accounting as acc
+    out = {
+        "metric": "MoE expert FFN TFLOP/s (whole call)", "value": round(tf, 3),
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": cfg.name, "T": cfg.T, "d": cfg.d, "E": cfg.E, "top_k": cfg.k,
+                   "inter": cfg.inter, "weights": cfg.fmt_name + " group-32",
+                   "variant": "fused", "call": "moe_ffn_fwd" if cfg.kind == "ffn" else "moe_dx_bwd"},
+        "roofline": {"bound": "mfma", "achieved": round(tf, 2),
+                     "peak": acc.BF16_DENSE_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tf / acc.BF16_DENSE_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "whole call"},
+    }
     print(json.dumps(out), flush=True)
 
 
