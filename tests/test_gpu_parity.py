@@ -500,6 +500,87 @@ def test_moe_router_bwd_parity(cfg):
         np.testing.assert_array_equal(dl, outs[0][1])
 
 
+def _random_shapes(seed, n):
+    """Seeded shapes within the documented limits: ragged expert groups, k up
+    to 8, K a multiple of 128, N of 64, and both weight formats."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        fmt = int(rng.integers(1, 3))
+        E = int(rng.integers(1, 40))
+        k = int(rng.integers(1, min(E, 8) + 1))
+        T = int(rng.integers(1, 300))
+        d = 128 * int(rng.integers(1, 5))
+        N = 64 * int(rng.integers(1, 9))
+        out.append(scaled(CONFIGS["tiny_mxfp4_proj"], T=T, d=d, E=E, k=k, N=N, fmt=fmt,
+                          seed=100 + i, chunks=(int(rng.integers(1, E + 1)),),
+                          name=f"rand{i}_f{fmt}_T{T}_E{E}_k{k}_d{d}_N{N}"))
+    return out
+
+
+@pytest.mark.parametrize("cfg", _random_shapes(7, 8), ids=lambda c: c.name)
+def test_grouped_gemm_random_shapes(cfg):
+    print(f"case {cfg.name}", flush=True)
+    logits, x, w = _inputs(cfg)
+    ids_ref, _ = oracle.route(logits, cfg.k)
+    ref = _proj_ref(cfg, w, x, ids_ref)
+    ids, _ = qgg.moe_route(torch.from_numpy(logits).to(DEV), cfg.k)
+    p, _ = qgg.expert_permute(ids, cfg.E)
+    np.testing.assert_array_equal(ids.cpu().numpy(), ids_ref)
+    xd = dev_bf16(x)
+    inv = p.inv_perm.cpu().numpy()
+    wd = dev_weights(cfg.fmt, *w, layout=qgg.LAYOUT_MFMA)
+    yf = host_u16(qgg.dequant_grouped_gemm(wd, xd, p, cfg.T, cfg.k, qgg.FUSED, 0))
+    yc = host_u16(qgg.dequant_grouped_gemm(wd, xd, p, cfg.T, cfg.k, qgg.CHUNKED, cfg.chunks[0]))
+    sync()
+    assert_close(bf16_to_f64(yf[inv]), ref, what=cfg.name)
+    np.testing.assert_array_equal(yc, yf)
+
+
+def _random_ffn_shapes(seed, n):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        fmt = int(rng.integers(1, 3))
+        E = int(rng.integers(2, 24))
+        k = int(rng.integers(1, min(E, 6) + 1))
+        T = int(rng.integers(1, 160))
+        d = 256 * int(rng.integers(1, 3))
+        inter = 256 * int(rng.integers(1, 3))
+        out.append(scaled(CONFIGS["mxfp4_ffn_prefill"], T=T, d=d, E=E, k=k, N=2 * inter,
+                          inter=inter, fmt=fmt, seed=200 + i,
+                          chunks=(int(rng.integers(1, E + 1)),),
+                          name=f"rffn{i}_f{fmt}_T{T}_E{E}_k{k}_d{d}_I{inter}"))
+    return out
+
+
+@pytest.mark.parametrize("cfg", _random_ffn_shapes(11, 4), ids=lambda c: c.name)
+def test_ffn_and_dx_random_shapes(cfg):
+    print(f"case {cfg.name}", flush=True)
+    logits = synth.configs.router_logits(cfg)
+    x = synth.configs.activations(cfg)
+    dy = synth.configs.grad_output(cfg)
+    gu, dn = _ffn_weights(cfg)
+    ids_ref, gates_ref = oracle.route(logits, cfg.k)
+    toks = np.arange(cfg.T, dtype=np.int32)
+    y_ref, _ = oracle.ffn(cfg.fmt, gu, dn, x, ids_ref, gates_ref, toks)
+    dx_ref, _ = oracle.dx(cfg.fmt, gu, dn, x, dy, ids_ref, gates_ref, toks)
+    wg = dev_weights(cfg.fmt, *gu, layout=qgg.LAYOUT_MFMA)
+    wd = dev_weights(cfg.fmt, *dn, layout=qgg.LAYOUT_MFMA)
+    lt, xd, dyd = torch.from_numpy(logits).to(DEV), dev_bf16(x), dev_bf16(dy)
+    outs = []
+    for variant, chunk in [(qgg.FUSED, 0), (qgg.CHUNKED, cfg.chunks[0])]:
+        r = qgg.moe_ffn_fwd(wg, wd, xd, lt, cfg.k, variant, chunk, save_h=True)
+        dx = qgg.moe_dx_bwd(wg, wd, dyd, r["topk_gates"], r["perm"], r["h"], cfg.k, variant, chunk)
+        sync()
+        y, dxh = host_u16(r["y"]), host_u16(dx)
+        assert_close(bf16_to_f64(y), y_ref, what=f"{cfg.name} y v{variant}")
+        assert_close(bf16_to_f64(dxh), dx_ref, what=f"{cfg.name} dx v{variant}")
+        outs.append((y, dxh))
+    np.testing.assert_array_equal(outs[0][0], outs[1][0])
+    np.testing.assert_array_equal(outs[0][1], outs[1][1])
+
+
 def test_empty_batch_every_entry_point():
     """T = 0: every call succeeds; the adapter gradients come back as exact zeros."""
     print("case empty batch", flush=True)
