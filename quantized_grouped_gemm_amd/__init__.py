@@ -197,7 +197,11 @@ def workspace_bytes(call: int, T: int, d: int, E: int, k: int, n_or_inter: int, 
 
 
 class Workspace:
-    """A reusable device byte buffer that grows on demand."""
+    """A reusable device byte buffer that grows on demand.
+
+    Calls run in stream order on the current stream, so one workspace serves any
+    number of calls issued on that stream; calls that may run concurrently on
+    different streams each need their own (the module default is shared)."""
 
     def __init__(self):
         self.buf = None
