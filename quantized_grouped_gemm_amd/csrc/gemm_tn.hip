@@ -163,15 +163,6 @@ __device__ __forceinline__ void store_bt(const BGroup<SRC>& b, uint8_t* base, co
   for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4_t*>(base + off[i]) = v[i];
 }
 
-// 4 BF16 of a B column (rows r .. r + 3) by a transposing LDS read: within
-// each 16-lane group, lane i receives element i % 4 of the 8-byte rows that
-// lanes i / 4, i / 4 + 4, i / 4 + 8, i / 4 + 12 point at.
-__device__ __forceinline__ uint2 lds_tr4(const uint8_t* p) {
-  typedef short s16x4_t __attribute__((ext_vector_type(4)));
-  const s16x4_t v =
-      __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)p);
-  return __builtin_bit_cast(uint2, v);
-}
 
 // One work item: tile (rows [row0, row0 + nrows) of one expert) x 256 output
 // columns starting at c0, NMB live 32-row blocks.  Branch-free like the

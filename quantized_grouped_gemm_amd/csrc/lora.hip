@@ -112,59 +112,80 @@ __global__ __launch_bounds__(256) void k_lora_bt(const uint16_t* __restrict__ B,
   }
 }
 
-// dx [P][K] BF16 = alpha du A_e for one 32-row block and 512 columns (two
-// per thread); du rows staged transposed, dut[j][r], so a float4 read gives
-// four rows' du_j
+// dx [P][K] BF16 = alpha du A_e for one 32-row block and 256 columns, on
+// MFMA: the expert's A rows for those columns sit row-major in LDS and the
+// B operand (8 consecutive rank indices of one column) is read back with
+// transposing reads, as in the transposed grouped GEMM; each wavefront owns
+// 64 columns.  du (fp32) is rounded to BF16 for the MFMA A operand.
 __global__ __launch_bounds__(256) void k_lora_dx(const float* __restrict__ du,
                                                  const int4* __restrict__ tiles,
                                                  const int32_t* __restrict__ ntiles, int MB,
                                                  const uint16_t* __restrict__ A, int rank, int K,
                                                  float alpha, uint16_t* __restrict__ dx) {
-  __shared__ __attribute__((aligned(16))) float dut[128][32];
+  extern __shared__ __attribute__((aligned(16))) uint8_t at[];   // [rank][256] BF16
   const int t = blockIdx.x / MB, mb = blockIdx.x % MB;
   if (t >= *ntiles) return;
   const int4 tile = tiles[t];
   const int expert = tile.x, row0 = tile.y, nrows = tile.z;
   if (mb * 32 >= nrows) return;
   const int tid = threadIdx.x;
-  const int nr = min(32, nrows - mb * 32);
-  for (int q = tid; q < 32 * rank; q += 256) {
-    const int r = q / rank, j = q % rank;
-    dut[j][r] = r < nr ? du[(int64_t)(row0 + mb * 32 + r) * rank + j] : 0.f;
+  const int c0 = blockIdx.y * 256;
+  // stage A_e[0..rank)[c0 .. c0 + 256) (columns past K read as zero)
+  for (int pc = tid; pc < rank * 32; pc += 256) {
+    const int j = pc >> 5, piece = pc & 31;
+    const int col = c0 + 8 * piece;
+    u32x4_t v = {0u, 0u, 0u, 0u};
+    if (col < K) v = *reinterpret_cast<const u32x4_t*>(A + ((int64_t)expert * rank + j) * K + col);
+    *reinterpret_cast<u32x4_t*>(at + j * 512 + piece * 16) = v;
   }
   __syncthreads();
-  const int k0 = blockIdx.y * 512 + tid, k1 = k0 + 256;
-  float a0[32], a1[32];
+  const int wave = tid >> 6, lane = tid & 63;
+  const int col = lane & 31, half = lane >> 5;
+  const int G = lane >> 4, p = lane & 15;
+  // A operand: this lane's du row (clamped into the block)
+  const int r = min(mb * 32 + col, nrows - 1);
+  const float* dur = du + (int64_t)(row0 + r) * rank + 8 * half;
+  // B operand read offsets (sub-step 0): lane 16 G + p points at rank row
+  // 8 (G >> 1) + 4 up + p / 4, column 64 wave + 32 nb + 16 (G & 1) + 4 (p & 3)
+  int boff[2][2];
 #pragma unroll
-  for (int r = 0; r < 32; ++r) a0[r] = a1[r] = 0.f;
-  const uint16_t* a = A + (int64_t)expert * rank * K;
-  const int kc0 = k0 < K ? k0 : K - 1, kc1 = k1 < K ? k1 : K - 1;
+  for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+    for (int up = 0; up < 2; ++up)
+      boff[nb][up] = (8 * (G >> 1) + 4 * up + (p >> 2)) * 512 +
+                     (64 * wave + 32 * nb + 16 * (G & 1) + 4 * (p & 3)) * 2;
+  f32x16_t acc[2];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[nb][i] = 0.f;
   for (int j0 = 0; j0 < rank; j0 += 16) {
-    // the 16 rows' loads first, so they are in flight together
-    float w0[16], w1[16];
+    const f32x4_t lo = *reinterpret_cast<const f32x4_t*>(dur + j0);
+    const f32x4_t hi = *reinterpret_cast<const f32x4_t*>(dur + j0 + 4);
+    const bf16x8_t a = __builtin_bit_cast(
+        bf16x8_t, u32x4_t{pack_bf16x2(lo[0], lo[1]), pack_bf16x2(lo[2], lo[3]),
+                          pack_bf16x2(hi[0], hi[1]), pack_bf16x2(hi[2], hi[3])});
 #pragma unroll
-    for (int jj = 0; jj < 16; ++jj) {
-      w0[jj] = bf16_to_f32(a[(int64_t)(j0 + jj) * K + kc0]);
-      w1[jj] = bf16_to_f32(a[(int64_t)(j0 + jj) * K + kc1]);
-    }
-#pragma unroll
-    for (int jj = 0; jj < 16; ++jj) {
-#pragma unroll
-      for (int r4 = 0; r4 < 8; ++r4) {
-        const f32x4_t d = *reinterpret_cast<const f32x4_t*>(&dut[j0 + jj][4 * r4]);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          a0[4 * r4 + c] = fmaf(d[c], w0[jj], a0[4 * r4 + c]);
-          a1[4 * r4 + c] = fmaf(d[c], w1[jj], a1[4 * r4 + c]);
-        }
-      }
+    for (int nb = 0; nb < 2; ++nb) {
+      const uint2 b0 = lds_tr4(at + j0 * 512 + boff[nb][0]);
+      const uint2 b1 = lds_tr4(at + j0 * 512 + boff[nb][1]);
+      const bf16x8_t b = __builtin_bit_cast(bf16x8_t, u32x4_t{b0.x, b0.y, b1.x, b1.y});
+      acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[nb], 0, 0, 0);
     }
   }
+  // C layout: lane holds column `col` of rows 8 i + 4 half + jj
 #pragma unroll
-  for (int r = 0; r < 32; ++r) {
-    uint16_t* o = dx + (int64_t)(row0 + mb * 32 + r) * K;
-    if (r < nr && k0 < K) o[k0] = __builtin_bit_cast(uint16_t, (__bf16)(alpha * a0[r]));
-    if (r < nr && k1 < K) o[k1] = __builtin_bit_cast(uint16_t, (__bf16)(alpha * a1[r]));
+  for (int nb = 0; nb < 2; ++nb) {
+    const int k = c0 + 64 * wave + 32 * nb + col;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int rr = mb * 32 + 8 * i + 4 * half + jj;
+        if (rr < nrows && k < K)
+          dx[(int64_t)(row0 + rr) * K + k] =
+              __builtin_bit_cast(uint16_t, (__bf16)(alpha * acc[nb][4 * i + jj]));
+      }
   }
 }
 
@@ -290,8 +311,9 @@ hipError_t launch_lora_bwd(const uint16_t* x, int K, int N, int E, const int32_t
       lora_rows_x_wt<float>(dy, N, perm, 1, kASorted, tiles, ntiles, max_tiles, MB, bt, rank,
                             1.0f, du, s);
       if (dx)
-        hipLaunchKernelGGL(k_lora_dx, dim3((unsigned)(max_tiles * MB), (K + 511) / 512),
-                           dim3(256), 0, s, du, tiles, ntiles, MB, A, rank, K, alpha, dx);
+        hipLaunchKernelGGL(k_lora_dx, dim3((unsigned)(max_tiles * MB), (K + 255) / 256),
+                           dim3(256), (size_t)rank * 512, s, du, tiles, ntiles, MB, A, rank, K,
+                           alpha, dx);
     }
     if (dA) launch_wgrad<float, false>(du, rank, x, K, E, offsets, perm, topk, amode, alpha, dA, s);
   }

@@ -106,6 +106,16 @@ __device__ __forceinline__ void dq8_int4(uint32_t w, float s512, float neg8s, ui
   out[3] = pack_bf16x2(__builtin_fmaf(e46[1], s512, neg8s), __builtin_fmaf(e57[1], s512, neg8s));
 }
 
+// 4 BF16 of a B column (rows r .. r + 3) by a transposing LDS read: within
+// each 16-lane group, lane i receives element i % 4 of the 8-byte rows that
+// lanes i / 4, i / 4 + 4, i / 4 + 8, i / 4 + 12 point at.
+__device__ __forceinline__ uint2 lds_tr4(const uint8_t* p) {
+  typedef short s16x4_t __attribute__((ext_vector_type(4)));
+  const s16x4_t v =
+      __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)p);
+  return __builtin_bit_cast(uint2, v);
+}
+
 // ---- memory pipeline helpers shared by the GEMM kernels
 
 // s_waitcnt immediate: wait until at most n vector-memory operations are
