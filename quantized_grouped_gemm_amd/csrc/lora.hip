@@ -92,9 +92,8 @@ __global__ __launch_bounds__(256) void k_lora_u(const uint16_t* __restrict__ x, 
 // base frozen: du = dY B_e, dx = alpha du A_e, dA_e = alpha sum_i du_i (x) x_i,
 // dB_e = sum_i dY_i (x) u_i.  du is the same row-times-matrix product as u
 // (k_lora_u on MFMA, with B_e transposed once to [rank][N]); the other three
-// are fp32 FMA kernels whose broadcast operand sits in LDS as float4 rows, two
-// output columns per thread.  Every sum runs in a fixed order, so results are
-// deterministic.
+// run on MFMA with operands staged in LDS and read back transposed.  Every
+// sum runs in a fixed order, so results are deterministic.
 
 // Bt[e][j][n] = B[e][n][j]: a 64-row slab of one expert through LDS
 __global__ __launch_bounds__(256) void k_lora_bt(const uint16_t* __restrict__ B, int N, int rank,
@@ -189,95 +188,123 @@ __global__ __launch_bounds__(256) void k_lora_dx(const float* __restrict__ du,
   }
 }
 
-// Weight gradient of one expert, G[j][c] = scale sum_i L[i][j] R[i][c] over
-// the expert's rows i (ascending): L rows [rank] fp32 or BF16 staged in LDS,
-// R rows read per thread at NC columns c, c + 256, ... (out [rank][C] when
-// !TRANS_OUT, [C][rank] when TRANS_OUT).
-template <int R, int NC, typename LT, bool TRANS_OUT>
+// Weight gradient of one expert on MFMA, reduced over the expert's rows i
+// (ascending, 16 per MFMA step): G[j][c] = scale sum_i L[i][j] R[i][c] for
+// dA (L = du, R = the rows' x; stored [rank][C]), or G[c][j] = sum_i R[i][c]
+// L[i][j] for dB (L = u, R = dY; stored [C][rank]).  Each step stages 16 rows
+// of R (256 columns) and of L (rank, zero-padded to 32s) in LDS, row-major;
+// both MFMA operands (8 consecutive rows of one column) come back through
+// transposing reads.  Rows past the expert's end are zero.
+template <int NJB, typename LT, bool TRANS_OUT>
 __global__ __launch_bounds__(256) void k_lora_wgrad(const LT* __restrict__ L, int rank,
                                                     const uint16_t* __restrict__ Rm, int C,
                                                     const int32_t* __restrict__ offsets,
                                                     const int32_t* __restrict__ perm, int topk,
                                                     int amode, float scale,
                                                     float* __restrict__ G) {
-  __shared__ __attribute__((aligned(16))) float ls[32][R];
-  __shared__ int64_t src[32];
+  constexpr int LW = 32 * NJB;                     // L tile width (elements)
+  __shared__ __attribute__((aligned(16))) uint8_t rt[16 * 512];
+  __shared__ __attribute__((aligned(16))) uint8_t lt[16 * LW * 2];
   const int e = blockIdx.x;
+  const int c0 = blockIdx.y * 256;
   const int tid = threadIdx.x;
-  const int cb = blockIdx.y * 256 * NC + tid;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int col = lane & 31, half = lane >> 5;
+  const int Gq = lane >> 4, p = lane & 15;
   const int i0 = offsets[e], i1 = offsets[e + 1];
-  float g[NC][R];
+  // transposing-read offsets: lane 16 Gq + p points at tile row
+  // 8 (Gq >> 1) + 4 up + p / 4 and column 16 (Gq & 1) + 4 (p & 3) of its block
+  const int trow0 = 8 * (Gq >> 1) + (p >> 2);
+  const int tcol = 16 * (Gq & 1) + 4 * (p & 3);
+  f32x16_t acc[NJB][2];
 #pragma unroll
-  for (int c = 0; c < NC; ++c)
+  for (int jb = 0; jb < NJB; ++jb)
 #pragma unroll
-    for (int j = 0; j < R; ++j) g[c][j] = 0.f;
-  for (int b = i0; b < i1; b += 32) {
-    const int nr = min(32, i1 - b);
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[jb][nb][q] = 0.f;
+  for (int b = i0; b < i1; b += 16) {
     __syncthreads();
-    for (int q = tid; q < 32 * R; q += 256) {
-      const int r = q / R, j = q % R;
+    for (int pc = tid; pc < 16 * 32; pc += 256) {
+      const int r = pc >> 5, piece = pc & 31;
+      const int i = b + r;
+      const int cc = c0 + 8 * piece;
+      u32x4_t v = {0u, 0u, 0u, 0u};
+      if (i < i1 && cc < C) {
+        const int64_t src = amode == kATokens ? perm[i] / topk : (int64_t)i;
+        v = *reinterpret_cast<const u32x4_t*>(Rm + src * C + cc);
+      }
+      *reinterpret_cast<u32x4_t*>(rt + r * 512 + piece * 16) = v;
+    }
+    for (int q = tid; q < 16 * LW; q += 256) {
+      const int r = q / LW, j = q % LW;
       float v = 0.f;
-      if (r < nr && j < rank) {
+      if (b + r < i1 && j < rank) {
         if constexpr (std::is_same<LT, float>::value) v = L[(int64_t)(b + r) * rank + j];
         else v = bf16_to_f32(L[(int64_t)(b + r) * rank + j]);
       }
-      ls[r][j] = v;
+      reinterpret_cast<uint16_t*>(lt)[r * LW + j] = __builtin_bit_cast(uint16_t, (__bf16)v);
     }
-    if (tid < 32)
-      src[tid] = tid < nr ? (amode == kATokens ? perm[b + tid] / topk : (int64_t)(b + tid)) : 0;
     __syncthreads();
-    // rows in groups of 8 (padding rows of ls are zero), the group's loads
-    // issued together
-    for (int r0 = 0; r0 < nr; r0 += 8) {
-      float xv[8][NC];
+    bf16x8_t lf[NJB], rf[2];
 #pragma unroll
-      for (int rr = 0; rr < 8; ++rr) {
-        const uint16_t* row = Rm + src[r0 + rr] * C;
-#pragma unroll
-        for (int c = 0; c < NC; ++c) {
-          const int col = cb + 256 * c;
-          xv[rr][c] = bf16_to_f32(row[col < C ? col : C - 1]);
-        }
-      }
-#pragma unroll
-      for (int rr = 0; rr < 8; ++rr) {
-#pragma unroll
-        for (int j4 = 0; j4 < R / 4; ++j4) {
-          const f32x4_t l = *reinterpret_cast<const f32x4_t*>(&ls[r0 + rr][4 * j4]);
-#pragma unroll
-          for (int c = 0; c < NC; ++c)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) g[c][4 * j4 + q] = fmaf(l[q], xv[rr][c], g[c][4 * j4 + q]);
-        }
-      }
+    for (int jb = 0; jb < NJB; ++jb) {
+      const uint2 a0 = lds_tr4(lt + trow0 * LW * 2 + (32 * jb + tcol) * 2);
+      const uint2 a1 = lds_tr4(lt + (trow0 + 4) * LW * 2 + (32 * jb + tcol) * 2);
+      lf[jb] = __builtin_bit_cast(bf16x8_t, u32x4_t{a0.x, a0.y, a1.x, a1.y});
     }
-  }
 #pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    const int col = cb + 256 * c;
-#pragma unroll
-    for (int j = 0; j < R; ++j) {
-      if (j < rank && col < C) {
-        if constexpr (TRANS_OUT) G[((int64_t)e * C + col) * rank + j] = scale * g[c][j];
-        else G[((int64_t)e * rank + j) * C + col] = scale * g[c][j];
-      }
+    for (int nb = 0; nb < 2; ++nb) {
+      const int cb = 64 * wave + 32 * nb + tcol;
+      const uint2 b0 = lds_tr4(rt + trow0 * 512 + cb * 2);
+      const uint2 b1 = lds_tr4(rt + (trow0 + 4) * 512 + cb * 2);
+      rf[nb] = __builtin_bit_cast(bf16x8_t, u32x4_t{b0.x, b0.y, b1.x, b1.y});
     }
+#pragma unroll
+    for (int jb = 0; jb < NJB; ++jb)
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        if constexpr (TRANS_OUT)
+          acc[jb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(rf[nb], lf[jb], acc[jb][nb], 0, 0, 0);
+        else
+          acc[jb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(lf[jb], rf[nb], acc[jb][nb], 0, 0, 0);
+      }
   }
+  // C layout: lane holds column `col` of rows 8 q + 4 half + qq of each tile
+#pragma unroll
+  for (int jb = 0; jb < NJB; ++jb)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+          const int tr = 8 * q + 4 * half + qq;     // tile row
+          const float v = scale * acc[jb][nb][4 * q + qq];
+          if constexpr (TRANS_OUT) {
+            const int n = c0 + 64 * wave + 32 * nb + tr, j = 32 * jb + col;
+            if (n < C && j < rank) G[((int64_t)e * C + n) * rank + j] = v;
+          } else {
+            const int j = 32 * jb + tr, c = c0 + 64 * wave + 32 * nb + col;
+            if (j < rank && c < C) G[((int64_t)e * rank + j) * C + c] = v;
+          }
+        }
 }
 
 template <typename LT, bool TRANS_OUT>
 void launch_wgrad(const LT* L, int rank, const uint16_t* Rm, int C, int E,
                   const int32_t* offsets, const int32_t* perm, int topk, int amode, float scale,
                   float* G, hipStream_t s) {
-  if (rank <= 32)
-    hipLaunchKernelGGL((k_lora_wgrad<32, 2, LT, TRANS_OUT>), dim3((unsigned)E, (C + 511) / 512),
-                       dim3(256), 0, s, L, rank, Rm, C, offsets, perm, topk, amode, scale, G);
-  else if (rank <= 64)
-    hipLaunchKernelGGL((k_lora_wgrad<64, 1, LT, TRANS_OUT>), dim3((unsigned)E, (C + 255) / 256),
-                       dim3(256), 0, s, L, rank, Rm, C, offsets, perm, topk, amode, scale, G);
+  const dim3 grid((unsigned)E, (C + 255) / 256);
+  const int njb = (rank + 31) / 32;
+  if (njb == 1)
+    hipLaunchKernelGGL((k_lora_wgrad<1, LT, TRANS_OUT>), grid, dim3(256), 0, s, L, rank, Rm, C, offsets, perm, topk, amode, scale, G);
+  else if (njb == 2)
+    hipLaunchKernelGGL((k_lora_wgrad<2, LT, TRANS_OUT>), grid, dim3(256), 0, s, L, rank, Rm, C, offsets, perm, topk, amode, scale, G);
+  else if (njb == 3)
+    hipLaunchKernelGGL((k_lora_wgrad<3, LT, TRANS_OUT>), grid, dim3(256), 0, s, L, rank, Rm, C, offsets, perm, topk, amode, scale, G);
   else
-    hipLaunchKernelGGL((k_lora_wgrad<128, 1, LT, TRANS_OUT>), dim3((unsigned)E, (C + 255) / 256),
-                       dim3(256), 0, s, L, rank, Rm, C, offsets, perm, topk, amode, scale, G);
+    hipLaunchKernelGGL((k_lora_wgrad<4, LT, TRANS_OUT>), grid, dim3(256), 0, s, L, rank, Rm, C, offsets, perm, topk, amode, scale, G);
 }
 
 }  // namespace
