@@ -1,7 +1,7 @@
 """HIP-graph capture of whole calls.  The entry points never synchronize with
 the host (the chunked variant runs a fixed-length chunk loop whose bounds are
-read on the device), so moe_ffn_fwd, moe_dx_bwd and moe_router_bwd can be
-captured once and replayed.  Each replay, with unrelated eager work and host synchronizations
+read on the device), so moe_ffn_fwd, moe_dx_bwd, moe_router_bwd and the adapter
+calls can be captured once and replayed.  Each replay, with unrelated eager work and host synchronizations
 between replays, must reproduce the eager result bit for bit."""
 import numpy as np
 import pytest
@@ -66,6 +66,50 @@ def test_ffn_and_dx_graph_replays_match_eager(cfg, variant, chunk):
         for name, a, b in zip(("y", "h", "dx", "dgates", "dlogits"), got, ref):
             np.testing.assert_array_equal(a, b, err_msg=f"{name} replay {rep}")
         for t in outs:                                     # eager work between replays
+            t.zero_()
+        step()
+        sync()
+
+
+def test_adapter_calls_graph_replays_match_eager():
+    cfg = scaled(CONFIGS["kimi_int4_gate_up"], T=96, d=256, E=12, k=4, N=320, chunks=(5,),
+                 name="int4_lora_graph")
+    rank = 32
+    print(f"case {cfg.name} rank {rank}", flush=True)
+    logits = torch.from_numpy(synth.configs.router_logits(cfg)).to(DEV)
+    x = dev_bf16(synth.configs.activations(cfg))
+    w = dev_weights(cfg.fmt, *synth.configs.first_weights(cfg), layout=qgg.LAYOUT_MFMA)
+    A = dev_bf16(synth.normal_bf16(cfg.seed, 7, (cfg.E, rank, cfg.d), std=0.05))
+    B = dev_bf16(synth.normal_bf16(cfg.seed, 8, (cfg.E, cfg.N, rank), std=0.05))
+    dy = dev_bf16(synth.normal_bf16(cfg.seed, 5, (cfg.T * cfg.k, cfg.N)))
+
+    def step():
+        ids, _ = qgg.moe_route(logits, cfg.k)
+        p, _ = qgg.expert_permute(ids, cfg.E)
+        y, u = qgg.lora_grouped_gemm(w, A, B, 0.5, x, p, cfg.T, cfg.k, qgg.CHUNKED, 5)
+        g = qgg.lora_grouped_gemm_bwd(A, B, 0.5, x, dy, u, p, cfg.T, cfg.k)
+        return y, u, g["dx"], g["dA"], g["dB"]
+
+    def host(outs):
+        return [host_u16(t) for t in outs[:3]] + [t.cpu().numpy() for t in outs[3:]]
+
+    ref = host(step())
+    sync()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    sync()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        outs = step()
+    for rep in range(3):
+        graph.replay()
+        sync()
+        for name, a, b in zip(("y", "u", "dx", "dA", "dB"), host(outs), ref):
+            np.testing.assert_array_equal(a, b, err_msg=f"{name} replay {rep}")
+        for t in outs:
             t.zero_()
         step()
         sync()
