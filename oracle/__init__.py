@@ -60,6 +60,8 @@ def _L():
                                             ctypes.c_double, P, P, P, P]
         lib.oracle_lora_bwd.argtypes = [i32, i64, i64, P, P, i64, P, P, i32, ctypes.c_double,
                                         P, P, P, P, P]
+        lib.oracle_ffn_lora.argtypes = [i32, P, P, P, P, i32, i64, i64, P, i32, P, P, i64, P,
+                                        i32, ctypes.c_double, P, P, P, P, P]
         lib.oracle_silu.argtypes = [ctypes.c_double]
         lib.oracle_silu.restype = ctypes.c_double
         lib.oracle_silu_grad.argtypes = [ctypes.c_double]
@@ -224,6 +226,28 @@ def lora_bwd(x, dy, tok, expert, A, B, alpha):
                                 _p(np.ascontiguousarray(B, np.uint16)), _p(dx), _p(dA), _p(dB)),
            "lora_bwd")
     return dx, dA, dB
+
+
+def ffn_lora(fmt, gu, dn, x, ids, gates, toks, lora_gu, lora_dn, alpha):
+    """y [ntok][d] of the SwiGLU FFN with LoRA adapters: lora_gu = (A [E][r][d],
+    B [E][2I][r]) and lora_dn = (A [E][r][I], B [E][d][r]) BF16 bits, or None."""
+    gu_p, gu_s = gu
+    dn_p, dn_s = dn
+    E, N2, d2 = gu_p.shape
+    d, I = 2 * d2, N2 // 2
+    k = ids.shape[1]
+    rank = (lora_gu or lora_dn)[0].shape[1]
+    toks = np.ascontiguousarray(toks, np.int32)
+    y = np.zeros((toks.size, d), np.float64)
+    c = lambda a: None if a is None else np.ascontiguousarray(a, np.uint16)
+    Agu, Bgu = (c(lora_gu[0]), c(lora_gu[1])) if lora_gu else (None, None)
+    Adn, Bdn = (c(lora_dn[0]), c(lora_dn[1])) if lora_dn else (None, None)
+    _check(_L().oracle_ffn_lora(fmt, _p(gu_p), _p(gu_s), _p(dn_p), _p(dn_s), E, d, I, _p(x), k,
+                                _p(np.ascontiguousarray(ids, np.int32)),
+                                _p(np.ascontiguousarray(gates, np.float64)), toks.size, _p(toks),
+                                rank, float(alpha), _p(Agu), _p(Bgu), _p(Adn), _p(Bdn), _p(y)),
+           "ffn_lora")
+    return y
 
 
 def router_bwd(fmt, gu, dn, x, dy, logits, ids, toks):

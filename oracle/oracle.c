@@ -589,3 +589,96 @@ int oracle_lora_bwd(int E, int64_t N, int64_t K, const uint16_t* x, const uint16
   free(du);
   return 0;
 }
+
+/* The SwiGLU FFN of oracle_ffn with a LoRA adapter on each projection (null
+ * adapter pointers: none on that projection), in double:
+ *   h = W_gu x + alpha B_gu (A_gu x),  a = silu(h[:I]) * h[I:],
+ *   o = W_dn a + alpha B_dn (A_dn a),  y[t] = sum over j ascending of g o.
+ * A_gu [E][rank][d], B_gu [E][2I][rank], A_dn [E][rank][I], B_dn [E][d][rank]. */
+int oracle_ffn_lora(int fmt, const uint8_t* gu_p, const void* gu_s, const uint8_t* dn_p,
+                    const void* dn_s, int E, int64_t d, int64_t I, const uint16_t* x, int k,
+                    const int32_t* ids, const double* gates, int64_t ntok, const int32_t* toks,
+                    int rank, double alpha, const uint16_t* Agu, const uint16_t* Bgu,
+                    const uint16_t* Adn, const uint16_t* Bdn, double* y) {
+  if (rank <= 0) return 1;
+  const int64_t N2 = 2 * I;
+  float* wgu = (float*)malloc(sizeof(float) * (size_t)(N2 * d));
+  float* wdn = (float*)malloc(sizeof(float) * (size_t)(d * I));
+  double* xr = (double*)malloc(sizeof(double) * (size_t)d);
+  double* h = (double*)malloc(sizeof(double) * (size_t)N2);
+  double* a = (double*)malloc(sizeof(double) * (size_t)I);
+  double* op = (double*)malloc(sizeof(double) * (size_t)(ntok * k * d));   /* per pair */
+  double* u = (double*)malloc(sizeof(double) * (size_t)rank);
+  int rc = (!wgu || !wdn || !xr || !h || !a || !op || !u) ? 3 : 0;
+  for (int e = 0; e < E && !rc; ++e) {
+    int used = 0;
+    for (int64_t s = 0; s < ntok * k && !used; ++s)
+      used = ids[(int64_t)toks[s / k] * k + s % k] == e;
+    if (!used) continue;
+    const uint8_t* pe;
+    const void* se;
+    expert_ptrs(fmt, gu_p, gu_s, N2, d, e, &pe, &se);
+    rc |= oracle_decode(fmt, pe, se, N2, d, wgu);
+    expert_ptrs(fmt, dn_p, dn_s, d, I, e, &pe, &se);
+    rc |= oracle_decode(fmt, pe, se, d, I, wdn);
+    if (rc) break;
+    for (int64_t s = 0; s < ntok * k; ++s) {
+      const int64_t t = toks[s / k];
+      const int64_t j = s % k;
+      if (ids[t * k + j] != e) continue;
+      oracle_bf16_to_f64(x + t * d, d, xr);
+      for (int64_t r = 0; r < N2; ++r) h[r] = dot_f64(xr, wgu + r * d, d);
+      if (Agu && Bgu) {
+        for (int q = 0; q < rank; ++q) {
+          double acc = 0.0;
+          for (int64_t c = 0; c < d; ++c)
+            acc += xr[c] * (double)bf16_to_float(Agu[((int64_t)e * rank + q) * d + c]);
+          u[q] = acc;
+        }
+        for (int64_t r = 0; r < N2; ++r) {
+          double acc = 0.0;
+          for (int q = 0; q < rank; ++q)
+            acc += u[q] * (double)bf16_to_float(Bgu[((int64_t)e * N2 + r) * rank + q]);
+          h[r] += alpha * acc;
+        }
+      }
+      for (int64_t i = 0; i < I; ++i) a[i] = oracle_silu(h[i]) * h[I + i];
+      double* o = op + s * d;
+      for (int64_t n = 0; n < d; ++n) {
+        double acc = 0.0;
+        for (int64_t i = 0; i < I; ++i) acc += (double)wdn[n * I + i] * a[i];
+        o[n] = acc;
+      }
+      if (Adn && Bdn) {
+        for (int q = 0; q < rank; ++q) {
+          double acc = 0.0;
+          for (int64_t i = 0; i < I; ++i)
+            acc += a[i] * (double)bf16_to_float(Adn[((int64_t)e * rank + q) * I + i]);
+          u[q] = acc;
+        }
+        for (int64_t n = 0; n < d; ++n) {
+          double acc = 0.0;
+          for (int q = 0; q < rank; ++q)
+            acc += u[q] * (double)bf16_to_float(Bdn[((int64_t)e * d + n) * rank + q]);
+          o[n] += alpha * acc;
+        }
+      }
+    }
+  }
+  for (int64_t s = 0; s < ntok && !rc; ++s) {
+    const int64_t t = toks[s];
+    for (int64_t n = 0; n < d; ++n) {
+      double acc = 0.0;
+      for (int j = 0; j < k; ++j) acc += gates[t * k + j] * op[(s * k + j) * d + n];
+      y[s * d + n] = acc;
+    }
+  }
+  free(wgu);
+  free(wdn);
+  free(xr);
+  free(h);
+  free(a);
+  free(op);
+  free(u);
+  return rc;
+}

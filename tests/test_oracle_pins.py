@@ -521,6 +521,39 @@ def test_lora_bwd_matches_finite_differences():
         assert np.all(dA[e] == 0) and np.all(dB[e] == 0)
 
 
+@pytest.mark.parametrize("fmt", [1, 2])
+def test_ffn_lora_matches_twin_and_reduces_to_ffn(fmt):
+    T, d, I, E, k, rank = 5, 64, 32, 4, 2, 16
+    gu, dn, x, ids, gates = _tiny_ffn_inputs(fmt, T=T, d=d, I=I, E=E, k=k, seed=8)
+    Agu = synth.normal_bf16(8, 7, (E, rank, d), std=0.1)
+    Bgu = synth.normal_bf16(8, 8, (E, 2 * I, rank), std=0.1)
+    Adn = synth.normal_bf16(8, 9, (E, rank, I), std=0.1)
+    Bdn = synth.normal_bf16(8, 10, (E, d, rank), std=0.1)
+    toks = np.arange(T, dtype=np.int32)
+    alpha = 0.5
+    y = oracle.ffn_lora(fmt, gu, dn, x, ids, gates, toks, (Agu, Bgu), (Adn, Bdn), alpha)
+    # without adapters (alpha = 0) it is the plain FFN, exactly
+    y0 = oracle.ffn_lora(fmt, gu, dn, x, ids, gates, toks, (Agu, Bgu), (Adn, Bdn), 0.0)
+    yf, _ = oracle.ffn(fmt, gu, dn, x, ids, gates, toks)
+    np.testing.assert_array_equal(y0, yf)
+    # numpy twin
+    xf = _bf16_bits_to_f64(x)
+    for t in range(T):
+        ref = np.zeros(d)
+        for j in range(k):
+            e = ids[t, j]
+            Wg = _decode_bits(fmt, gu[0][e], gu[1][e]).astype(np.float64)
+            Wd = _decode_bits(fmt, dn[0][e], dn[1][e]).astype(np.float64)
+            h = Wg @ xf[t] + alpha * (_bf16_bits_to_f64(Bgu[e]) @ (_bf16_bits_to_f64(Agu[e]) @ xf[t]))
+            a = h[:I] / (1.0 + np.exp(-h[:I])) * h[I:]
+            o = Wd @ a + alpha * (_bf16_bits_to_f64(Bdn[e]) @ (_bf16_bits_to_f64(Adn[e]) @ a))
+            ref += gates[t, j] * o
+        np.testing.assert_allclose(y[t], ref, rtol=1e-12, atol=1e-12)
+    # an adapter on one projection only
+    yg = oracle.ffn_lora(fmt, gu, dn, x, ids, gates, toks, (Agu, Bgu), None, alpha)
+    assert not np.array_equal(yg, yf) and not np.array_equal(yg, y)
+
+
 # ------------------------------------------------------------ router backward
 
 def _twin_pair_outputs(fmt, gu, dn, xf, ids, t):
