@@ -220,6 +220,28 @@ qgg_status moe_ffn_fwd(const qgg_qweight* w_gate_up, const qgg_qweight* w_down,
                        const qgg_perm* p, uint16_t* h_save, int32_t* err_flag, void* workspace,
                        size_t ws_bytes, uint16_t* y, qgg_stream_t stream);
 
+/* moe_ffn_fwd_lora -- moe_ffn_fwd with a BF16 LoRA adapter on the gate_up
+ * and/or the down projection (either pointer may be NULL, not both): the
+ * forward of the base + adapter path that the Orbit page runs in training
+ * and in rollout alike (opening section).  h = x W_gu^T + u_gu B_gu^T with
+ * u_gu = alpha_gu x A_gu^T (A_gu [E][rank][d], B_gu [E][2*inter][rank]); a as
+ * in moe_ffn_fwd; o = a W_dn^T + u_dn B_dn^T with u_dn = alpha_dn a A_dn^T
+ * (A_dn [E][rank][inter], B_dn [E][d][rank]).  u_gate_up / u_down receive u
+ * ([P][rank] BF16, sorted order) for each given adapter.  Each up projection
+ * accumulates into its GEMM's fp32 accumulators (one BF16 rounding).  The
+ * CHUNKED variant runs every chunk's gate_up before any chunk's down when a
+ * down adapter is given (its u needs all of a); scratch stays one chunk.
+ * Same shapes, workspace (QGG_CALL_FFN_FWD) and errors as moe_ffn_fwd; a
+ * rank outside [16, 128] or not a multiple of 16 returns
+ * QGG_ERR_UNSUPPORTED. */
+qgg_status moe_ffn_fwd_lora(const qgg_qweight* w_gate_up, const qgg_qweight* w_down,
+                            const qgg_lora* lora_gate_up, const qgg_lora* lora_down,
+                            const uint16_t* x, const float* logits, int T, int d, int E, int k,
+                            int inter, int variant, int chunk, int32_t* topk_ids,
+                            float* topk_gates, const qgg_perm* p, uint16_t* h_save,
+                            uint16_t* u_gate_up, uint16_t* u_down, int32_t* err_flag,
+                            void* workspace, size_t ws_bytes, uint16_t* y, qgg_stream_t stream);
+
 /* moe_dx_bwd -- input gradient of moe_ffn_fwd with the base frozen: no
  * weight gradient and no gate gradient (gates are constants).
  * dA = (g * dY[t]) . W_down, dH = [dA * up * silu'(gate) | dA * silu(gate)]

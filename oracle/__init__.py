@@ -61,7 +61,7 @@ def _L():
         lib.oracle_lora_bwd.argtypes = [i32, i64, i64, P, P, i64, P, P, i32, ctypes.c_double,
                                         P, P, P, P, P]
         lib.oracle_ffn_lora.argtypes = [i32, P, P, P, P, i32, i64, i64, P, i32, P, P, i64, P,
-                                        i32, ctypes.c_double, P, P, P, P, P]
+                                        i32, ctypes.c_double, ctypes.c_double, P, P, P, P, P]
         lib.oracle_silu.argtypes = [ctypes.c_double]
         lib.oracle_silu.restype = ctypes.c_double
         lib.oracle_silu_grad.argtypes = [ctypes.c_double]
@@ -228,9 +228,11 @@ def lora_bwd(x, dy, tok, expert, A, B, alpha):
     return dx, dA, dB
 
 
-def ffn_lora(fmt, gu, dn, x, ids, gates, toks, lora_gu, lora_dn, alpha):
+def ffn_lora(fmt, gu, dn, x, ids, gates, toks, lora_gu, lora_dn, alpha_gu, alpha_dn=None):
     """y [ntok][d] of the SwiGLU FFN with LoRA adapters: lora_gu = (A [E][r][d],
-    B [E][2I][r]) and lora_dn = (A [E][r][I], B [E][d][r]) BF16 bits, or None."""
+    B [E][2I][r]) and lora_dn = (A [E][r][I], B [E][d][r]) BF16 bits, or None;
+    alpha_dn defaults to alpha_gu."""
+    alpha_dn = alpha_gu if alpha_dn is None else alpha_dn
     gu_p, gu_s = gu
     dn_p, dn_s = dn
     E, N2, d2 = gu_p.shape
@@ -245,7 +247,8 @@ def ffn_lora(fmt, gu, dn, x, ids, gates, toks, lora_gu, lora_dn, alpha):
     _check(_L().oracle_ffn_lora(fmt, _p(gu_p), _p(gu_s), _p(dn_p), _p(dn_s), E, d, I, _p(x), k,
                                 _p(np.ascontiguousarray(ids, np.int32)),
                                 _p(np.ascontiguousarray(gates, np.float64)), toks.size, _p(toks),
-                                rank, float(alpha), _p(Agu), _p(Bgu), _p(Adn), _p(Bdn), _p(y)),
+                                rank, float(alpha_gu), float(alpha_dn), _p(Agu), _p(Bgu), _p(Adn),
+                                _p(Bdn), _p(y)),
            "ffn_lora")
     return y
 

@@ -592,14 +592,14 @@ int oracle_lora_bwd(int E, int64_t N, int64_t K, const uint16_t* x, const uint16
 
 /* The SwiGLU FFN of oracle_ffn with a LoRA adapter on each projection (null
  * adapter pointers: none on that projection), in double:
- *   h = W_gu x + alpha B_gu (A_gu x),  a = silu(h[:I]) * h[I:],
- *   o = W_dn a + alpha B_dn (A_dn a),  y[t] = sum over j ascending of g o.
+ *   h = W_gu x + alpha_gu B_gu (A_gu x),  a = silu(h[:I]) * h[I:],
+ *   o = W_dn a + alpha_dn B_dn (A_dn a),  y[t] = sum over j ascending of g o.
  * A_gu [E][rank][d], B_gu [E][2I][rank], A_dn [E][rank][I], B_dn [E][d][rank]. */
 int oracle_ffn_lora(int fmt, const uint8_t* gu_p, const void* gu_s, const uint8_t* dn_p,
                     const void* dn_s, int E, int64_t d, int64_t I, const uint16_t* x, int k,
                     const int32_t* ids, const double* gates, int64_t ntok, const int32_t* toks,
-                    int rank, double alpha, const uint16_t* Agu, const uint16_t* Bgu,
-                    const uint16_t* Adn, const uint16_t* Bdn, double* y) {
+                    int rank, double alpha_gu, double alpha_dn, const uint16_t* Agu,
+                    const uint16_t* Bgu, const uint16_t* Adn, const uint16_t* Bdn, double* y) {
   if (rank <= 0) return 1;
   const int64_t N2 = 2 * I;
   float* wgu = (float*)malloc(sizeof(float) * (size_t)(N2 * d));
@@ -639,7 +639,7 @@ int oracle_ffn_lora(int fmt, const uint8_t* gu_p, const void* gu_s, const uint8_
           double acc = 0.0;
           for (int q = 0; q < rank; ++q)
             acc += u[q] * (double)bf16_to_float(Bgu[((int64_t)e * N2 + r) * rank + q]);
-          h[r] += alpha * acc;
+          h[r] += alpha_gu * acc;
         }
       }
       for (int64_t i = 0; i < I; ++i) a[i] = oracle_silu(h[i]) * h[I + i];
@@ -660,7 +660,7 @@ int oracle_ffn_lora(int fmt, const uint8_t* gu_p, const void* gu_s, const uint8_
           double acc = 0.0;
           for (int q = 0; q < rank; ++q)
             acc += u[q] * (double)bf16_to_float(Bdn[((int64_t)e * d + n) * rank + q]);
-          o[n] += alpha * acc;
+          o[n] += alpha_dn * acc;
         }
       }
     }

@@ -40,8 +40,9 @@ STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too sm
 
 # Every symbol include/qgg.h declares.
 EXPORTS = ("moe_route", "expert_permute", "dequant_grouped_gemm", "lora_grouped_gemm",
-           "lora_grouped_gemm_bwd", "moe_ffn_fwd", "moe_dx_bwd", "moe_router_bwd",
-           "qgg_repack_weights", "qgg_workspace_bytes", "qgg_status_string", "qgg_version")
+           "lora_grouped_gemm_bwd", "moe_ffn_fwd", "moe_ffn_fwd_lora", "moe_dx_bwd",
+           "moe_router_bwd", "qgg_repack_weights", "qgg_workspace_bytes", "qgg_status_string",
+           "qgg_version")
 
 _lib = None
 
@@ -86,6 +87,10 @@ def lib():
         L.moe_ffn_fwd.argtypes = [ctypes.POINTER(_QWeight), ctypes.POINTER(_QWeight), P, P, i32,
                                   i32, i32, i32, i32, i32, i32, P, P, ctypes.POINTER(_Perm), P, P,
                                   P, sz, P, P]
+        L.moe_ffn_fwd_lora.argtypes = [ctypes.POINTER(_QWeight), ctypes.POINTER(_QWeight),
+                                       ctypes.POINTER(_Lora), ctypes.POINTER(_Lora), P, P, i32,
+                                       i32, i32, i32, i32, i32, i32, P, P, ctypes.POINTER(_Perm),
+                                       P, P, P, P, P, sz, P, P]
         L.moe_dx_bwd.argtypes = [ctypes.POINTER(_QWeight), ctypes.POINTER(_QWeight), P, P,
                                  ctypes.POINTER(_Perm), P, i32, i32, i32, i32, i32, i32, i32, P,
                                  sz, P, P]
@@ -101,7 +106,8 @@ def lib():
         L.qgg_status_string.restype = ctypes.c_char_p
         L.qgg_version.restype = ctypes.c_char_p
         for f in ("moe_route", "expert_permute", "dequant_grouped_gemm", "lora_grouped_gemm",
-                  "lora_grouped_gemm_bwd", "moe_ffn_fwd", "moe_dx_bwd", "moe_router_bwd"):
+                  "lora_grouped_gemm_bwd", "moe_ffn_fwd", "moe_ffn_fwd_lora", "moe_dx_bwd",
+                  "moe_router_bwd"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -337,6 +343,46 @@ def moe_ffn_fwd(w_gate_up: QWeight, w_down: QWeight, x, logits, k: int, variant:
                              _ptr(h), _ptr(err_flag), _ptr(buf), buf.numel(), _ptr(y), _stream()),
            "moe_ffn_fwd")
     return dict(y=y, topk_ids=ids, topk_gates=gates, perm=p, h=h)
+
+
+def moe_ffn_fwd_lora(w_gate_up: QWeight, w_down: QWeight, lora_gate_up, lora_down, x, logits,
+                     k: int, variant: int = FUSED, chunk: int = 0, save_h: bool = False,
+                     err_flag=None, ws: Workspace | None = None):
+    """moe_ffn_fwd with BF16 LoRA adapters: lora_gate_up / lora_down are (A, B, alpha)
+    tuples of device tensors (A [E, r, K], B [E, N, r]) or None.  Adds u_gate_up /
+    u_down [P, r] (sorted order) to the result."""
+    import torch
+    T, d = x.shape
+    E = w_gate_up.E
+    inter = w_gate_up.N // 2
+    dev = x.device
+    P = T * k
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    gates = torch.empty((T, k), dtype=torch.float32, device=dev)
+    p = Perm.empty(P, E, dev)
+    h = torch.empty((P, 2 * inter), dtype=torch.bfloat16, device=dev) if save_h else None
+    y = torch.empty((T, d), dtype=torch.bfloat16, device=dev)
+
+    def adapter(l):
+        if l is None:
+            return None, None
+        A, B, alpha = l
+        u = torch.empty((P, A.shape[1]), dtype=torch.bfloat16, device=dev)
+        return _Lora(A.shape[1], float(alpha), A.data_ptr(), B.data_ptr()), u
+
+    lgu, ugu = adapter(lora_gate_up)
+    ldn, udn = adapter(lora_down)
+    nb, _ = workspace_bytes(CALL_FFN_FWD, T, d, E, k, inter, variant, chunk)
+    buf = (ws or _default_ws).get(nb, dev)
+    g, dn, pc = w_gate_up.c(), w_down.c(), p.c()
+    _check(lib().moe_ffn_fwd_lora(ctypes.byref(g), ctypes.byref(dn),
+                                  ctypes.byref(lgu) if lgu else None,
+                                  ctypes.byref(ldn) if ldn else None, _ptr(x), _ptr(logits), T, d,
+                                  E, k, inter, variant, chunk, _ptr(ids), _ptr(gates),
+                                  ctypes.byref(pc), _ptr(h), _ptr(ugu), _ptr(udn),
+                                  _ptr(err_flag), _ptr(buf), buf.numel(), _ptr(y), _stream()),
+           "moe_ffn_fwd_lora")
+    return dict(y=y, topk_ids=ids, topk_gates=gates, perm=p, h=h, u_gate_up=ugu, u_down=udn)
 
 
 def moe_dx_bwd(w_gate_up: QWeight, w_down: QWeight, dy, topk_gates, perm: Perm, h_saved, k: int,

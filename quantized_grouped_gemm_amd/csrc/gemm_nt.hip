@@ -333,10 +333,11 @@ __device__ __forceinline__ void gemm_nt_item(const GemmArgs& g,
   __builtin_amdgcn_s_waitcnt(vm_lgkm0_imm(0));
 
   if (!active) return;
-  if constexpr (EPI == kEpiStore) {
+  {
     // LoRA up projection as extra K steps on the same accumulators: A rows
     // from u (this lane's row of each block, clamped into the tile), B rows
-    // from the expert's adapter B (this wave's two output columns)
+    // from the expert's adapter B (this wave's two weight rows: two output
+    // column blocks, or the gate and up blocks of a SwiGLU item)
     if (g.lora_rank > 0) {
       const int rk = g.lora_rank;
       const uint16_t* b0p = g.lora_b + ((int64_t)expert * g.N + wrow0) * rk + 8 * half;

@@ -372,11 +372,14 @@ qgg_status lora_grouped_gemm_bwd(const qgg_lora* lora, int E, int N, int K, cons
   return QGG_OK;
 }
 
-qgg_status moe_ffn_fwd(const qgg_qweight* w_gate_up, const qgg_qweight* w_down,
-                       const uint16_t* x, const float* logits, int T, int d, int E, int k,
-                       int inter, int variant, int chunk, int32_t* topk_ids, float* topk_gates,
-                       const qgg_perm* p, uint16_t* h_save, int32_t* err_flag, void* workspace,
-                       size_t ws_bytes, uint16_t* y, qgg_stream_t stream) {
+// Shared body of moe_ffn_fwd and moe_ffn_fwd_lora (adapters nullable).
+static qgg_status ffn_forward(const qgg_qweight* w_gate_up, const qgg_qweight* w_down,
+                              const qgg_lora* lgu, const qgg_lora* ldn, const uint16_t* x,
+                              const float* logits, int T, int d, int E, int k, int inter,
+                              int variant, int chunk, int32_t* topk_ids, float* topk_gates,
+                              const qgg_perm* p, uint16_t* h_save, uint16_t* u_gu, uint16_t* u_dn,
+                              int32_t* err_flag, void* workspace, size_t ws_bytes, uint16_t* y,
+                              qgg_stream_t stream) {
   if (!valid_route_dims(T, E, k) || d <= 0 || inter <= 0 || chunk < 0) return QGG_ERR_INVALID_ARG;
   if (!valid_weight(w_gate_up, E, 2 * inter, d) || !valid_weight(w_down, E, d, inter))
     return QGG_ERR_INVALID_ARG;
@@ -408,6 +411,7 @@ qgg_status moe_ffn_fwd(const qgg_qweight* w_gate_up, const qgg_qweight* w_down,
   }
   QGG_HIP(launch_permute_plan(topk_ids, P, E, pp, err_flag, pws, 32 * pl.mb,
                               variant == QGG_CHUNKED ? C : 0, pl.tiles, pl.chunk_first, stream));
+  const int32_t* ntiles = pl.chunk_first + E + 1;
 
   GemmArgs gu = base_args(w_gate_up, pl);
   gu.a = x;
@@ -432,9 +436,51 @@ qgg_status moe_ffn_fwd(const qgg_qweight* w_gate_up, const qgg_qweight* w_down,
   dn.ldy = d;
   dn.epi = kEpiStore;
 
+  // adapter up projections ride on the GEMMs' accumulators; u of the down
+  // adapter needs the whole SwiGLU output first
+  if (lgu) {
+    QGG_HIP(launch_lora_u(x, d, p->perm, k, kATokens, pl.tiles, ntiles, (int)pl.cap, pl.mb,
+                          lgu->A, lgu->rank, lgu->alpha, u_gu, stream));
+    gu.lora_rank = lgu->rank;
+    gu.lora_u = u_gu;
+    gu.lora_b = lgu->B;
+  }
+  if (ldn) {
+    dn.lora_rank = ldn->rank;
+    dn.lora_u = u_dn;
+    dn.lora_b = ldn->B;
+  }
+  auto down_u = [&]() {
+    return launch_lora_u(abuf, inter, p->perm, k, kASorted, pl.tiles, ntiles, (int)pl.cap,
+                         pl.mb, ldn->A, ldn->rank, ldn->alpha, u_dn, stream);
+  };
   if (variant == QGG_FUSED) {
     QGG_HIP(launch_gemm_nt(gu, pl.mb, stream));
+    if (ldn) QGG_HIP(down_u());
     QGG_HIP(launch_gemm_nt(dn, pl.mb, stream));
+  } else if (ldn) {
+    // every chunk's gate_up first (the down adapter's u reads all of a),
+    // then every chunk's down projection, through the same one-chunk scratch
+    const int nch = chunk_iterations(E, P, C);
+    gu.src = dn.src = kSrcBF16;
+    gu.wbf16 = dn.wbf16 = sbuf;
+    gu.max_tiles = dn.max_tiles = (int)pl.cap;
+    for (int c = 0; c < nch; ++c) {
+      gu.range = pl.chunk_first + c;
+      gu.bf16_slot_base = c * C;
+      QGG_HIP(launch_dequant(w_gate_up->fmt, w_gate_up->packed, w_gate_up->scales,
+                             w_gate_up->layout, 2 * inter, d, p->active, p->n_active, c * C, C,
+                             true, sbuf, stream));
+      QGG_HIP(launch_gemm_nt(gu, pl.mb, stream));
+    }
+    QGG_HIP(down_u());
+    for (int c = 0; c < nch; ++c) {
+      dn.range = pl.chunk_first + c;
+      dn.bf16_slot_base = c * C;
+      QGG_HIP(launch_dequant(w_down->fmt, w_down->packed, w_down->scales, w_down->layout, d,
+                             inter, p->active, p->n_active, c * C, C, true, sbuf, stream));
+      QGG_HIP(launch_gemm_nt(dn, pl.mb, stream));
+    }
   } else {
     const int nch = chunk_iterations(E, P, C);
     gu.src = dn.src = kSrcBF16;
@@ -454,6 +500,41 @@ qgg_status moe_ffn_fwd(const qgg_qweight* w_gate_up, const qgg_qweight* w_down,
   }
   QGG_HIP(launch_combine(obuf, d, p->inv_perm, topk_gates, T, k, y, stream));
   return QGG_OK;
+}
+
+qgg_status moe_ffn_fwd(const qgg_qweight* w_gate_up, const qgg_qweight* w_down,
+                       const uint16_t* x, const float* logits, int T, int d, int E, int k,
+                       int inter, int variant, int chunk, int32_t* topk_ids, float* topk_gates,
+                       const qgg_perm* p, uint16_t* h_save, int32_t* err_flag, void* workspace,
+                       size_t ws_bytes, uint16_t* y, qgg_stream_t stream) {
+  return ffn_forward(w_gate_up, w_down, nullptr, nullptr, x, logits, T, d, E, k, inter, variant,
+                     chunk, topk_ids, topk_gates, p, h_save, nullptr, nullptr, err_flag,
+                     workspace, ws_bytes, y, stream);
+}
+
+static bool valid_lora_rank(const qgg_lora* l) {
+  return !l || (l->rank >= 16 && l->rank <= 128 && l->rank % 16 == 0);
+}
+
+qgg_status moe_ffn_fwd_lora(const qgg_qweight* w_gate_up, const qgg_qweight* w_down,
+                            const qgg_lora* lora_gate_up, const qgg_lora* lora_down,
+                            const uint16_t* x, const float* logits, int T, int d, int E, int k,
+                            int inter, int variant, int chunk, int32_t* topk_ids,
+                            float* topk_gates, const qgg_perm* p, uint16_t* h_save,
+                            uint16_t* u_gate_up, uint16_t* u_down, int32_t* err_flag,
+                            void* workspace, size_t ws_bytes, uint16_t* y, qgg_stream_t stream) {
+  if (!lora_gate_up && !lora_down) return QGG_ERR_INVALID_ARG;
+  if (!valid_lora_rank(lora_gate_up) || !valid_lora_rank(lora_down)) return QGG_ERR_UNSUPPORTED;
+  if ((lora_gate_up && !std::isfinite(lora_gate_up->alpha)) ||
+      (lora_down && !std::isfinite(lora_down->alpha)))
+    return QGG_ERR_INVALID_ARG;
+  if (T > 0 && lora_gate_up && (!lora_gate_up->A || !lora_gate_up->B || !u_gate_up))
+    return QGG_ERR_INVALID_ARG;
+  if (T > 0 && lora_down && (!lora_down->A || !lora_down->B || !u_down))
+    return QGG_ERR_INVALID_ARG;
+  return ffn_forward(w_gate_up, w_down, lora_gate_up, lora_down, x, logits, T, d, E, k, inter,
+                     variant, chunk, topk_ids, topk_gates, p, h_save, u_gate_up, u_down,
+                     err_flag, workspace, ws_bytes, y, stream);
 }
 
 // Shared body of moe_dx_bwd and moe_router_bwd.  dx == nullptr skips the

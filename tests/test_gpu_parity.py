@@ -581,6 +581,50 @@ def test_ffn_and_dx_random_shapes(cfg):
     np.testing.assert_array_equal(outs[0][1], outs[1][1])
 
 
+FFN_LORA_CASES = [(FFN_CASES[0], 16), (FFN_CASES[2], 32),
+                  (scaled(CONFIGS["int4_ffn_decode_zipf"], T=40, d=256, E=20, k=4, N=512,
+                          inter=256, chunks=(6,), name="int4_ffn_zipf_lora"), 48)]
+
+
+@pytest.mark.parametrize("cfg,rank", FFN_LORA_CASES,
+                         ids=lambda v: v.name if hasattr(v, "name") else str(v))
+def test_moe_ffn_fwd_lora_parity(cfg, rank):
+    print(f"case {cfg.name} rank {rank}", flush=True)
+    logits = synth.configs.router_logits(cfg)
+    x = synth.configs.activations(cfg)
+    gu, dn = _ffn_weights(cfg)
+    I = cfg.inter
+    Agu = synth.normal_bf16(cfg.seed, STREAM["lora_a"], (cfg.E, rank, cfg.d), std=0.05)
+    Bgu = synth.normal_bf16(cfg.seed, STREAM["lora_b"], (cfg.E, 2 * I, rank), std=0.05)
+    Adn = synth.normal_bf16(cfg.seed + 1, STREAM["lora_a"], (cfg.E, rank, I), std=0.05)
+    Bdn = synth.normal_bf16(cfg.seed + 1, STREAM["lora_b"], (cfg.E, cfg.d, rank), std=0.05)
+    ids_ref, gates_ref = oracle.route(logits, cfg.k)
+    toks = np.arange(cfg.T, dtype=np.int32)
+    wg = dev_weights(cfg.fmt, *gu, layout=qgg.LAYOUT_MFMA)
+    wd = dev_weights(cfg.fmt, *dn, layout=qgg.LAYOUT_MFMA)
+    lt, xd = torch.from_numpy(logits).to(DEV), dev_bf16(x)
+    agu = (dev_bf16(Agu), dev_bf16(Bgu), 0.5)
+    adn = (dev_bf16(Adn), dev_bf16(Bdn), 0.75)
+    for which, (lg, ld) in {"both": (agu, adn), "gate_up": (agu, None),
+                            "down": (None, adn)}.items():
+        ref = oracle.ffn_lora(cfg.fmt, gu, dn, x, ids_ref, gates_ref, toks,
+                              (Agu, Bgu) if lg else None, (Adn, Bdn) if ld else None, 0.5, 0.75)
+        outs = []
+        for variant, chunk in [(qgg.FUSED, 0), (qgg.CHUNKED, cfg.chunks[0])]:
+            r = qgg.moe_ffn_fwd_lora(wg, wd, lg, ld, xd, lt, cfg.k, variant, chunk)
+            sync()
+            y = host_u16(r["y"])
+            assert_close(bf16_to_f64(y), ref, what=f"{cfg.name} r{rank} {which} v{variant}")
+            outs.append(y)
+        np.testing.assert_array_equal(outs[0], outs[1])
+    # zero scales: the adapters add exact zeros to the base FFN
+    r0 = qgg.moe_ffn_fwd_lora(wg, wd, (agu[0], agu[1], 0.0), (adn[0], adn[1], 0.0), xd, lt,
+                              cfg.k, qgg.FUSED, 0)
+    rb = qgg.moe_ffn_fwd(wg, wd, xd, lt, cfg.k, qgg.FUSED, 0)
+    sync()
+    np.testing.assert_array_equal(host_u16(r0["y"]), host_u16(rb["y"]))
+
+
 def test_empty_batch_every_entry_point():
     """T = 0: every call succeeds; the adapter gradients come back as exact zeros."""
     print("case empty batch", flush=True)
