@@ -8,20 +8,20 @@
 // 三 微缩放量化的原理.
 //
 // Work decomposition (gfx950, 64-wide wavefronts, v_mfma_f32_32x32x16_bf16):
-//  - a work item is (M-tile of up to 32*MB rows of one expert, 256 output
+//  - a work item is (M-tile of up to 32*MB rows of one expert, 64*NW output
 //    columns); a persistent grid walks the items, split into 8 contiguous
 //    ranges so that each XCD (blocks are dealt round-robin to the 8 XCDs)
 //    works on neighbouring items that share A rows and weights in its L2;
-//  - 4 wavefronts per workgroup, each owning 64 output columns (two 32-column
-//    MFMA blocks) for all rows of the tile, so each weight element is loaded
-//    and decoded exactly once per tile;
+//  - NW wavefronts per workgroup (8, or 4 for 32-row tiles), each owning 64
+//    output columns (two 32-column MFMA blocks) for all rows of the tile, so
+//    each weight element is loaded and decoded exactly once per tile;
 //  - weights go from HBM straight into MFMA B-operand registers: lane (c, h)
 //    of a column block loads the 16 bytes of one 32-element scale group of
 //    W row c (group 2s+h of a 64-wide K step), decodes 8 elements per MFMA;
 //    the K order inside an MFMA is permuted identically for A and B, which
 //    leaves each dot product unchanged;
 //  - activation rows (gathered through perm when they are token-ordered) are
-//    staged through double-buffered LDS, 128 K elements per stage.
+//    staged through a ring of four LDS stage buffers, 64 K elements per stage.
 #include "qgg_device.hpp"
 #include "qgg_internal.hpp"
 
@@ -34,6 +34,16 @@ namespace {
 constexpr int kKL = 64;                  // K elements per stage (one K step)
 constexpr int kStageRowB = kKL * 2;      // A bytes per tile row per stage
 constexpr int kNBuf = 4;                 // stages in the LDS ring of A tiles
+// Wavefronts per workgroup (each owns 64 output columns of an item) and
+// workgroups per CU.  Tiles of 64 or 128 rows take 512-column items on eight
+// waves: every A stage copied into LDS then feeds twice the columns, which
+// halves the L2 -> LDS traffic of A.  Short tiles (decode-sized expert groups)
+// need fewer registers, and a third 4-wave workgroup keeps more weight loads
+// in flight.
+template <int MB>
+constexpr int nt_waves() { return MB == 1 ? 4 : 8; }
+template <int MB>
+constexpr int nt_occupancy() { return MB == 1 ? 3 : 1; }
 // weight steps in flight per wavefront (BF16 steps are 4x larger)
 template <int SRC>
 constexpr int ring_depth() { return SRC == kSrcBF16 ? 2 : 4; }
@@ -157,7 +167,7 @@ __device__ __forceinline__ bf16x8_t b_operand(const BRegs<SRC>& r, const BScale<
   return __builtin_bit_cast(bf16x8_t, v);
 }
 
-// One work item: tile (expert, rows [row0, row0 + nrows)) x 256 output
+// One work item: tile (expert, rows [row0, row0 + nrows)) x 64 NW output
 // columns, with NMB live 32-row blocks.  The K loop is branch-free: every
 // load index is clamped into range instead of guarded, so the compiler keeps
 // exact vmcnt counts.  Both operand streams run ahead of the MFMAs: the A
@@ -170,7 +180,9 @@ __device__ __forceinline__ void gemm_nt_item(const GemmArgs& g,
                                              int nt) {
   constexpr int kRing = ring_depth<SRC>();
   constexpr int kBL = b_loads_per_stage<SRC>();
-  constexpr int kStageLoads = NMB + kBL;            // vector-memory ops per stage
+  constexpr int NW = nt_waves<MB>();
+  constexpr int kNCA = (256 * NMB + 64 * NW - 1) / (64 * NW);   // A copies per thread
+  constexpr int kStageLoads = kNCA + kBL;           // vector-memory ops per stage
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
@@ -179,15 +191,16 @@ __device__ __forceinline__ void gemm_nt_item(const GemmArgs& g,
   const int nsteps = g.K / kKL;
   const int expert = tile.x, row0 = tile.y, nrows = tile.z;
 
-  // A copies: 16-byte slot p = 256 i + tid of a stage (i < NMB: block i
-  // covers tile rows 32 i .. 32 i + 31) receives K chunk (p & 7) ^ swz(r) of
-  // tile row r = p >> 3; rows past the tile's end copy its first row
+  // A copies: 16-byte slot p = 64 NW i + tid of a stage (i < kNCA; block mb
+  // holds tile rows 32 mb .. 32 mb + 31) receives K chunk (p & 7) ^ swz(r) of
+  // tile row r = p >> 3; rows past the tile's end copy its first row (with
+  // NMB < MB the extra slots stay inside the MB-block stage buffer)
   // (byte offsets into the A buffer; the host keeps A under 4 GiB)
   const __amdgpu_buffer_rsrc_t arsrc = raw_buffer(g.a, (uint32_t)(g.a_rows * g.lda * 2));
-  uint32_t aoffs[NMB];
+  uint32_t aoffs[kNCA];
 #pragma unroll
-  for (int i = 0; i < NMB; ++i) {
-    const int p = 256 * i + tid;
+  for (int i = 0; i < kNCA; ++i) {
+    const int p = 64 * NW * i + tid;
     const int r = p >> 3;
     const int kc = (p & 7) ^ swz(r);
     const int rr = r < nrows ? r : 0;
@@ -200,8 +213,8 @@ __device__ __forceinline__ void gemm_nt_item(const GemmArgs& g,
     constexpr int BUF = decltype(buf_c)::value;
     const uint32_t soff = (uint32_t)((st < nsteps ? st : nsteps - 1) * kStageRowB);
 #pragma unroll
-    for (int i = 0; i < NMB; ++i)
-      copy16_to_lds(arsrc, aoffs[i], soff, As.b[BUF] + (256 * i + 64 * wave) * 16);
+    for (int i = 0; i < kNCA; ++i)
+      copy16_to_lds(arsrc, aoffs[i], soff, As.b[BUF] + (64 * NW * i + 64 * wave) * 16);
   };
   // LDS offsets of this lane's A operand chunks (row col of a block, K chunk
   // 4 half + s): the chunk's slot is xb ^ c with c = s ^ 4 (mb & 1)
@@ -216,14 +229,14 @@ __device__ __forceinline__ void gemm_nt_item(const GemmArgs& g,
   int cb0, cb1, ocol;
   bool active;
   if constexpr (EPI == kEpiSwiGLU) {
-    const int base = nt * 128 + wave * 32;
+    const int base = nt * 32 * NW + wave * 32;
     active = base < g.inter;
     const int cbase = active ? base : g.inter - 32;
     ocol = cbase + col;
     cb0 = cbase >> 5;                  // gate rows
     cb1 = (g.inter + cbase) >> 5;      // up rows
   } else {
-    const int base = nt * 256 + wave * 64;
+    const int base = nt * 64 * NW + wave * 64;
     active = base < g.N;
     const int cbase = active ? base : g.N - 64;
     ocol = cbase + col;
@@ -267,7 +280,7 @@ __device__ __forceinline__ void gemm_nt_item(const GemmArgs& g,
     load_b<SRC>(bs1, st, ring[r][1]);
   }
   static_assert(kRing * kBL >= kStageLoads, "prologue leaves too few younger loads");
-  stage_barrier<2 * NMB + kRing * kBL>();
+  stage_barrier<2 * kNCA + kRing * kBL>();
 
   // one stage = one 64-wide K step; BUF = stage % kNBuf (compile-time)
   auto kstage = [&](int step, BRegs<SRC>(&slot)[2], auto buf_c) {
@@ -388,13 +401,8 @@ __device__ __forceinline__ void gemm_nt_item(const GemmArgs& g,
   }
 }
 
-// workgroups per CU: short tiles (decode-sized expert groups) need fewer
-// registers, and a third workgroup keeps more weight loads in flight
-template <int MB>
-constexpr int nt_occupancy() { return MB == 1 ? 3 : 2; }
-
 template <int SRC, int MB, int EPI, int AMODE>
-__global__ __launch_bounds__(256, nt_occupancy<MB>()) void k_gemm_nt(GemmArgs g) {
+__global__ __launch_bounds__(64 * nt_waves<MB>(), nt_occupancy<MB>()) void k_gemm_nt(GemmArgs g) {
   __shared__ __attribute__((aligned(16))) uint8_t A0[32 * MB * kStageRowB];
   __shared__ __attribute__((aligned(16))) uint8_t A1[32 * MB * kStageRowB];
   __shared__ __attribute__((aligned(16))) uint8_t A2[32 * MB * kStageRowB];
@@ -403,7 +411,9 @@ __global__ __launch_bounds__(256, nt_occupancy<MB>()) void k_gemm_nt(GemmArgs g)
   static_assert(kNBuf == 4, "four A stage buffers");
   const int t_begin = g.range[0];
   const int t_end = g.range[1];
-  const int n_tiles_n = EPI == kEpiSwiGLU ? (g.inter + 127) / 128 : (g.N + 255) / 256;
+  constexpr int NW = nt_waves<MB>();
+  const int n_tiles_n = EPI == kEpiSwiGLU ? (g.inter + 32 * NW - 1) / (32 * NW)
+                                          : (g.N + 64 * NW - 1) / (64 * NW);
   const int items = (t_end - t_begin) * n_tiles_n;
   const int per_xcd = gridDim.x >> 3;
   const int xcd = blockIdx.x & 7;
@@ -427,12 +437,15 @@ __global__ __launch_bounds__(256, nt_occupancy<MB>()) void k_gemm_nt(GemmArgs g)
 
 template <int SRC, int MB, int EPI, int AMODE>
 hipError_t launch_nt_t(const GemmArgs& g, hipStream_t s) {
-  const int n_tiles_n = EPI == kEpiSwiGLU ? (g.inter + 127) / 128 : (g.N + 255) / 256;
+  constexpr int NW = nt_waves<MB>();
+  const int n_tiles_n = EPI == kEpiSwiGLU ? (g.inter + 32 * NW - 1) / (32 * NW)
+                                          : (g.N + 64 * NW - 1) / (64 * NW);
   const int64_t bound = (int64_t)g.max_tiles * n_tiles_n;
   if (bound <= 0) return hipSuccess;
   int64_t grid = std::min<int64_t>(bound, (int64_t)num_cus() * nt_occupancy<MB>());
   grid = (grid + 7) / 8 * 8;
-  hipLaunchKernelGGL((k_gemm_nt<SRC, MB, EPI, AMODE>), dim3((unsigned)grid), dim3(256), 0, s, g);
+  hipLaunchKernelGGL((k_gemm_nt<SRC, MB, EPI, AMODE>), dim3((unsigned)grid), dim3(64 * NW), 0, s,
+                     g);
   return hipGetLastError();
 }
 
