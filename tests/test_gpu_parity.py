@@ -176,6 +176,12 @@ PROJ_CASES = [
     # >200 rows per expert: several 128-row tiles per expert, ragged
     scaled(CONFIGS["kimi_int4_gate_up"], T=700, d=256, E=6, k=2, N=320, chunks=(4,),
            name="int4_tall"),
+    # 128-row tiles take 512-column items: one full item and a 64-column item
+    # on which only the first wavefront stores
+    scaled(CONFIGS["kimi_int4_gate_up"], T=600, d=256, E=3, k=1, N=576, chunks=(2,),
+           name="int4_512col_ragged"),
+    scaled(CONFIGS["tiny_mxfp4_proj"], T=600, d=128, E=2, k=1, N=64, chunks=(1,),
+           name="mxfp4_n64_tall"),
 ]
 
 
@@ -380,6 +386,10 @@ FFN_CASES = [
            name="mxfp4_ffn_tall"),
     scaled(CONFIGS["mxfp4_ffn_prefill"], T=300, d=256, E=8, k=2, N=256, inter=128, chunks=(4,),
            name="mxfp4_ffn_mb4"),
+    # SwiGLU items of 256 intermediate columns (384 = one full + one half item)
+    # and a down projection of 640 = 512 + 128 columns
+    scaled(CONFIGS["mxfp4_ffn_prefill"], T=400, d=640, E=3, k=1, N=768, inter=384, chunks=(2,),
+           name="mxfp4_ffn_ragged_items"),
 ]
 
 
