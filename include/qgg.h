@@ -148,12 +148,27 @@ qgg_status expert_permute(const int32_t* topk_ids, int T, int k, int E, const qg
                           const uint16_t* x, int d, uint16_t* x_perm, int32_t* err_flag,
                           void* workspace, size_t ws_bytes, qgg_stream_t stream);
 
-/* dequant_grouped_gemm -- one grouped projection over the routed rows:
+/* dequant_grouped_gemm -- one grouped projection over the routed rows
+ * (Orbit page, section 时刻细节, "Active-expert-chunked dequantization": the
+ * chunk's experts are dequantized for the duration of the chunk and run as
+ * one grouped matrix multiplication; the group-32 scales along K follow
+ * "超大规模开放权重模型技术解析", 三 微缩放量化的原理):
  * y[i][:] = a_row(i) . W_e^T for every sorted row i of expert e (fp32
  * accumulate, BF16 out), y is [P][N] in sorted order.  With QGG_TRANSPOSE_W
- * the product is a_row(i) . W_e (a is [.][N], y is [P][K]).  variant and
- * chunk (experts per chunk, 0 = all active) as above; chunking never changes
- * the result.  p must come from expert_permute on the same routing. */
+ * the product is a_row(i) . W_e (a is [.][N], y is [P][K]): the transposed
+ * access of the input-gradient backward (same Orbit section, the
+ * bypass-base-weight-grad GEMM backward).  variant and chunk (experts per
+ * chunk, 0 = every expert that can be active, i.e. min(E, T*k) of them) as
+ * above; chunking never changes the result.  p must come from
+ * expert_permute on the same routing.  QGG_CHUNKED's BF16 scratch is
+ * chunk' * N * K * 2 bytes of the workspace, chunk' = chunk or, for 0,
+ * min(E, T*k): the host does not know how many experts the routing will
+ * activate, so a caller that knows the count passes it as chunk.
+ * Exactness: QGG_CHUNKED decodes every code and scale as the format defines
+ * (value rounded once to BF16).  QGG_FUSED decodes the same values for every
+ * MXFP4 scale code and for INT4 scales that are NaN or finite with
+ * magnitude below 2^119; INT4 groups whose scale is +-Inf or has magnitude
+ * >= 2^119 are outside its exact domain (qgg_check_weights flags them). */
 qgg_status dequant_grouped_gemm(const qgg_qweight* w, const uint16_t* a, int flags,
                                 const qgg_perm* p, int T, int k, int variant, int chunk,
                                 void* workspace, size_t ws_bytes, uint16_t* y,
@@ -173,8 +188,12 @@ typedef struct {
  * frozen quantized base: y[i][:] = a_row(i) . W_e^T + u[i] . B_e^T with
  * u[i][:] = alpha * a_row(i) . A_e^T.  Orbit page, opening section: the base
  * stays frozen in its low-precision format and one BF16 adapter on top of it
- * is what trains (the Orbit repository's issue #1 names LoRA as that
- * adapter's common form).  u is formed first (fp32 accumulate, stored BF16 in
+ * is what trains.  The adapter's form is a reading: the Orbit issue page
+ * ("What's the difference between this and the slime framework?") has the
+ * maintainers choose orthogonal finetuning (OFT / QOFT) as the default and
+ * prefer it to LoRA, which the question raises; the pages give no OFT
+ * formula, so the additive low-rank form, the one the pages name and define
+ * least ambiguously, is the one built.  u is formed first (fp32 accumulate, stored BF16 in
  * u_out [P][rank], sorted order: the activation the adapter's backward
  * needs); the up projection runs as extra MFMA steps on the same fp32
  * accumulators as the base product, so y is rounded to BF16 once.  Arguments
@@ -207,7 +226,11 @@ qgg_status lora_grouped_gemm_bwd(const qgg_lora* lora, int E, int N, int K, cons
                                  size_t ws_bytes, uint16_t* dx, float* dA, float* dB,
                                  qgg_stream_t stream);
 
-/* moe_ffn_fwd -- the SwiGLU expert FFN for a routed batch: route, permute,
+/* moe_ffn_fwd -- the SwiGLU expert FFN for a routed batch (Orbit page,
+ * section 时刻细节: routing, active-expert chunks, temporary dequantization
+ * and grouped GEMMs; the expert FFN's SwiGLU form, its gate|up concatenation
+ * and the gate-weighted scatter-combine are the workload definition this
+ * library targets, T=8192 d=7168 E=256 top-8 inter=2048): route, permute,
  * h = x . W_gu^T (rows [0,inter) of W_gu are gate, [inter, 2*inter) up),
  * a = silu(gate) * up, o = a . W_down^T, y[t] = sum_j g[t,j] * o[pair(t,j)]
  * (fp32 sum in ascending j).  w_gate_up: N = 2*inter, K = d; w_down: N = d,
@@ -242,8 +265,11 @@ qgg_status moe_ffn_fwd_lora(const qgg_qweight* w_gate_up, const qgg_qweight* w_d
                             uint16_t* u_gate_up, uint16_t* u_down, int32_t* err_flag,
                             void* workspace, size_t ws_bytes, uint16_t* y, qgg_stream_t stream);
 
-/* moe_dx_bwd -- input gradient of moe_ffn_fwd with the base frozen: no
- * weight gradient and no gate gradient (gates are constants).
+/* moe_dx_bwd -- input gradient of moe_ffn_fwd with the base frozen (Orbit
+ * page, section 时刻细节, the bypass-base-weight-grad GEMM backward: the
+ * frozen base gets no weight gradient, so only dX flows through it; the
+ * weights are read transposed): no weight gradient and no gate gradient
+ * (gates are constants).
  * dA = (g * dY[t]) . W_down, dH = [dA * up * silu'(gate) | dA * silu(gate)]
  * using h_saved from the forward, dXp = dH . W_gu, dx[t] = sum_j dXp[pair(t,j)]
  * (fp32 sum in ascending j).  dy, dx [T][d] BF16; topk_gates [T][k]. */
@@ -284,6 +310,17 @@ qgg_status moe_router_bwd(const qgg_qweight* w_gate_up, const qgg_qweight* w_dow
  * A pure permutation of bytes and scale entries; values are untouched. */
 qgg_status qgg_repack_weights(const qgg_qweight* src, uint8_t* packed_out, void* scales_out,
                               qgg_stream_t stream);
+
+/* qgg_check_weights -- scan the scales of a frozen weight tensor (either
+ * layout) for values the QGG_FUSED decoder does not reproduce exactly, and
+ * set bit 4 (value 4) of *err_flag (device int32, which the caller zeroes
+ * first) if there is one: an INT4 BF16 scale that is +-Inf or has magnitude
+ * >= 2^119 (the fused decode forms q*s as fma(n' 2^-9, 512 s, -8 s) and needs
+ * 512 s finite).  NaN scales decode to NaN in both variants; every MXFP4
+ * E8M0 code decodes exactly in both.  Meant for load time, beside
+ * qgg_repack_weights; QGG_CHUNKED decodes flagged weights exactly.  The
+ * group-32 scale formats: "超大规模开放权重模型技术解析", 三 微缩放量化的原理. */
+qgg_status qgg_check_weights(const qgg_qweight* w, int32_t* err_flag, qgg_stream_t stream);
 
 /* Workspace bytes a call needs.  N_or_inter is N for QGG_CALL_GEMM (with K =
  * d) and inter for the FFN calls.  *scratch_bytes (nullable) receives the part

@@ -41,8 +41,8 @@ STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too sm
 # Every symbol include/qgg.h declares.
 EXPORTS = ("moe_route", "expert_permute", "dequant_grouped_gemm", "lora_grouped_gemm",
            "lora_grouped_gemm_bwd", "moe_ffn_fwd", "moe_ffn_fwd_lora", "moe_dx_bwd",
-           "moe_router_bwd", "qgg_repack_weights", "qgg_workspace_bytes", "qgg_status_string",
-           "qgg_version")
+           "moe_router_bwd", "qgg_repack_weights", "qgg_check_weights", "qgg_workspace_bytes",
+           "qgg_status_string", "qgg_version")
 
 _lib = None
 
@@ -99,6 +99,8 @@ def lib():
                                      P, sz, P, P, P, P]
         L.qgg_repack_weights.argtypes = [ctypes.POINTER(_QWeight), P, P, P]
         L.qgg_repack_weights.restype = ctypes.c_int
+        L.qgg_check_weights.argtypes = [ctypes.POINTER(_QWeight), P, P]
+        L.qgg_check_weights.restype = ctypes.c_int
         L.qgg_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32,
                                           ctypes.POINTER(ctypes.c_size_t)]
         L.qgg_workspace_bytes.restype = ctypes.c_size_t
@@ -170,6 +172,19 @@ def repack(w: "QWeight") -> "QWeight":
     _check(lib().qgg_repack_weights(ctypes.byref(wc), _ptr(p), _ptr(s), _stream()),
            "qgg_repack_weights")
     return QWeight(w.fmt, p, s, LAYOUT_MFMA, w.shape)
+
+
+def check_weights(w: "QWeight", err_flag=None):
+    """qgg_check_weights: bit 4 of the returned device int32 flag is set when a
+    scale of ``w`` lies outside the fused decoder's exact domain (``err_flag``,
+    if given, is that device tensor, zeroed by the caller)."""
+    import torch
+    if err_flag is None:
+        err_flag = torch.zeros(1, dtype=torch.int32, device=w.packed.device)
+    wc = w.c()
+    _check(lib().qgg_check_weights(ctypes.byref(wc), _ptr(err_flag), _stream()),
+           "qgg_check_weights")
+    return err_flag
 
 
 @dataclass

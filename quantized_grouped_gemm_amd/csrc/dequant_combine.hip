@@ -172,7 +172,33 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ ro
   reinterpret_cast<u32x4_t*>(out + t * d)[c] = o;
 }
 
+// Scale validation for the fused decoder: an INT4 group whose BF16 scale is
+// +-Inf or has magnitude >= 2^119 (exponent field 246..255 without NaN, i.e.
+// |bits| in [0x7B00, 0x7F80]) sets bit 4 of *err.  The fused INT4 decode
+// forms q * s as fma(n' 2^-9, 512 s, -8 s), which needs 512 s finite; NaN
+// scales decode to NaN on both variants and are not flagged.  MXFP4 scale
+// codes all decode exactly on both variants.
+__global__ __launch_bounds__(256) void k_check_scales_int4(const uint16_t* __restrict__ scales,
+                                                           int64_t n, int32_t* __restrict__ err) {
+  bool bad = false;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const uint32_t m = scales[i] & 0x7FFFu;
+    bad |= m >= 0x7B00u && m <= 0x7F80u;
+  }
+  if (__any(bad) && (threadIdx.x & 63) == 0) atomicOr(err, 4);
+}
+
 }  // namespace
+
+hipError_t launch_check_scales(int fmt, const void* scales, int64_t n, int32_t* err,
+                               hipStream_t s) {
+  if (fmt != 2 || n <= 0) return hipSuccess;
+  const dim3 grid((unsigned)std::min<int64_t>((n + 255) / 256, (int64_t)num_cus() * 8));
+  hipLaunchKernelGGL(k_check_scales_int4, grid, dim3(256), 0, s,
+                     static_cast<const uint16_t*>(scales), n, err);
+  return hipGetLastError();
+}
 
 hipError_t launch_dequant(int fmt, const uint8_t* packed, const void* scales, int layout, int N,
                           int K, const int32_t* active, const int32_t* n_active, int first,

@@ -164,6 +164,15 @@ qgg_status qgg_repack_weights(const qgg_qweight* src, uint8_t* packed_out, void*
   return QGG_OK;
 }
 
+qgg_status qgg_check_weights(const qgg_qweight* w, int32_t* err_flag, qgg_stream_t stream) {
+  if (!w || !valid_fmt(w->fmt) || !valid_layout(w->layout) || !w->scales || !err_flag ||
+      w->E <= 0 || w->N <= 0 || w->K <= 0 || w->K % 32)
+    return QGG_ERR_INVALID_ARG;
+  const int64_t n = (int64_t)w->E * w->N * (w->K / 32);
+  QGG_HIP(launch_check_scales(w->fmt, w->scales, n, err_flag, stream));
+  return QGG_OK;
+}
+
 // Workspace layout per call (each piece 256-byte aligned, in this order):
 //  PERMUTE  segment counts
 //  GEMM     plan (tiles, chunk table) | BF16 chunk scratch (CHUNKED)

@@ -111,6 +111,11 @@ hipError_t launch_dequant(int fmt, const uint8_t* packed, const void* scales, in
                           int K, const int32_t* active, const int32_t* n_active, int first,
                           int count, bool tiled_out, uint16_t* dst, hipStream_t s);
 
+// Sets bit 4 of *err if any of the n scale entries lies outside the fused
+// decoder's exact domain (see dequant_combine.hip).
+hipError_t launch_check_scales(int fmt, const void* scales, int64_t n, int32_t* err,
+                               hipStream_t s);
+
 // ROWS -> MFMA-tiled copy of packed weights and scales.
 hipError_t launch_repack(int fmt, const uint8_t* packed, const void* scales, int E, int N, int K,
                          uint8_t* packed_out, void* scales_out, hipStream_t s);

@@ -111,7 +111,10 @@ __global__ __launch_bounds__(256) void k_route(const float* __restrict__ logits,
 // (t, j): dg_j = <dY[t], o[t, j]>, summed from the per-item partials the
 // SwiGLU-backward epilogue left in gpart (ascending item).  The gates are
 // the softmax of the kept logits, whose backward is
-// dl_j = g_j (dg_j - sum_i g_i dg_i); experts not kept get 0.
+// dl_j = g_j (dg_j - sum_i g_i dg_i); experts not kept get 0.  A pair that
+// the permutation dropped (its expert id was outside [0, E), inv_perm -1)
+// contributed nothing to the forward output, so its dg is 0 and no logit
+// entry belongs to it.
 __global__ __launch_bounds__(256) void k_router_bwd(const float* __restrict__ gpart, int nitems,
                                                     const int32_t* __restrict__ inv_perm,
                                                     const int32_t* __restrict__ ids,
@@ -125,10 +128,13 @@ __global__ __launch_bounds__(256) void k_router_bwd(const float* __restrict__ gp
   int id = -1;
   if (lane < k) {
     const int64_t q = (int64_t)t * k + lane;
-    const float* row = gpart + (int64_t)inv_perm[q] * nitems;
-    for (int c = 0; c < nitems; ++c) dg += row[c];
+    const int src = inv_perm[q];
+    if (src >= 0) {
+      const float* row = gpart + (int64_t)src * nitems;
+      for (int c = 0; c < nitems; ++c) dg += row[c];
+      id = ids[q];
+    }
     g = gates[q];
-    id = ids[q];
     if (dgates) dgates[q] = dg;
   }
   if (!dlogits) return;

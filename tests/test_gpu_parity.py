@@ -510,6 +510,60 @@ def test_moe_router_bwd_parity(cfg):
         np.testing.assert_array_equal(dl, outs[0][1])
 
 
+def test_router_bwd_ignores_pairs_the_permutation_dropped():
+    """An expert id outside [0, E) is flagged by expert_permute and its pair is
+    dropped from the sort (inv_perm -1).  The router backward must then read
+    no partial sums for that pair: its dgate is 0, every other token's
+    gradients are those of the same call without the bad id, bit for bit, and
+    the token's other experts get the kept-softmax backward with the dropped
+    pair's dg = 0."""
+    cfg = scaled(CONFIGS["mxfp4_dx_bwd"], T=64, d=256, E=6, k=2, N=512, inter=256,
+                 chunks=(4,), name="router_dropped_pair")
+    logits = synth.configs.router_logits(cfg)
+    x = synth.configs.activations(cfg)
+    dy = synth.configs.grad_output(cfg)
+    gu, dn = _ffn_weights(cfg)
+    wg, wd = dev_weights(cfg.fmt, *gu), dev_weights(cfg.fmt, *dn)
+    xd, dyd = dev_bf16(x), dev_bf16(dy)
+    ids, gates = qgg.moe_route(torch.from_numpy(logits).to(DEV), cfg.k)
+    t0, j0 = 17, 1
+    bad_ids = ids.clone()
+    bad_ids[t0, j0] = cfg.E + 5
+    flag = torch.zeros(1, dtype=torch.int32, device=DEV)
+    runs = {}
+    for name, rid, fl in (("good", ids, None), ("bad", bad_ids, flag)):
+        p, _ = qgg.expert_permute(rid, cfg.E, err_flag=fl)
+        # h in this permutation's sorted order (the gate_up projection)
+        h = qgg.dequant_grouped_gemm(wg, xd, p, cfg.T, cfg.k, qgg.FUSED, 0)
+        for variant, chunk in ((qgg.FUSED, 0), (qgg.CHUNKED, cfg.chunks[0])):
+            r = qgg.moe_router_bwd(wg, wd, dyd, rid, gates, p, h, cfg.k, variant, chunk)
+            sync()
+            runs[(name, variant)] = (r["dgates"].cpu().numpy(), r["dlogits"].cpu().numpy())
+    assert int(flag.item()) & 2, "expert_permute did not flag the bad id"
+    g = gates.cpu().numpy().astype(np.float64)
+    idn = ids.cpu().numpy()
+    dg_good, dl_good = runs[("good", qgg.FUSED)]
+    for variant in (qgg.FUSED, qgg.CHUNKED):
+        dg, dl = runs[("bad", variant)]
+        assert np.all(np.isfinite(dg)) and np.all(np.isfinite(dl))
+        assert dg[t0, j0] == 0.0
+        other = np.arange(cfg.T) != t0
+        np.testing.assert_array_equal(dg[other], dg_good[other])
+        np.testing.assert_array_equal(dl[other], dl_good[other])
+        np.testing.assert_array_equal(dg[t0, :j0], dg_good[t0, :j0])
+        np.testing.assert_array_equal(dg[t0, j0 + 1:], dg_good[t0, j0 + 1:])
+        d = dg_good[t0].astype(np.float64)
+        d[j0] = 0.0
+        want = g[t0] * (d - np.sum(g[t0] * d))
+        kept = [j for j in range(cfg.k) if j != j0]
+        got = dl[t0, idn[t0, kept]]
+        np.testing.assert_allclose(got, want[kept], rtol=1e-5,
+                                   atol=1e-6 * np.max(np.abs(want)))
+        mask = np.ones(cfg.E, bool)
+        mask[idn[t0, kept]] = False
+        assert np.all(dl[t0, mask] == 0.0)
+
+
 def _random_shapes(seed, n):
     """Seeded shapes within the documented limits: ragged expert groups, k up
     to 8, K a multiple of 128, N of 64, and both weight formats."""
