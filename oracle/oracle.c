@@ -492,9 +492,12 @@ int oracle_router_bwd(int fmt, const uint8_t* gu_p, const void* gu_s, const uint
 /* ------------------------------------------------------ adapter (LoRA) */
 
 /* Orbit page, opening section: the base is frozen in its low-precision
- * format and one BF16 adapter on top of it is what trains; the Orbit
- * repository's issue #1 names LoRA as that adapter's common form.  LoRA form
- * of one expert projection:
+ * format and one BF16 adapter on top of it is what trains.  Which adapter is
+ * a reading: on the Orbit issue page the maintainers make orthogonal
+ * finetuning (OFT / QOFT) the default and prefer it to LoRA, the feature the
+ * question mentions; no OFT formula is on the pages, so the additive
+ * low-rank (LoRA) form is what is built.  LoRA form of one expert
+ * projection:
  *   y[i][n] = sum_k x[t][k] W_e[n][k] + alpha * sum_j u[i][j] B_e[n][j],
  *   u[i][j] = sum_k x[t][k] A_e[j][k]
  * with t = tok[i], e = expert[i]; A is BF16 [E][rank][K], B BF16 [E][N][rank].

@@ -2,8 +2,10 @@
 // projection u = alpha * (x . A_e^T) per routed row.
 //
 // Orbit page, opening section: the base stays frozen in its low-precision
-// format and a BF16 adapter on top of it is what trains; the Orbit
-// repository's issue #1 names LoRA as that adapter's common form.  The up
+// format and a BF16 adapter on top of it is what trains.  The adapter form is
+// a reading: the Orbit issue page has the maintainers default to orthogonal
+// finetuning (OFT / QOFT) over LoRA, which the question raises, and the
+// pages give no OFT formula, so the additive low-rank form is built.  The up
 // projection u . B_e^T is folded into the forward grouped GEMM as extra
 // MFMA steps after its quantized K loop (same fp32 accumulators, one BF16
 // rounding), so only u is formed here.
