@@ -1,10 +1,12 @@
 """Byte and FLOP accounting for the quantized MoE grouped-GEMM path.
 
-Bytes per stored weight follow the grouped low-bit storage arithmetic on the
-page "超大规模开放权重模型技术解析" (section 三, 先算清存储账 and the
-estimate_storage helper in 实践提醒): a b-bit body plus one s-bit scale per group
-of g elements costs b + s/g bits per weight.  MXFP4 (4-bit E2M1, 8-bit E8M0
-scale, g = 32) is 4.25 bits; INT4 with a BF16 scale per 32 is 4.5 bits.
+Bits per stored weight follow from the microscaling format itself (page
+"超大规模开放权重模型技术解析", section 三, 微缩放量化的原理: a group of g
+elements stored with b bits each shares one s-bit scale), so a grouped 4-bit
+weight costs b + s/g bits: MXFP4 (E2M1 body, 8-bit E8M0 scale, g = 32) is
+4.25 bits, INT4 with a BF16 scale per 32 is 4.5 bits.  The same section's
+storage arithmetic (先算清存储账) then keeps a small share of the parameters
+in 16-bit precision.
 """
 from __future__ import annotations
 
@@ -19,18 +21,21 @@ HBM_PEAK_GBPS = 8000.0
 BF16_DENSE_PEAK_TFLOPS = 2516.6   # 256 CU x 4096 FLOP/clk x 2.4 GHz
 
 
-def storage_bytes(total_params: float, bits: int = 4, group_size: int = 32, scale_bits: int = 8,
-                  sensitive_ratio: float = 0.0, sensitive_bytes: float = 2.0) -> float:
-    """Grouped low-bit storage: body + one scale per group (+ a high-precision share)."""
-    quantized = total_params * (1.0 - sensitive_ratio)
-    body = quantized * bits / 8.0
-    scales = quantized / group_size * scale_bits / 8.0
-    sensitive = total_params * sensitive_ratio * sensitive_bytes
-    return body + scales + sensitive
+def grouped_bits(body_bits: float, group: int, scale_bits: float) -> float:
+    """Bits per weight of a group-scaled format: the body plus the group's
+    shared scale spread over its elements."""
+    return body_bits + scale_bits / group
+
+
+def storage_bytes(total_params: float, bits_per_weight: float, high_share: float = 0.0,
+                  high_bytes: float = 2.0) -> float:
+    """Bytes of a checkpoint whose parameters are stored at bits_per_weight,
+    except a fraction high_share kept at high_bytes each (FP16: 2)."""
+    return total_params * ((1.0 - high_share) * bits_per_weight / 8.0 + high_share * high_bytes)
 
 
 def bits_per_weight(fmt: int) -> float:
-    return 4.0 + SCALE_BITS[fmt] / GROUP
+    return grouped_bits(4, GROUP, SCALE_BITS[fmt])
 
 
 def packed_bytes(fmt: int, N: int, K: int) -> int:

@@ -7,11 +7,13 @@ multiply-add), so its exactness is checked on its own here: identity probes
 read every decoded weight back through the grouped GEMM.  A one-hot A row
 e_k gives y[n] = W[n][k] (one exact product; every other term is 0 * a finite
 weight), in both orientations: y = x W^T (one-hot over K) and the transposed
-y = a W (one-hot over N).  A weight that is NaN or Inf would turn the zero
-terms of its own dot products into NaN, so each probe row holds one group of
-interest and every group that can decode to a non-finite value sits in W
-positions no other such group shares; the oracle sums the same terms in
-double and shows the same NaNs.
+y = a W (one-hot over N).  The reference is the oracle's decode in its BF16
+view (the value rounded once to BF16, as both variants feed it to the
+matrix cores), element by element.  A weight that is NaN or Inf turns the
+zero terms of its own dot products into NaN, so each probe row holds one
+group of interest, every group that can decode to a non-finite value sits in
+W positions no other such group shares, and the reference marks as NaN every
+output whose dot product holds such a term.
 
 Formats ("超大规模开放权重模型技术解析", 三 微缩放量化的原理: 32 elements share
 one scale): all 256 E8M0 codes x 16 E2M1 codes, and all 65536 BF16 INT4 scale
@@ -205,18 +207,38 @@ def _transposed(fmt, packed, scales, layout):
     return host_u16(yf)[inv], host_u16(yc)[inv]
 
 
+def _decoded(fmt, packed, scales):
+    """The oracle's decoded weights of one expert in their BF16 view, as
+    float64 (the GEMMs' B operand values)."""
+    return oracle.bf16_to_f64(oracle.bf16_view(oracle.decode(fmt, packed, scales)))
+
+
+def _poisoned(w):
+    """For each element, whether another element of the same dot product is
+    non-finite: along the row (axis 1) for the one-hot probes over K."""
+    bad = ~np.isfinite(w)
+    return (bad.sum(axis=1, keepdims=True) - bad) > 0
+
+
 def _oracle_forward(fmt, packed, scales):
-    N, K = packed.shape[0], packed.shape[1] * 2
-    x = np.zeros((K, K), np.uint16)
-    x[np.arange(K), np.arange(K)] = ONE
-    return oracle.project(fmt, packed[None], scales[None], x, np.arange(K, dtype=np.int32),
-                          np.zeros(K, np.int32))
+    """y[t][n] = sum_k e_t[k] W[n][k] = W[n][t], plus NaN when another weight
+    of row n is non-finite (0 * Inf or 0 * NaN)."""
+    w = _decoded(fmt, packed, scales)
+    ref = w.copy()
+    ref[_poisoned(w)] = np.nan
+    return np.ascontiguousarray(ref.T)
 
 
 def _oracle_transposed(fmt, packed, scales):
-    E, Ne = packed.shape[0], packed.shape[1]
-    a, ids = _one_hot_over_rows(E, Ne)
-    return oracle.project_t(fmt, packed, scales, a, ids[:, 0])
+    """Token t = e * Ne + n: y[t][c] = sum_m e_n[m] W_e[m][c] = W_e[n][c], plus
+    NaN when another weight of column c of W_e is non-finite."""
+    out = []
+    for e in range(packed.shape[0]):
+        w = _decoded(fmt, packed[e], scales[e])
+        ref = w.copy()
+        ref[_poisoned(w.T).T] = np.nan
+        out.append(ref)
+    return np.concatenate(out, axis=0)
 
 
 def _check(what, fused, chunked, ref, allowed_cols=None):

@@ -634,8 +634,9 @@ def test_storage_accounting_worked_example():
                 a, b = ln.split()
                 kv[a] = float(b)
     P = kv["total_params"]
-    total = accounting.storage_bytes(P, int(kv["bits"]), int(kv["group_size"]),
-                                     int(kv["scale_bits"]), kv["sensitive_ratio"])
+    bpw = accounting.grouped_bits(kv["bits"], int(kv["group_size"]), kv["scale_bits"])
+    assert bpw == 4.25
+    total = accounting.storage_bytes(P, bpw, kv["sensitive_ratio"])
     assert abs(total - 1.56975e12) < 1e3
     assert round(total / 1e12, 2) in (1.56, 1.57)     # page prints ~1.56 TB
     assert abs(P * 2 - kv["fp16_bytes_printed"]) < 1
