@@ -243,6 +243,28 @@ qgg_status moe_ffn_fwd(const qgg_qweight* w_gate_up, const qgg_qweight* w_down,
                        const qgg_perm* p, uint16_t* h_save, int32_t* err_flag, void* workspace,
                        size_t ws_bytes, uint16_t* y, qgg_stream_t stream);
 
+/* moe_ffn_fwd_noalloc -- moe_ffn_fwd for callers that cannot allocate device
+ * memory or hand over a workspace (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation): the same kernels, with
+ * the workspace taken from a library-owned static device array of
+ * QGG_STATIC_SCRATCH_BYTES (32 MiB) per GPU, kept until the process ends.
+ * Arguments and results as moe_ffn_fwd without workspace / ws_bytes.  A call
+ * whose qgg_workspace_bytes(QGG_CALL_FFN_FWD, ...) exceeds the array returns
+ * QGG_ERR_WORKSPACE_TOO_SMALL before any launch (e.g. the FUSED decode batch
+ * T=64, d=7168, E=384, top-8, inter=2048 needs about 10 MiB; a CHUNKED call
+ * needs chunk * 2 * inter * d * 2 bytes of scratch on top).  It calls no
+ * allocator.  Every call on one GPU shares that GPU's array and leaves its
+ * contents behind; every byte a call reads from it is written by the same
+ * call first, so no clearing is needed, but calls that overlap on one GPU
+ * (different streams or threads) race and must be serialised by the
+ * caller. */
+#define QGG_STATIC_SCRATCH_BYTES (32u << 20)
+qgg_status moe_ffn_fwd_noalloc(const qgg_qweight* w_gate_up, const qgg_qweight* w_down,
+                               const uint16_t* x, const float* logits, int T, int d, int E, int k,
+                               int inter, int variant, int chunk, int32_t* topk_ids,
+                               float* topk_gates, const qgg_perm* p, uint16_t* h_save,
+                               int32_t* err_flag, uint16_t* y, qgg_stream_t stream);
+
 /* moe_ffn_fwd_lora -- moe_ffn_fwd with a BF16 LoRA adapter on the gate_up
  * and/or the down projection (either pointer may be NULL, not both): the
  * forward of the base + adapter path that the Orbit page runs in training

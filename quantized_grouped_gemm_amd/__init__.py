@@ -40,7 +40,8 @@ STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too sm
 
 # Every symbol include/qgg.h declares.
 EXPORTS = ("moe_route", "expert_permute", "dequant_grouped_gemm", "lora_grouped_gemm",
-           "lora_grouped_gemm_bwd", "moe_ffn_fwd", "moe_ffn_fwd_lora", "moe_dx_bwd",
+           "lora_grouped_gemm_bwd", "moe_ffn_fwd", "moe_ffn_fwd_noalloc", "moe_ffn_fwd_lora",
+           "moe_dx_bwd",
            "moe_router_bwd", "qgg_repack_weights", "qgg_check_weights", "qgg_workspace_bytes",
            "qgg_status_string", "qgg_version")
 
@@ -87,6 +88,9 @@ def lib():
         L.moe_ffn_fwd.argtypes = [ctypes.POINTER(_QWeight), ctypes.POINTER(_QWeight), P, P, i32,
                                   i32, i32, i32, i32, i32, i32, P, P, ctypes.POINTER(_Perm), P, P,
                                   P, sz, P, P]
+        L.moe_ffn_fwd_noalloc.argtypes = [ctypes.POINTER(_QWeight), ctypes.POINTER(_QWeight), P,
+                                          P, i32, i32, i32, i32, i32, i32, i32, P, P,
+                                          ctypes.POINTER(_Perm), P, P, P, P]
         L.moe_ffn_fwd_lora.argtypes = [ctypes.POINTER(_QWeight), ctypes.POINTER(_QWeight),
                                        ctypes.POINTER(_Lora), ctypes.POINTER(_Lora), P, P, i32,
                                        i32, i32, i32, i32, i32, i32, P, P, ctypes.POINTER(_Perm),
@@ -108,8 +112,8 @@ def lib():
         L.qgg_status_string.restype = ctypes.c_char_p
         L.qgg_version.restype = ctypes.c_char_p
         for f in ("moe_route", "expert_permute", "dequant_grouped_gemm", "lora_grouped_gemm",
-                  "lora_grouped_gemm_bwd", "moe_ffn_fwd", "moe_ffn_fwd_lora", "moe_dx_bwd",
-                  "moe_router_bwd"):
+                  "lora_grouped_gemm_bwd", "moe_ffn_fwd", "moe_ffn_fwd_noalloc",
+                  "moe_ffn_fwd_lora", "moe_dx_bwd", "moe_router_bwd"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -357,6 +361,32 @@ def moe_ffn_fwd(w_gate_up: QWeight, w_down: QWeight, x, logits, k: int, variant:
                              inter, variant, chunk, _ptr(ids), _ptr(gates), ctypes.byref(pc),
                              _ptr(h), _ptr(err_flag), _ptr(buf), buf.numel(), _ptr(y), _stream()),
            "moe_ffn_fwd")
+    return dict(y=y, topk_ids=ids, topk_gates=gates, perm=p, h=h)
+
+
+STATIC_SCRATCH_BYTES = 32 << 20
+
+
+def moe_ffn_fwd_noalloc(w_gate_up: QWeight, w_down: QWeight, x, logits, k: int,
+                        variant: int = FUSED, chunk: int = 0, save_h: bool = False,
+                        err_flag=None):
+    """moe_ffn_fwd on the library's static scratch (no workspace); same result dict."""
+    import torch
+    T, d = x.shape
+    E = w_gate_up.E
+    inter = w_gate_up.N // 2
+    dev = x.device
+    P = T * k
+    ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+    gates = torch.empty((T, k), dtype=torch.float32, device=dev)
+    p = Perm.empty(P, E, dev)
+    h = torch.empty((P, 2 * inter), dtype=torch.bfloat16, device=dev) if save_h else None
+    y = torch.empty((T, d), dtype=torch.bfloat16, device=dev)
+    g, dn, pc = w_gate_up.c(), w_down.c(), p.c()
+    _check(lib().moe_ffn_fwd_noalloc(ctypes.byref(g), ctypes.byref(dn), _ptr(x), _ptr(logits), T,
+                                     d, E, k, inter, variant, chunk, _ptr(ids), _ptr(gates),
+                                     ctypes.byref(pc), _ptr(h), _ptr(err_flag), _ptr(y),
+                                     _stream()), "moe_ffn_fwd_noalloc")
     return dict(y=y, topk_ids=ids, topk_gates=gates, perm=p, h=h)
 
 

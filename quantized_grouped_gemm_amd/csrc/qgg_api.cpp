@@ -133,6 +133,38 @@ int chunk_iterations(int E, int64_t P, int C) {
 }  // namespace
 }  // namespace qgg
 
+// Library-owned scratch of the allocation-free entry point: one copy per GPU,
+// held until the process ends.  Host code reaches it only through the device
+// address hipGetSymbolAddress returns (the array's name is a host-side stand-in
+// in host code).
+static __device__ __align__(256) uint8_t scratch[QGG_STATIC_SCRATCH_BYTES];
+
+namespace qgg {
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// Device address of `scratch` on the current device, looked up once per device
+// (with that device current) and kept.
+hipError_t static_scratch(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return hipErrorInvalidDevice;
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* ptr = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? ptr : nullptr;
+  });
+  *out = g_scratch_ptr[dev];
+  return g_scratch_err[dev];
+}
+
+}  // namespace
+}  // namespace qgg
+
 using namespace qgg;
 
 extern "C" {
@@ -519,6 +551,24 @@ qgg_status moe_ffn_fwd(const qgg_qweight* w_gate_up, const qgg_qweight* w_down,
   return ffn_forward(w_gate_up, w_down, nullptr, nullptr, x, logits, T, d, E, k, inter, variant,
                      chunk, topk_ids, topk_gates, p, h_save, nullptr, nullptr, err_flag,
                      workspace, ws_bytes, y, stream);
+}
+
+qgg_status moe_ffn_fwd_noalloc(const qgg_qweight* w_gate_up, const qgg_qweight* w_down,
+                               const uint16_t* x, const float* logits, int T, int d, int E, int k,
+                               int inter, int variant, int chunk, int32_t* topk_ids,
+                               float* topk_gates, const qgg_perm* p, uint16_t* h_save,
+                               int32_t* err_flag, uint16_t* y, qgg_stream_t stream) {
+  if (!valid_route_dims(T, E, k) || d <= 0 || inter <= 0 || chunk < 0) return QGG_ERR_INVALID_ARG;
+  if (variant != QGG_CHUNKED && variant != QGG_FUSED) return QGG_ERR_INVALID_ARG;
+  const size_t need =
+      qgg_workspace_bytes(QGG_CALL_FFN_FWD, T, d, E, k, inter, variant, chunk, nullptr);
+  if (need == 0) return QGG_ERR_INVALID_ARG;
+  if (need > QGG_STATIC_SCRATCH_BYTES) return QGG_ERR_WORKSPACE_TOO_SMALL;
+  void* ws = nullptr;
+  if (static_scratch(&ws) != hipSuccess || !ws) return QGG_ERR_HIP;
+  return ffn_forward(w_gate_up, w_down, nullptr, nullptr, x, logits, T, d, E, k, inter, variant,
+                     chunk, topk_ids, topk_gates, p, h_save, nullptr, nullptr, err_flag, ws,
+                     QGG_STATIC_SCRATCH_BYTES, y, stream);
 }
 
 static bool valid_lora_rank(const qgg_lora* l) {
