@@ -350,6 +350,30 @@ qgg_status qgg_check_weights(const qgg_qweight* w, int32_t* err_flag, qgg_stream
 size_t qgg_workspace_bytes(int call, int T, int d, int E, int k, int N_or_inter, int variant,
                            int chunk, size_t* scratch_bytes);
 
+/* Measurement hook (not part of the path): while `events` is not NULL, each
+ * kernel launch the calling thread makes through this library (every launch
+ * function: routing, permutation, each grouped GEMM, each chunk's dequant,
+ * combine, ...) is bracketed by hipEventRecord(events[2i]) and
+ * hipEventRecord(events[2i+1]) on the call's stream, for the first
+ * `capacity` launches (at most 4096) after this call; events are hipEvent_t
+ * handles the caller created with timing enabled.  qgg_timing_count() gives
+ * the number of launches recorded so far and qgg_timing_kind(i) the kind of
+ * launch i (QGG_KERNEL_*).  Pass NULL to stop.  Not for use while the stream
+ * is being captured into a graph.  Returns QGG_ERR_INVALID_ARG for a
+ * capacity outside [1, 4096]. */
+#define QGG_KERNEL_ROUTE 1
+#define QGG_KERNEL_PERMUTE 2     /* permutation and M-tile plan */
+#define QGG_KERNEL_GEMM 3        /* grouped GEMM y = a W^T */
+#define QGG_KERNEL_GEMM_T 4      /* transposed grouped GEMM y = a W */
+#define QGG_KERNEL_DEQUANT 5     /* one chunk's dequantization (QGG_CHUNKED) */
+#define QGG_KERNEL_COMBINE 6     /* gate-weighted combine / scatter-sum */
+#define QGG_KERNEL_LORA 7
+#define QGG_KERNEL_ROUTER_BWD 8
+#define QGG_KERNEL_OTHER 9
+qgg_status qgg_set_timing_events(void* const* events, int capacity);
+int qgg_timing_count(void);
+int qgg_timing_kind(int i);
+
 /* Human-readable name of a status code (static storage). */
 const char* qgg_status_string(qgg_status s);
 

@@ -43,7 +43,8 @@ EXPORTS = ("moe_route", "expert_permute", "dequant_grouped_gemm", "lora_grouped_
            "lora_grouped_gemm_bwd", "moe_ffn_fwd", "moe_ffn_fwd_noalloc", "moe_ffn_fwd_lora",
            "moe_dx_bwd",
            "moe_router_bwd", "qgg_repack_weights", "qgg_check_weights", "qgg_workspace_bytes",
-           "qgg_status_string", "qgg_version")
+           "qgg_set_timing_events", "qgg_timing_count", "qgg_timing_kind", "qgg_status_string",
+           "qgg_version")
 
 _lib = None
 
@@ -108,6 +109,11 @@ def lib():
         L.qgg_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32,
                                           ctypes.POINTER(ctypes.c_size_t)]
         L.qgg_workspace_bytes.restype = ctypes.c_size_t
+        L.qgg_set_timing_events.argtypes = [P, i32]
+        L.qgg_set_timing_events.restype = ctypes.c_int
+        L.qgg_timing_count.restype = ctypes.c_int
+        L.qgg_timing_kind.argtypes = [i32]
+        L.qgg_timing_kind.restype = ctypes.c_int
         L.qgg_status_string.argtypes = [i32]
         L.qgg_status_string.restype = ctypes.c_char_p
         L.qgg_version.restype = ctypes.c_char_p
@@ -189,6 +195,31 @@ def check_weights(w: "QWeight", err_flag=None):
     _check(lib().qgg_check_weights(ctypes.byref(wc), _ptr(err_flag), _stream()),
            "qgg_check_weights")
     return err_flag
+
+
+_timing_keep = None
+
+
+def set_timing_events(events, capacity: int):
+    """qgg_set_timing_events with a list of 2*capacity recorded-once
+    torch.cuda.Event(enable_timing=True) objects (None stops)."""
+    global _timing_keep
+    if events is None:
+        _timing_keep = None
+        _check(lib().qgg_set_timing_events(None, 0), "qgg_set_timing_events")
+        return
+    arr = (ctypes.c_void_p * len(events))(*[e.cuda_event for e in events])
+    _timing_keep = arr
+    _check(lib().qgg_set_timing_events(ctypes.cast(arr, ctypes.c_void_p), capacity),
+           "qgg_set_timing_events")
+
+
+def timing_count() -> int:
+    return int(lib().qgg_timing_count())
+
+
+def timing_kinds(n: int):
+    return [int(lib().qgg_timing_kind(i)) for i in range(n)]
 
 
 @dataclass

@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 SO = os.path.join(HERE, "libqgg.so")
 SOURCES = ["route_permute.hip", "gemm_nt.hip", "gemm_tn.hip", "dequant_combine.hip", "lora.hip",
-           "qgg_api.cpp"]
+           "qgg_api.cpp", "timing.cpp"]
 ARCH = os.environ.get("QGG_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -193,6 +193,7 @@ __global__ __launch_bounds__(256) void k_check_scales_int4(const uint16_t* __res
 
 hipError_t launch_check_scales(int fmt, const void* scales, int64_t n, int32_t* err,
                                hipStream_t s) {
+  TimedLaunch timed_(kLOther, s);
   if (fmt != 2 || n <= 0) return hipSuccess;
   const dim3 grid((unsigned)std::min<int64_t>((n + 255) / 256, (int64_t)num_cus() * 8));
   hipLaunchKernelGGL(k_check_scales_int4, grid, dim3(256), 0, s,
@@ -203,6 +204,7 @@ hipError_t launch_check_scales(int fmt, const void* scales, int64_t n, int32_t* 
 hipError_t launch_dequant(int fmt, const uint8_t* packed, const void* scales, int layout, int N,
                           int K, const int32_t* active, const int32_t* n_active, int first,
                           int count, bool tiled_out, uint16_t* dst, hipStream_t s) {
+  TimedLaunch timed_(kLDequant, s);
   const int64_t groups = (int64_t)count * N * (K / 32);
   if (groups <= 0) return hipSuccess;
   const dim3 grid((unsigned)std::min<int64_t>((groups + 255) / 256, (int64_t)num_cus() * 32));
@@ -217,6 +219,7 @@ hipError_t launch_dequant(int fmt, const uint8_t* packed, const void* scales, in
 
 hipError_t launch_repack(int fmt, const uint8_t* packed, const void* scales, int E, int N, int K,
                          uint8_t* packed_out, void* scales_out, hipStream_t s) {
+  TimedLaunch timed_(kLOther, s);
   const int64_t total = (int64_t)E * N * (K / 32);
   if (total <= 0) return hipSuccess;
   const dim3 grid((unsigned)((total + 255) / 256));
@@ -231,6 +234,7 @@ hipError_t launch_repack(int fmt, const uint8_t* packed, const void* scales, int
 
 hipError_t launch_combine(const uint16_t* rows, int d, const int32_t* inv_perm,
                           const float* gates, int T, int k, uint16_t* out, hipStream_t s) {
+  TimedLaunch timed_(kLCombine, s);
   if (T == 0) return hipSuccess;
   hipLaunchKernelGGL(k_combine, dim3(T, (d / 8 + 255) / 256), dim3(256), 0, s, rows, d, inv_perm,
                      gates, k, out);

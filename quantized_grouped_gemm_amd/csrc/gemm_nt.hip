@@ -471,6 +471,7 @@ hipError_t launch_nt_m(const GemmArgs& g, int MB, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_gemm_nt(const GemmArgs& g, int MB, hipStream_t s) {
+  TimedLaunch timed_(kLGemm, s);
   switch (g.src) {
     case kSrcBF16: return launch_nt_m<kSrcBF16>(g, MB, s);
     case kSrcMXFP4: return launch_nt_m<kSrcMXFP4>(g, MB, s);

@@ -497,6 +497,7 @@ hipError_t launch_tn_m(const GemmArgs& g, int MB, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_gemm_tn(const GemmArgs& g, int MB, hipStream_t s) {
+  TimedLaunch timed_(kLGemmT, s);
   switch (g.src) {
     case kSrcBF16: return launch_tn_m<kSrcBF16>(g, MB, s);
     case kSrcMXFP4: return launch_tn_m<kSrcMXFP4>(g, MB, s);

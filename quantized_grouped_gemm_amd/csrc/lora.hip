@@ -333,6 +333,7 @@ hipError_t launch_lora_bwd(const uint16_t* x, int K, int N, int E, const int32_t
                            const uint16_t* B, int rank, float alpha, const uint16_t* dy,
                            const uint16_t* u, uint16_t* bt, float* du, uint16_t* dx, float* dA,
                            float* dB, hipStream_t s) {
+  TimedLaunch timed_(kLLora, s);
   if (dx || dA) {
     // du = dY B_e over the sorted rows (zero rows: nothing to form)
     hipLaunchKernelGGL(k_lora_bt, dim3((unsigned)E, N / 64), dim3(256), 0, s, B, N, rank, bt);
@@ -353,6 +354,7 @@ hipError_t launch_lora_bwd(const uint16_t* x, int K, int N, int E, const int32_t
 hipError_t launch_lora_u(const uint16_t* x, int K, const int32_t* perm, int topk, int amode,
                          const int4* tiles, const int32_t* ntiles, int max_tiles, int MB,
                          const uint16_t* A, int rank, float alpha, uint16_t* u, hipStream_t s) {
+  TimedLaunch timed_(kLLora, s);
   if (max_tiles <= 0) return hipSuccess;
   lora_rows_x_wt<uint16_t>(x, K, perm, topk, amode, tiles, ntiles, max_tiles, MB, A, rank, alpha,
                            u, s);

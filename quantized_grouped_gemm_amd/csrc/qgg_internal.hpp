@@ -127,4 +127,21 @@ hipError_t launch_combine(const uint16_t* rows, int d, const int32_t* inv_perm,
 
 int num_cus();
 
+// Measurement hook (qgg_set_timing_events): while the calling thread has
+// events registered, each library launch function brackets its kernels with
+// a pair of them on its stream.  Scopes nest; only the outermost records.
+enum LaunchKind {
+  kLRoute = 1, kLPermute = 2, kLGemm = 3, kLGemmT = 4, kLDequant = 5, kLCombine = 6,
+  kLLora = 7, kLRouterBwd = 8, kLOther = 9
+};
+void timing_begin(int kind, hipStream_t s);
+void timing_end(hipStream_t s);
+struct TimedLaunch {
+  hipStream_t s;
+  TimedLaunch(int kind, hipStream_t st) : s(st) { timing_begin(kind, s); }
+  ~TimedLaunch() { timing_end(s); }
+  TimedLaunch(const TimedLaunch&) = delete;
+  TimedLaunch& operator=(const TimedLaunch&) = delete;
+};
+
 }  // namespace qgg

@@ -400,6 +400,7 @@ __global__ __launch_bounds__(1024) void k_perm_tiny(const int32_t* __restrict__ 
 
 hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* gates,
                         int32_t* err, hipStream_t s) {
+  TimedLaunch timed_(kLRoute, s);
   if (T == 0) return hipSuccess;
   hipLaunchKernelGGL(k_route, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, k, ids, gates,
                      err);
@@ -409,6 +410,7 @@ hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* ids, 
 hipError_t launch_router_bwd(const float* gpart, int nitems, const int32_t* inv_perm,
                              const int32_t* ids, const float* gates, int T, int E, int k,
                              float* dgates, float* dlogits, hipStream_t s) {
+  TimedLaunch timed_(kLRouterBwd, s);
   if (T == 0) return hipSuccess;
   hipLaunchKernelGGL(k_router_bwd, dim3((T + 3) / 4), dim3(256), 0, s, gpart, nitems, inv_perm,
                      ids, gates, T, E, k, dgates, dlogits);
@@ -423,6 +425,7 @@ size_t permute_ws_bytes(int64_t P, int E) {
 hipError_t launch_permute_plan(const int32_t* ids, int64_t P, int E, const PermPtrs& pp,
                                int32_t* err, void* ws, int MT, int C, int4* tiles,
                                int32_t* chunk_first, hipStream_t s) {
+  TimedLaunch timed_(kLPermute, s);
   if (P <= kTiny) {
     hipLaunchKernelGGL(k_perm_tiny, dim3(1), dim3(1024), E * sizeof(int), s, ids, P, E,
                        static_cast<int32_t*>(ws), pp, err, MT, C, tiles, chunk_first);
@@ -448,6 +451,7 @@ hipError_t launch_permute(const int32_t* ids, int64_t P, int E, const PermPtrs& 
 
 hipError_t launch_gather(const uint16_t* x, int d, const PermPtrs& pp, int E, int k, int64_t P,
                          uint16_t* out, hipStream_t s) {
+  TimedLaunch timed_(kLOther, s);
   if (P == 0) return hipSuccess;
   hipLaunchKernelGGL(k_gather_rows, dim3((unsigned)((P + 3) / 4)), dim3(256), 0, s, x, d,
                      pp.perm, pp.offsets, E, k, out);
@@ -456,6 +460,7 @@ hipError_t launch_gather(const uint16_t* x, int d, const PermPtrs& pp, int E, in
 
 hipError_t launch_tile_plan(const PermPtrs& pp, int E, int MT, int C, int4* tiles,
                             int32_t* chunk_first, hipStream_t s) {
+  TimedLaunch timed_(kLPermute, s);
   hipLaunchKernelGGL(k_tile_plan, dim3(1), dim3(1024), 0, s, pp.counts, pp.offsets, pp.active,
                      pp.n_active, MT, C, tiles, chunk_first, E);
   return hipGetLastError();

@@ -24,7 +24,7 @@ def _lib_or_skip():
 def _header_functions():
     src = open(os.path.join(ROOT, "include", "qgg.h")).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:qgg_status|size_t|const char\*)\s+(\w+)\s*\(", src,
+    return sorted(set(re.findall(r"^\s*(?:qgg_status|size_t|int|const char\*)\s+(\w+)\s*\(", src,
                                  flags=re.M)))
 
 
