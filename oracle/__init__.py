@@ -62,6 +62,9 @@ def _L():
                                         P, P, P, P, P]
         lib.oracle_ffn_lora.argtypes = [i32, P, P, P, P, i32, i64, i64, P, i32, P, P, i64, P,
                                         i32, ctypes.c_double, ctypes.c_double, P, P, P, P, P]
+        lib.oracle_ffn_lora_bwd.argtypes = [i32, P, P, P, P, i32, i64, i64, P, P, i32, P, P, i64,
+                                            P, i32, i32, ctypes.c_double, ctypes.c_double, P, P,
+                                            P, P, P, P, P, P, P]
         lib.oracle_silu.argtypes = [ctypes.c_double]
         lib.oracle_silu.restype = ctypes.c_double
         lib.oracle_silu_grad.argtypes = [ctypes.c_double]
@@ -251,6 +254,43 @@ def ffn_lora(fmt, gu, dn, x, ids, gates, toks, lora_gu, lora_dn, alpha_gu, alpha
                                 _p(Bdn), _p(y)),
            "ffn_lora")
     return y
+
+
+def ffn_lora_bwd(fmt, gu, dn, x, dy, ids, gates, toks, lora_gu=None, lora_dn=None):
+    """Backward of the SwiGLU FFN with LoRA adapters for L = <dY, y>, base and
+    gates fixed.  lora_gu = (A [E][r][d], B [E][2I][r], alpha) and lora_dn =
+    (A [E][r][I], B [E][d][r], alpha) BF16 bits, or None.  Returns a dict of
+    double arrays: dx [ntok][d] for the selected tokens, dA_gu, dB_gu, dA_dn,
+    dB_dn (None for an absent adapter; sums over the selected tokens' pairs)."""
+    gu_p, gu_s = gu
+    dn_p, dn_s = dn
+    E, N2, d2 = gu_p.shape
+    d, I = 2 * d2, N2 // 2
+    k = ids.shape[1]
+    toks = np.ascontiguousarray(toks, np.int32)
+    c = lambda a: np.ascontiguousarray(a, np.uint16)  # noqa: E731
+    out = {"dx": np.zeros((toks.size, d), np.float64)}
+    args = []
+    for name, l, K, N in (("gu", lora_gu, d, N2), ("dn", lora_dn, I, d)):
+        if l is None:
+            args.append((0, 0.0, None, None))
+            out["dA_" + name] = out["dB_" + name] = None
+            continue
+        A, B, alpha = l
+        r = A.shape[1]
+        assert A.shape == (E, r, K) and B.shape == (E, N, r)
+        out["dA_" + name] = np.zeros((E, r, K), np.float64)
+        out["dB_" + name] = np.zeros((E, N, r), np.float64)
+        args.append((r, float(alpha), c(A), c(B)))
+    (rg, ag, Ag, Bg), (rd, ad, Ad, Bd) = args
+    _check(_L().oracle_ffn_lora_bwd(fmt, _p(gu_p), _p(gu_s), _p(dn_p), _p(dn_s), E, d, I,
+                                    _p(c(x)), _p(c(dy)), k,
+                                    _p(np.ascontiguousarray(ids, np.int32)),
+                                    _p(np.ascontiguousarray(gates, np.float64)), toks.size,
+                                    _p(toks), rg, rd, ag, ad, _p(Ag), _p(Bg), _p(Ad), _p(Bd),
+                                    _p(out["dx"]), _p(out["dA_gu"]), _p(out["dB_gu"]),
+                                    _p(out["dA_dn"]), _p(out["dB_dn"])), "ffn_lora_bwd")
+    return out
 
 
 def router_bwd(fmt, gu, dn, x, dy, logits, ids, toks):

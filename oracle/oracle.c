@@ -685,3 +685,181 @@ int oracle_ffn_lora(int fmt, const uint8_t* gu_p, const void* gu_s, const uint8_
   free(u);
   return rc;
 }
+
+/* Backward of oracle_ffn_lora for L = <dY, y>, the base and the gates held
+ * fixed: the gradients of both adapters and the input gradient through them
+ * and the frozen base.  Orbit page, opening section: the base stays frozen and
+ * the BF16 adapter is what trains; section 时刻细节: no gradient is formed for
+ * the frozen base.  The pages give no formula for this step; it is the chain
+ * rule through the forward above, per (token, slot) pair with e = ids[t][j],
+ * g = gates[t][j], the forward quantities recomputed in double:
+ *   u_gu = alpha_gu A_gu x,  h = W_gu x + B_gu u_gu,  a = silu(h_g) h_u,
+ *   u_dn = alpha_dn A_dn a,  o = W_dn a + B_dn u_dn,
+ * then, from dO = g dY[t]:
+ *   dB_dn += dO (x) u_dn,  du_dn = B_dn^T dO,  dA_dn += alpha_dn du_dn (x) a,
+ *   da = W_dn^T dO + alpha_dn A_dn^T du_dn,
+ *   dH = [da h_u silu'(h_g) | da silu(h_g)],
+ *   dB_gu += dH (x) u_gu,  du_gu = B_gu^T dH,  dA_gu += alpha_gu du_gu (x) x,
+ *   dXp = W_gu^T dH + alpha_gu A_gu^T du_gu,
+ * and dX[s] = sum over j ascending of dXp[t,j] for the selected tokens.
+ * A null A or B leaves that projection without an adapter.  Shapes: A_gu
+ * [E][r_gu][d], B_gu [E][2I][r_gu], A_dn [E][r_dn][I], B_dn [E][d][r_dn];
+ * outputs (each nullable; the weight gradients are overwritten, zero for
+ * experts no pair uses): dx [ntok][d], dA_gu [E][r_gu][d], dB_gu
+ * [E][2I][r_gu], dA_dn [E][r_dn][I], dB_dn [E][d][r_dn]. */
+int oracle_ffn_lora_bwd(int fmt, const uint8_t* gu_p, const void* gu_s, const uint8_t* dn_p,
+                        const void* dn_s, int E, int64_t d, int64_t I, const uint16_t* x,
+                        const uint16_t* dy, int k, const int32_t* ids, const double* gates,
+                        int64_t ntok, const int32_t* toks, int r_gu, int r_dn, double alpha_gu,
+                        double alpha_dn, const uint16_t* Agu, const uint16_t* Bgu,
+                        const uint16_t* Adn, const uint16_t* Bdn, double* dx, double* dAgu,
+                        double* dBgu, double* dAdn, double* dBdn) {
+  const int has_gu = Agu && Bgu, has_dn = Adn && Bdn;
+  if ((has_gu && r_gu <= 0) || (has_dn && r_dn <= 0)) return 1;
+  const int64_t N2 = 2 * I;
+  const int rmax = (r_gu > r_dn ? r_gu : r_dn) > 0 ? (r_gu > r_dn ? r_gu : r_dn) : 1;
+  float* wgu = (float*)malloc(sizeof(float) * (size_t)(N2 * d));
+  float* wdn = (float*)malloc(sizeof(float) * (size_t)(d * I));
+  double* xr = (double*)malloc(sizeof(double) * (size_t)d);
+  double* h = (double*)malloc(sizeof(double) * (size_t)N2);
+  double* a = (double*)malloc(sizeof(double) * (size_t)I);
+  double* dO = (double*)malloc(sizeof(double) * (size_t)d);
+  double* da = (double*)malloc(sizeof(double) * (size_t)I);
+  double* dH = (double*)malloc(sizeof(double) * (size_t)N2);
+  double* ugu = (double*)malloc(sizeof(double) * (size_t)rmax);
+  double* udn = (double*)malloc(sizeof(double) * (size_t)rmax);
+  double* du = (double*)malloc(sizeof(double) * (size_t)rmax);
+  double* dxp = (double*)malloc(sizeof(double) * (size_t)(ntok * k * d));
+  int rc = (!wgu || !wdn || !xr || !h || !a || !dO || !da || !dH || !ugu || !udn || !du || !dxp)
+               ? 3 : 0;
+  if (dAgu && has_gu) memset(dAgu, 0, sizeof(double) * (size_t)(E * r_gu * d));
+  if (dBgu && has_gu) memset(dBgu, 0, sizeof(double) * (size_t)(E * N2 * r_gu));
+  if (dAdn && has_dn) memset(dAdn, 0, sizeof(double) * (size_t)(E * r_dn * I));
+  if (dBdn && has_dn) memset(dBdn, 0, sizeof(double) * (size_t)(E * d * r_dn));
+  for (int e = 0; e < E && !rc; ++e) {
+    int used = 0;
+    for (int64_t s = 0; s < ntok * k && !used; ++s)
+      used = ids[(int64_t)toks[s / k] * k + s % k] == e;
+    if (!used) continue;
+    const uint8_t* pe;
+    const void* se;
+    expert_ptrs(fmt, gu_p, gu_s, N2, d, e, &pe, &se);
+    rc |= oracle_decode(fmt, pe, se, N2, d, wgu);
+    expert_ptrs(fmt, dn_p, dn_s, d, I, e, &pe, &se);
+    rc |= oracle_decode(fmt, pe, se, d, I, wdn);
+    if (rc) break;
+    const uint16_t* Ag = has_gu ? Agu + (int64_t)e * r_gu * d : NULL;
+    const uint16_t* Bg = has_gu ? Bgu + (int64_t)e * N2 * r_gu : NULL;
+    const uint16_t* Ad = has_dn ? Adn + (int64_t)e * r_dn * I : NULL;
+    const uint16_t* Bd = has_dn ? Bdn + (int64_t)e * d * r_dn : NULL;
+    for (int64_t s = 0; s < ntok * k; ++s) {
+      const int64_t t = toks[s / k];
+      const int64_t j = s % k;
+      if (ids[t * k + j] != e) continue;
+      /* forward */
+      oracle_bf16_to_f64(x + t * d, d, xr);
+#pragma omp parallel for schedule(static)
+      for (int64_t r = 0; r < N2; ++r) h[r] = dot_f64(xr, wgu + r * d, d);
+      if (has_gu) {
+        for (int q = 0; q < r_gu; ++q) {
+          double acc = 0.0;
+          for (int64_t c = 0; c < d; ++c) acc += (double)bf16_to_float(Ag[q * d + c]) * xr[c];
+          ugu[q] = alpha_gu * acc;
+        }
+        for (int64_t r = 0; r < N2; ++r) {
+          double acc = 0.0;
+          for (int q = 0; q < r_gu; ++q) acc += (double)bf16_to_float(Bg[r * r_gu + q]) * ugu[q];
+          h[r] += acc;
+        }
+      }
+      for (int64_t i = 0; i < I; ++i) a[i] = oracle_silu(h[i]) * h[I + i];
+      if (has_dn) {
+        for (int q = 0; q < r_dn; ++q) {
+          double acc = 0.0;
+          for (int64_t i = 0; i < I; ++i) acc += (double)bf16_to_float(Ad[q * I + i]) * a[i];
+          udn[q] = alpha_dn * acc;
+        }
+      }
+      /* backward */
+      const double g = gates[t * k + j];
+      for (int64_t n = 0; n < d; ++n) dO[n] = g * (double)bf16_to_float(dy[t * d + n]);
+#pragma omp parallel for schedule(static)
+      for (int64_t i = 0; i < I; ++i) {
+        double acc = 0.0;
+        for (int64_t n = 0; n < d; ++n) acc += dO[n] * (double)wdn[n * I + i];
+        da[i] = acc;
+      }
+      if (has_dn) {
+        for (int q = 0; q < r_dn; ++q) {
+          double acc = 0.0;
+          for (int64_t n = 0; n < d; ++n) acc += (double)bf16_to_float(Bd[n * r_dn + q]) * dO[n];
+          du[q] = acc;
+        }
+        if (dBdn)
+          for (int64_t n = 0; n < d; ++n)
+            for (int q = 0; q < r_dn; ++q) dBdn[((int64_t)e * d + n) * r_dn + q] += dO[n] * udn[q];
+        if (dAdn)
+          for (int q = 0; q < r_dn; ++q)
+            for (int64_t i = 0; i < I; ++i)
+              dAdn[((int64_t)e * r_dn + q) * I + i] += alpha_dn * du[q] * a[i];
+        for (int64_t i = 0; i < I; ++i) {
+          double acc = 0.0;
+          for (int q = 0; q < r_dn; ++q) acc += (double)bf16_to_float(Ad[q * I + i]) * du[q];
+          da[i] += alpha_dn * acc;
+        }
+      }
+      for (int64_t i = 0; i < I; ++i) {
+        dH[i] = da[i] * h[I + i] * oracle_silu_grad(h[i]);
+        dH[I + i] = da[i] * oracle_silu(h[i]);
+      }
+      double* o = dxp + s * d;
+#pragma omp parallel for schedule(static)
+      for (int64_t c = 0; c < d; ++c) {
+        double acc = 0.0;
+        for (int64_t r = 0; r < N2; ++r) acc += dH[r] * (double)wgu[r * d + c];
+        o[c] = acc;
+      }
+      if (has_gu) {
+        for (int q = 0; q < r_gu; ++q) {
+          double acc = 0.0;
+          for (int64_t r = 0; r < N2; ++r) acc += (double)bf16_to_float(Bg[r * r_gu + q]) * dH[r];
+          du[q] = acc;
+        }
+        if (dBgu)
+          for (int64_t r = 0; r < N2; ++r)
+            for (int q = 0; q < r_gu; ++q)
+              dBgu[((int64_t)e * N2 + r) * r_gu + q] += dH[r] * ugu[q];
+        if (dAgu)
+          for (int q = 0; q < r_gu; ++q)
+            for (int64_t c = 0; c < d; ++c)
+              dAgu[((int64_t)e * r_gu + q) * d + c] += alpha_gu * du[q] * xr[c];
+        for (int64_t c = 0; c < d; ++c) {
+          double acc = 0.0;
+          for (int q = 0; q < r_gu; ++q) acc += (double)bf16_to_float(Ag[q * d + c]) * du[q];
+          o[c] += alpha_gu * acc;
+        }
+      }
+    }
+  }
+  if (!rc && dx) {
+    for (int64_t s = 0; s < ntok; ++s)
+      for (int64_t c = 0; c < d; ++c) {
+        double acc = 0.0;
+        for (int j = 0; j < k; ++j) acc += dxp[(s * k + j) * d + c];
+        dx[s * d + c] = acc;
+      }
+  }
+  free(wgu);
+  free(wdn);
+  free(xr);
+  free(h);
+  free(a);
+  free(dO);
+  free(da);
+  free(dH);
+  free(ugu);
+  free(udn);
+  free(du);
+  free(dxp);
+  return rc;
+}

@@ -554,6 +554,107 @@ def test_ffn_lora_matches_twin_and_reduces_to_ffn(fmt):
     assert not np.array_equal(yg, yf) and not np.array_equal(yg, y)
 
 
+def _twin_ffn_lora_loss(fmt, gu, dn, xf, dyf, ids, gates, ad_gu, ad_dn):
+    """<dY, y> of the SwiGLU FFN with LoRA adapters, numpy float64 (adapters
+    as (A, B, alpha) float arrays, or None)."""
+    T, d = xf.shape
+    I = gu[0].shape[1] // 2
+    total = 0.0
+    for t in range(T):
+        y = np.zeros(d)
+        for j in range(ids.shape[1]):
+            e = ids[t, j]
+            Wg = _decode_bits(fmt, gu[0][e], gu[1][e]).astype(np.float64)
+            Wd = _decode_bits(fmt, dn[0][e], dn[1][e]).astype(np.float64)
+            h = Wg @ xf[t]
+            if ad_gu is not None:
+                A, B, al = ad_gu
+                h = h + B[e] @ (al * (A[e] @ xf[t]))
+            a = h[:I] / (1.0 + np.exp(-h[:I])) * h[I:]
+            o = Wd @ a
+            if ad_dn is not None:
+                A, B, al = ad_dn
+                o = o + B[e] @ (al * (A[e] @ a))
+            y += gates[t, j] * o
+        total += float(dyf[t] @ y)
+    return total
+
+
+@pytest.mark.parametrize("which", ["both", "gate_up", "down"])
+def test_ffn_lora_bwd_matches_finite_differences(which):
+    fmt = 1 if which == "both" else 2
+    T, d, I, E, k = 5, 64, 32, 5, 2
+    gu, dn, x, ids, gates = _tiny_ffn_inputs(fmt, T=T, d=d, I=I, E=E, k=k, seed=12)
+    dy = synth.normal_bf16(12, 5, (T, d))
+    toks = np.arange(T, dtype=np.int32)
+    lgu = (synth.normal_bf16(12, 7, (E, 16, d), std=0.1),
+           synth.normal_bf16(12, 8, (E, 2 * I, 16), std=0.1), 0.5)
+    ldn = (synth.normal_bf16(12, 9, (E, 32, I), std=0.1),
+           synth.normal_bf16(12, 10, (E, d, 32), std=0.1), 0.75)
+    lgu = lgu if which in ("both", "gate_up") else None
+    ldn = ldn if which in ("both", "down") else None
+    g = oracle.ffn_lora_bwd(fmt, gu, dn, x, dy, ids, gates, toks, lgu, ldn)
+    xf, dyf = _bf16_bits_to_f64(x), _bf16_bits_to_f64(dy)
+    f64 = lambda l: None if l is None else (_bf16_bits_to_f64(l[0]), _bf16_bits_to_f64(l[1]), l[2])  # noqa: E731
+    point = {"x": xf, "gu": f64(lgu), "dn": f64(ldn)}
+
+    def loss(pt):
+        return _twin_ffn_lora_loss(fmt, gu, dn, pt["x"], dyf, ids, gates, pt["gu"], pt["dn"])
+
+    def moved(name, V, eps):
+        pt = dict(point)
+        if name == "x":
+            pt["x"] = xf + eps * V
+        else:
+            side, part = name[-2:], name[1]            # dA_gu -> ("gu", "A")
+            A, B, al = pt[side]
+            pt[side] = (A + eps * V, B, al) if part == "A" else (A, B + eps * V, al)
+        return pt
+
+    rng = np.random.default_rng(13)
+    eps = 1e-4
+    names = ["dx"] + [f"d{p}_{s}" for s in ("gu", "dn") for p in "AB"
+                      if point[s] is not None]
+    for name in names:
+        grad = g[name]
+        for _ in range(3):
+            V = rng.standard_normal(grad.shape)
+            key = "x" if name == "dx" else name
+            fd = (loss(moved(key, V, eps)) - loss(moved(key, V, -eps))) / (2 * eps)
+            an = float(np.sum(grad * V))
+            assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), (which, name, fd, an)
+    # experts no pair uses get zero adapter gradients
+    unused = sorted(set(range(E)) - set(ids.reshape(-1).tolist()))
+    for name in names[1:]:
+        for e in unused:
+            assert np.all(g[name][e] == 0)
+
+
+def test_ffn_lora_bwd_special_cases():
+    T, d, I, E, k = 4, 64, 32, 4, 2
+    gu, dn, x, ids, gates = _tiny_ffn_inputs(1, T=T, d=d, I=I, E=E, k=k, seed=14)
+    dy = synth.normal_bf16(14, 5, (T, d))
+    toks = np.arange(T, dtype=np.int32)
+    A1 = synth.normal_bf16(14, 7, (E, 16, d), std=0.1)
+    B1 = synth.normal_bf16(14, 8, (E, 2 * I, 16), std=0.1)
+    A2 = synth.normal_bf16(14, 9, (E, 16, I), std=0.1)
+    B2 = synth.normal_bf16(14, 10, (E, d, 16), std=0.1)
+    # alpha = 0: the adapters are inert, dx is the frozen-base backward and
+    # every adapter gradient is exactly zero
+    g = oracle.ffn_lora_bwd(1, gu, dn, x, dy, ids, gates, toks, (A1, B1, 0.0), (A2, B2, 0.0))
+    dx0, _ = oracle.dx(1, gu, dn, x, dy, ids, gates, toks)
+    np.testing.assert_allclose(g["dx"], dx0, rtol=1e-12, atol=1e-12)
+    for name in ("dA_gu", "dB_gu", "dA_dn", "dB_dn"):
+        assert np.all(g[name] == 0), name
+    # B = 0: the adapters add nothing to the forward, so dx is again the base
+    # one and dA (which goes through B) is zero; dB is not
+    z1, z2 = np.zeros_like(B1), np.zeros_like(B2)
+    g = oracle.ffn_lora_bwd(1, gu, dn, x, dy, ids, gates, toks, (A1, z1, 0.5), (A2, z2, 0.5))
+    np.testing.assert_allclose(g["dx"], dx0, rtol=1e-12, atol=1e-12)
+    assert np.all(g["dA_gu"] == 0) and np.all(g["dA_dn"] == 0)
+    assert np.any(g["dB_gu"] != 0) and np.any(g["dB_dn"] != 0)
+
+
 # ------------------------------------------------------------ router backward
 
 def _twin_pair_outputs(fmt, gu, dn, xf, ids, t):
