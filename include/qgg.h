@@ -83,6 +83,7 @@ typedef int qgg_status;
 #define QGG_CALL_FFN_FWD 3
 #define QGG_CALL_DX_BWD 4
 #define QGG_CALL_LORA_BWD 5   /* d = N, N_or_inter = adapter rank */
+#define QGG_CALL_FFN_LORA_BWD 6   /* N_or_inter = inter; adapters up to rank 128 */
 
 /* Storage layouts of the packed weights and scales (the bytes are the same,
  * only their order differs):
@@ -300,6 +301,44 @@ qgg_status moe_dx_bwd(const qgg_qweight* w_gate_up, const qgg_qweight* w_down,
                       const uint16_t* h_saved, int T, int d, int E, int k, int inter, int variant,
                       int chunk, void* workspace, size_t ws_bytes, uint16_t* dx,
                       qgg_stream_t stream);
+
+/* moe_ffn_bwd_lora -- backward of moe_ffn_fwd_lora for L = <dY, y>: the base
+ * frozen and the gates constant, the BF16 adapters trained (Orbit page,
+ * opening section: the low-precision base stays frozen and the BF16 adapter
+ * on top of it is what trains, in training as in rollout; section 时刻细节:
+ * the backward forms no gradient for the frozen base).  Per routed pair with
+ * gate g, dO = g dY[t]:
+ *   down adapter   du = dO . B_dn (fp32); dA_down[e] = alpha_dn sum du (x) a,
+ *                  a = silu(h_gate) h_up recomputed from h_saved;
+ *                  dB_down[e] = sum dO (x) u_down;
+ *                  its share of dA, alpha_dn du . A_dn, is added to
+ *                  dO . W_down before the SwiGLU derivative;
+ *   dH = [dA * up * silu'(gate) | dA * silu(gate)] from h_saved;
+ *   gate_up adapter  du = dH . B_gu (fp32); dA_gate_up[e] = alpha_gu sum du (x)
+ *                  x[t]; dB_gate_up[e] = sum dH (x) u_gate_up;
+ *                  its share of dXp, alpha_gu du . A_gu, is added to dH . W_gu;
+ *   dx[t] = sum_j dXp[pair(t, j)] (fp32, ascending j; the two shares of a
+ *   pair added first).
+ * Sums over an expert's rows run in sorted order; experts with no rows get
+ * zero gradients.  Arguments: the weights and adapters given to
+ * moe_ffn_fwd_lora (either adapter NULL, not both), x [T][d] (its input;
+ * needed for dA_gate_up), dy [T][d] BF16, topk_gates and p from that call,
+ * h_saved [P][2*inter] and u_gate_up / u_down [P][rank] as it wrote them.
+ * Outputs, each nullable (at least one): dx [T][d] BF16, dA_gate_up
+ * [E][r][d], dB_gate_up [E][2*inter][r], dA_down [E][r][inter], dB_down
+ * [E][d][r] fp32 (written in full).  Same shape limits as moe_dx_bwd; ranks
+ * as moe_ffn_fwd_lora.  workspace: qgg_workspace_bytes(QGG_CALL_FFN_LORA_BWD,
+ * T, d, E, k, inter, variant, chunk).  The CHUNKED variant runs every chunk's
+ * down projection before any chunk's gate_up (the gate_up adapter needs all
+ * of dH); scratch stays one chunk.  Deterministic. */
+qgg_status moe_ffn_bwd_lora(const qgg_qweight* w_gate_up, const qgg_qweight* w_down,
+                            const qgg_lora* lora_gate_up, const qgg_lora* lora_down,
+                            const uint16_t* x, const uint16_t* dy, const float* topk_gates,
+                            const qgg_perm* p, const uint16_t* h_saved,
+                            const uint16_t* u_gate_up, const uint16_t* u_down, int T, int d,
+                            int E, int k, int inter, int variant, int chunk, void* workspace,
+                            size_t ws_bytes, uint16_t* dx, float* dA_gate_up, float* dB_gate_up,
+                            float* dA_down, float* dB_down, qgg_stream_t stream);
 
 /* moe_router_bwd -- the gradient a trainable router receives through the
  * frozen base: L = <dY, y> of moe_ffn_fwd differentiated with respect to the

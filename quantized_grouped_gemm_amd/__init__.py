@@ -35,13 +35,14 @@ CALL_GEMM = 2
 CALL_FFN_FWD = 3
 CALL_DX_BWD = 4
 CALL_LORA_BWD = 5
+CALL_FFN_LORA_BWD = 6
 
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "workspace too small", 4: "HIP error"}
 
 # Every symbol include/qgg.h declares.
 EXPORTS = ("moe_route", "expert_permute", "dequant_grouped_gemm", "lora_grouped_gemm",
            "lora_grouped_gemm_bwd", "moe_ffn_fwd", "moe_ffn_fwd_noalloc", "moe_ffn_fwd_lora",
-           "moe_dx_bwd",
+           "moe_dx_bwd", "moe_ffn_bwd_lora",
            "moe_router_bwd", "qgg_repack_weights", "qgg_check_weights", "qgg_workspace_bytes",
            "qgg_set_timing_events", "qgg_timing_count", "qgg_timing_kind", "qgg_status_string",
            "qgg_version")
@@ -99,6 +100,10 @@ def lib():
         L.moe_dx_bwd.argtypes = [ctypes.POINTER(_QWeight), ctypes.POINTER(_QWeight), P, P,
                                  ctypes.POINTER(_Perm), P, i32, i32, i32, i32, i32, i32, i32, P,
                                  sz, P, P]
+        L.moe_ffn_bwd_lora.argtypes = [ctypes.POINTER(_QWeight), ctypes.POINTER(_QWeight),
+                                       ctypes.POINTER(_Lora), ctypes.POINTER(_Lora), P, P, P,
+                                       ctypes.POINTER(_Perm), P, P, P, i32, i32, i32, i32, i32,
+                                       i32, i32, P, sz, P, P, P, P, P, P]
         L.moe_router_bwd.argtypes = [ctypes.POINTER(_QWeight), ctypes.POINTER(_QWeight), P, P, P,
                                      ctypes.POINTER(_Perm), P, i32, i32, i32, i32, i32, i32, i32,
                                      P, sz, P, P, P, P]
@@ -119,7 +124,7 @@ def lib():
         L.qgg_version.restype = ctypes.c_char_p
         for f in ("moe_route", "expert_permute", "dequant_grouped_gemm", "lora_grouped_gemm",
                   "lora_grouped_gemm_bwd", "moe_ffn_fwd", "moe_ffn_fwd_noalloc",
-                  "moe_ffn_fwd_lora", "moe_dx_bwd", "moe_router_bwd"):
+                  "moe_ffn_fwd_lora", "moe_dx_bwd", "moe_ffn_bwd_lora", "moe_router_bwd"):
             getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -477,6 +482,52 @@ def moe_dx_bwd(w_gate_up: QWeight, w_down: QWeight, dy, topk_gates, perm: Perm, 
                             ctypes.byref(pc), _ptr(h_saved), T, d, E, k, inter, variant, chunk,
                             _ptr(buf), buf.numel(), _ptr(dx), _stream()), "moe_dx_bwd")
     return dx
+
+
+def moe_ffn_bwd_lora(w_gate_up: QWeight, w_down: QWeight, lora_gate_up, lora_down, x, dy,
+                     topk_gates, perm: Perm, h_saved, u_gate_up, u_down, k: int,
+                     variant: int = FUSED, chunk: int = 0,
+                     want=("dx", "dA_gate_up", "dB_gate_up", "dA_down", "dB_down"),
+                     ws: Workspace | None = None):
+    """Backward of moe_ffn_fwd_lora: {"dx": [T, d] BF16, "dA_gate_up": [E, r, d],
+    "dB_gate_up": [E, 2I, r], "dA_down": [E, r, I], "dB_down": [E, d, r]} (fp32;
+    those in `want` whose adapter is given, else None).  lora_gate_up /
+    lora_down are (A, B, alpha) tuples as for moe_ffn_fwd_lora, or None."""
+    import torch
+    T, d = dy.shape
+    E = w_gate_up.E
+    inter = w_gate_up.N // 2
+    dev = dy.device
+
+    def grad(name, l, shape_of):
+        if l is None or name not in want:
+            return None
+        return torch.empty(shape_of(l), dtype=torch.float32, device=dev)
+
+    dx = torch.empty((T, d), dtype=torch.bfloat16, device=dev) if "dx" in want else None
+    dAg = grad("dA_gate_up", lora_gate_up, lambda l: tuple(l[0].shape))
+    dBg = grad("dB_gate_up", lora_gate_up, lambda l: tuple(l[1].shape))
+    dAd = grad("dA_down", lora_down, lambda l: tuple(l[0].shape))
+    dBd = grad("dB_down", lora_down, lambda l: tuple(l[1].shape))
+
+    def adapter(l):
+        if l is None:
+            return None
+        A, B, alpha = l
+        return _Lora(A.shape[1], float(alpha), A.data_ptr(), B.data_ptr())
+
+    lg, ld = adapter(lora_gate_up), adapter(lora_down)
+    nb, _ = workspace_bytes(CALL_FFN_LORA_BWD, T, d, E, k, inter, variant, chunk)
+    buf = (ws or _default_ws).get(nb, dev)
+    g, dn, pc = w_gate_up.c(), w_down.c(), perm.c()
+    _check(lib().moe_ffn_bwd_lora(ctypes.byref(g), ctypes.byref(dn),
+                                  ctypes.byref(lg) if lg else None,
+                                  ctypes.byref(ld) if ld else None, _ptr(x), _ptr(dy),
+                                  _ptr(topk_gates), ctypes.byref(pc), _ptr(h_saved),
+                                  _ptr(u_gate_up), _ptr(u_down), T, d, E, k, inter, variant,
+                                  chunk, _ptr(buf), buf.numel(), _ptr(dx), _ptr(dAg), _ptr(dBg),
+                                  _ptr(dAd), _ptr(dBd), _stream()), "moe_ffn_bwd_lora")
+    return {"dx": dx, "dA_gate_up": dAg, "dB_gate_up": dBg, "dA_down": dAd, "dB_down": dBd}
 
 
 def moe_router_bwd(w_gate_up: QWeight, w_down: QWeight, dy, topk_ids, topk_gates, perm: Perm,

@@ -133,9 +133,11 @@ __global__ __launch_bounds__(256) void k_repack(const uint8_t* __restrict__ pack
 }
 
 // out[t][:] = sum over j ascending of w_j * rows[inv_perm[t*k+j]][:], fp32
-// accumulation, BF16 out.  Grid (T, d / 2048): each thread owns 8 columns of
-// one token and issues its k row loads together.
-__global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ rows, int d,
+// accumulation, BF16 out; with rows2, each term is w_j * (rows + rows2) of
+// that sorted row (the two added in fp32 first).  Grid (T, d / 2048): each
+// thread owns 8 columns of one token and issues its k row loads together.
+__global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ rows,
+                                                 const uint16_t* __restrict__ rows2, int d,
                                                  const int32_t* __restrict__ inv_perm,
                                                  const float* __restrict__ gates, int k,
                                                  uint16_t* __restrict__ out) {
@@ -156,6 +158,28 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ ro
       w[b] = src < 0 ? 0.f : (gates ? gates[t * k + j] : 1.0f);
       v[b] = src < 0 ? u32x4_t{0u, 0u, 0u, 0u}
                      : reinterpret_cast<const u32x4_t*>(rows + (int64_t)src * d)[c];
+    }
+    if (rows2) {
+      u32x4_t v2[kB];
+#pragma unroll
+      for (int b = 0; b < kB; ++b) {
+        const int j = j0 + b;
+        const int src = j < k ? inv_perm[t * k + j] : -1;
+        v2[b] = src < 0 ? u32x4_t{0u, 0u, 0u, 0u}
+                        : reinterpret_cast<const u32x4_t*>(rows2 + (int64_t)src * d)[c];
+      }
+#pragma unroll
+      for (int b = 0; b < kB; ++b) {
+        if (j0 + b >= k) break;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float lo = bf16_to_f32(v[b][i] & 0xFFFFu) + bf16_to_f32(v2[b][i] & 0xFFFFu);
+          const float hi = bf16_to_f32(v[b][i] >> 16) + bf16_to_f32(v2[b][i] >> 16);
+          acc[2 * i] = __builtin_fmaf(w[b], lo, acc[2 * i]);
+          acc[2 * i + 1] = __builtin_fmaf(w[b], hi, acc[2 * i + 1]);
+        }
+      }
+      continue;
     }
 #pragma unroll
     for (int b = 0; b < kB; ++b) {
@@ -233,11 +257,45 @@ hipError_t launch_repack(int fmt, const uint8_t* packed, const void* scales, int
 }
 
 hipError_t launch_combine(const uint16_t* rows, int d, const int32_t* inv_perm,
-                          const float* gates, int T, int k, uint16_t* out, hipStream_t s) {
+                          const float* gates, int T, int k, uint16_t* out, hipStream_t s,
+                          const uint16_t* rows2) {
   TimedLaunch timed_(kLCombine, s);
   if (T == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_combine, dim3(T, (d / 8 + 255) / 256), dim3(256), 0, s, rows, d, inv_perm,
-                     gates, k, out);
+  hipLaunchKernelGGL(k_combine, dim3(T, (d / 8 + 255) / 256), dim3(256), 0, s, rows, rows2, d,
+                     inv_perm, gates, k, out);
+  return hipGetLastError();
+}
+
+// a[i][c] = silu(h[i][c]) * h[i][inter + c] for the sorted rows i < offsets[E]
+// (BF16 in and out, fp32 arithmetic): the SwiGLU output recomputed from the
+// saved h.  One thread per 8 columns.
+__global__ __launch_bounds__(256) void k_swiglu_act(const uint16_t* __restrict__ h, int inter,
+                                                    const int32_t* __restrict__ nrows_p,
+                                                    uint16_t* __restrict__ a) {
+  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int per = inter / 8;
+  const int64_t i = q / per;
+  const int c = (int)(q % per) * 8;
+  if (i >= *nrows_p) return;
+  const u32x4_t g = *reinterpret_cast<const u32x4_t*>(h + i * 2 * inter + c);
+  const u32x4_t u = *reinterpret_cast<const u32x4_t*>(h + i * 2 * inter + inter + c);
+  uint32_t o[4];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const float g0 = bf16_to_f32(g[w] & 0xFFFFu), g1 = bf16_to_f32(g[w] >> 16);
+    const float u0 = bf16_to_f32(u[w] & 0xFFFFu), u1 = bf16_to_f32(u[w] >> 16);
+    o[w] = pack_bf16x2(silu_f32(g0) * u0, silu_f32(g1) * u1);
+  }
+  *reinterpret_cast<u32x4_t*>(a + i * inter + c) = u32x4_t{o[0], o[1], o[2], o[3]};
+}
+
+hipError_t launch_swiglu_act(const uint16_t* h, int inter, const int32_t* offsets, int E,
+                             int64_t P, uint16_t* a, hipStream_t s) {
+  TimedLaunch timed_(kLOther, s);
+  const int64_t n = P * (inter / 8);
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_swiglu_act, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, h, inter,
+                     offsets + E, a);
   return hipGetLastError();
 }
 

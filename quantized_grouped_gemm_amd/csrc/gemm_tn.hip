@@ -375,12 +375,20 @@ __device__ __forceinline__ void gemm_tn_item(const GemmArgs& g, const LdsRing4& 
           for (int e = 0; e < 4; ++e) v[4 * q + e] = x[e];
         }
         if constexpr (EPI == kEpiSwiGLUBwd) {
-          // v = (dY . W_down)[c]; dA = g * v; h_saved holds [gate | up]
+          // v = (dY . W_down)[c]; dA = g * v (+ the adapter's share when
+          // lora_da is given); h_saved holds [gate | up]
           const float gate = Gl[r];
           const int64_t hb = orow * 2 * (int64_t)g.inter + ecol;
           const u32x4_t* hgp = reinterpret_cast<const u32x4_t*>(g.h + hb);
           const u32x4_t* hup = reinterpret_cast<const u32x4_t*>(g.h + hb + g.inter);
           const u32x4_t hg2[2] = {hgp[0], hgp[1]}, hu2[2] = {hup[0], hup[1]};
+          u32x4_t ld2[2] = {u32x4_t{0u, 0u, 0u, 0u}, u32x4_t{0u, 0u, 0u, 0u}};
+          if (g.lora_da) {
+            const u32x4_t* lp = reinterpret_cast<const u32x4_t*>(
+                g.lora_da + orow * (int64_t)g.inter + ecol);
+            ld2[0] = lp[0];
+            ld2[1] = lp[1];
+          }
           uint32_t og[8], ou[8];
           float gp = 0.f;   // this thread's 16 terms of <dY . W_down, a>
 #pragma unroll
@@ -392,7 +400,9 @@ __device__ __forceinline__ void gemm_tn_item(const GemmArgs& g, const LdsRing4& 
               const uint32_t wu = hu2[(e + h2) >> 3][((e + h2) & 7) >> 1];
               const float hg = bf16_to_f32(((e + h2) & 1) ? (wg >> 16) : (wg & 0xFFFFu));
               const float hu = bf16_to_f32(((e + h2) & 1) ? (wu >> 16) : (wu & 0xFFFFu));
-              const float da = gate * v[e + h2];
+              const uint32_t wl = ld2[(e + h2) >> 3][((e + h2) & 7) >> 1];
+              const float da = gate * v[e + h2] +
+                               bf16_to_f32(((e + h2) & 1) ? (wl >> 16) : (wl & 0xFFFFu));
               const float sg = 1.0f / (1.0f + __expf(-hg));
               const float dsilu = sg * (1.0f + hg * (1.0f - sg));
               rg[h2] = da * hu * dsilu;

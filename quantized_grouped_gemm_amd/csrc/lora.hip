@@ -293,6 +293,23 @@ __global__ __launch_bounds__(256) void k_lora_wgrad(const LT* __restrict__ L, in
         }
 }
 
+// du[i][:] *= g_i and us[i][:] = g_i * u[i][:] with g_i = gates[perm[i]], for
+// the sorted rows i < offsets[E]: the gate of a pair scales the upstream
+// gradient of its down-projection adapter (fp32).
+__global__ __launch_bounds__(256) void k_gate_rows(float* __restrict__ du,
+                                                   const uint16_t* __restrict__ u,
+                                                   float* __restrict__ us, int rank,
+                                                   const int32_t* __restrict__ perm,
+                                                   const float* __restrict__ gates,
+                                                   const int32_t* __restrict__ nrows_p) {
+  const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t i = q / rank;
+  if (i >= *nrows_p) return;
+  const float g = gates[perm[i]];
+  du[q] *= g;
+  if (u) us[q] = g * bf16_to_f32(u[q]);
+}
+
 template <typename LT, bool TRANS_OUT>
 void launch_wgrad(const LT* L, int rank, const uint16_t* Rm, int C, int E,
                   const int32_t* offsets, const int32_t* perm, int topk, int amode, float scale,
@@ -348,6 +365,33 @@ hipError_t launch_lora_bwd(const uint16_t* x, int K, int N, int E, const int32_t
     if (dA) launch_wgrad<float, false>(du, rank, x, K, E, offsets, perm, topk, amode, alpha, dA, s);
   }
   if (dB) launch_wgrad<uint16_t, true>(u, rank, dy, N, E, offsets, perm, 1, kASorted, 1.0f, dB, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_lora_bwd_gated(const uint16_t* a, int K, int N, int E, const int32_t* perm,
+                                 int topk, const float* gates, const int32_t* offsets,
+                                 const int4* tiles, const int32_t* ntiles, int max_tiles, int MB,
+                                 const uint16_t* A, const uint16_t* B, int rank, float alpha,
+                                 const uint16_t* dy, const uint16_t* u, uint16_t* bt, float* du,
+                                 float* us, uint16_t* dx, float* dA, float* dB, int64_t P,
+                                 hipStream_t s) {
+  TimedLaunch timed_(kLLora, s);
+  if (max_tiles > 0) {
+    // du = g * (dY[token] . B_e) per sorted row; us = g * u for dB
+    hipLaunchKernelGGL(k_lora_bt, dim3((unsigned)E, N / 64), dim3(256), 0, s, B, N, rank, bt);
+    lora_rows_x_wt<float>(dy, N, perm, topk, kATokens, tiles, ntiles, max_tiles, MB, bt, rank,
+                          1.0f, du, s);
+    const int64_t n = P * rank;
+    hipLaunchKernelGGL(k_gate_rows, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, du,
+                       dB ? u : nullptr, us, rank, perm, gates, offsets + E);
+    if (dx)
+      hipLaunchKernelGGL(k_lora_dx, dim3((unsigned)(max_tiles * MB), (K + 255) / 256), dim3(256),
+                         (size_t)rank * 512, s, du, tiles, ntiles, MB, A, rank, K, alpha, dx);
+  }
+  // weight gradients: the kernels run even with no routed rows, so dA and dB
+  // are written in full (zeros)
+  if (dA) launch_wgrad<float, false>(du, rank, a, K, E, offsets, perm, 1, kASorted, alpha, dA, s);
+  if (dB) launch_wgrad<float, true>(us, rank, dy, N, E, offsets, perm, topk, kATokens, 1.0f, dB, s);
   return hipGetLastError();
 }
 

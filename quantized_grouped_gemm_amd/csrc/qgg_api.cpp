@@ -29,6 +29,7 @@ int num_cus() {
 namespace {
 
 constexpr size_t kAlign = 256;
+constexpr int kMaxLoraRank = 128;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 // Bump allocator over the caller's workspace.
@@ -211,6 +212,9 @@ qgg_status qgg_check_weights(const qgg_qweight* w, int32_t* err_flag, qgg_stream
 //  FFN_FWD  segment counts | plan | a [P][inter] | o [P][d] | scratch
 //  DX_BWD   plan | dH [P][2*inter] | dXp [P][d] | scratch | gate partials [P][inter/256] fp32
 //  LORA_BWD plan | du [P][rank] fp32 | B transposed [E][rank][N] BF16
+//  FFN_LORA_BWD  DX_BWD's pieces | a [P][inter] | down adapter's dA share
+//           [P][inter] | gate_up adapter's dXp share [P][d] | du, us [P][128] fp32
+//           | B transposed [E][128][max(d, 2 inter)] BF16
 size_t qgg_workspace_bytes(int call, int T, int d, int E, int k, int N_or_inter, int variant,
                            int chunk, size_t* scratch_bytes) {
   if (scratch_bytes) *scratch_bytes = 0;
@@ -244,7 +248,8 @@ size_t qgg_workspace_bytes(int call, int T, int d, int E, int k, int N_or_inter,
       cv.take<char>((size_t)P * N_or_inter * 4);
       cv.take<char>((size_t)E * N_or_inter * d * 2);
       break;
-    case QGG_CALL_DX_BWD: {
+    case QGG_CALL_DX_BWD:
+    case QGG_CALL_FFN_LORA_BWD: {
       const int64_t I = N_or_inter;
       carve_plan(cv, P, E, pl);
       cv.take<char>((size_t)P * 2 * I * 2);
@@ -252,6 +257,14 @@ size_t qgg_workspace_bytes(int call, int T, int d, int E, int k, int N_or_inter,
       if (variant == QGG_CHUNKED) scratch = (size_t)C * 2 * I * d * 2;
       cv.take<char>(scratch);
       cv.take<char>((size_t)P * (I / 256 > 0 ? I / 256 : 1) * 4);
+      if (call == QGG_CALL_FFN_LORA_BWD) {
+        cv.take<char>((size_t)P * I * 2);
+        cv.take<char>((size_t)P * I * 2);
+        cv.take<char>((size_t)P * d * 2);
+        cv.take<char>((size_t)P * kMaxLoraRank * 4);
+        cv.take<char>((size_t)P * kMaxLoraRank * 4);
+        cv.take<char>((size_t)E * kMaxLoraRank * std::max<int64_t>(d, 2 * I) * 2);
+      }
       break;
     }
     default:
@@ -709,6 +722,138 @@ qgg_status moe_router_bwd(const qgg_qweight* w_gate_up, const qgg_qweight* w_dow
   if (T > 0 && !dgates && !dlogits) return QGG_ERR_INVALID_ARG;
   return backward(w_gate_up, w_down, dy, topk_ids, topk_gates, p, h_saved, T, d, E, k, inter,
                   variant, chunk, workspace, ws_bytes, dx, dgates, dlogits, stream);
+}
+
+qgg_status moe_ffn_bwd_lora(const qgg_qweight* w_gate_up, const qgg_qweight* w_down,
+                            const qgg_lora* lora_gate_up, const qgg_lora* lora_down,
+                            const uint16_t* x, const uint16_t* dy, const float* topk_gates,
+                            const qgg_perm* p, const uint16_t* h_saved,
+                            const uint16_t* u_gate_up, const uint16_t* u_down, int T, int d,
+                            int E, int k, int inter, int variant, int chunk, void* workspace,
+                            size_t ws_bytes, uint16_t* dx, float* dA_gate_up, float* dB_gate_up,
+                            float* dA_down, float* dB_down, qgg_stream_t stream) {
+  const qgg_lora* lgu = lora_gate_up;
+  const qgg_lora* ldn = lora_down;
+  if (!lgu && !ldn) return QGG_ERR_INVALID_ARG;
+  if (!valid_route_dims(T, E, k) || d <= 0 || inter <= 0 || chunk < 0) return QGG_ERR_INVALID_ARG;
+  if (!valid_lora_rank(lgu) || !valid_lora_rank(ldn)) return QGG_ERR_UNSUPPORTED;
+  if ((lgu && (!std::isfinite(lgu->alpha) || !lgu->A || !lgu->B)) ||
+      (ldn && (!std::isfinite(ldn->alpha) || !ldn->A || !ldn->B)))
+    return QGG_ERR_INVALID_ARG;
+  if (!valid_weight(w_gate_up, E, 2 * inter, d) || !valid_weight(w_down, E, d, inter))
+    return QGG_ERR_INVALID_ARG;
+  if (w_gate_up->fmt != w_down->fmt) return QGG_ERR_INVALID_ARG;
+  if (variant != QGG_CHUNKED && variant != QGG_FUSED) return QGG_ERR_INVALID_ARG;
+  if (!valid_perm(p, (int64_t)T * k)) return QGG_ERR_INVALID_ARG;
+  const bool want_gu = lgu && (dA_gate_up || dB_gate_up);
+  const bool want_dn = ldn && (dA_down || dB_down);
+  if (!dx && !want_gu && !want_dn) return QGG_ERR_INVALID_ARG;
+  if (T > 0 && (!dy || !topk_gates || !h_saved)) return QGG_ERR_INVALID_ARG;
+  if (T > 0 && lgu && ((dA_gate_up && !x) || (dB_gate_up && !u_gate_up)))
+    return QGG_ERR_INVALID_ARG;
+  if (T > 0 && ldn && dB_down && !u_down) return QGG_ERR_INVALID_ARG;
+  if (d % 256 || inter % 256) return QGG_ERR_UNSUPPORTED;
+  const int64_t P = (int64_t)T * k;
+  if (!a_fits(T, d) || !a_fits(P, 2 * inter)) return QGG_ERR_UNSUPPORTED;
+  size_t scratch = 0;
+  const size_t need =
+      qgg_workspace_bytes(QGG_CALL_FFN_LORA_BWD, T, d, E, k, inter, variant, chunk, &scratch);
+  if (!workspace || ws_bytes < need) return QGG_ERR_WORKSPACE_TOO_SMALL;
+  const int C = chunk > 0 ? std::min(chunk, E) : (int)std::min<int64_t>(E, std::max<int64_t>(P, 1));
+  Carver cv(workspace);
+  Plan pl;
+  carve_plan(cv, P, E, pl);
+  uint16_t* dh = cv.take<uint16_t>((size_t)P * 2 * inter * 2);
+  uint16_t* dxp = cv.take<uint16_t>((size_t)P * d * 2);
+  uint16_t* sbuf = cv.take<uint16_t>(scratch);
+  cv.take<float>((size_t)P * (inter / 256) * 4);
+  uint16_t* abuf = cv.take<uint16_t>((size_t)P * inter * 2);
+  uint16_t* da_share = cv.take<uint16_t>((size_t)P * inter * 2);
+  uint16_t* dx_share = cv.take<uint16_t>((size_t)P * d * 2);
+  float* du = cv.take<float>((size_t)P * kMaxLoraRank * 4);
+  float* us = cv.take<float>((size_t)P * kMaxLoraRank * 4);
+  uint16_t* bt =
+      cv.take<uint16_t>((size_t)E * kMaxLoraRank * std::max<int64_t>(d, 2 * inter) * 2);
+  const PermPtrs pp = to_ptrs(p);
+  const int32_t* ntiles = pl.chunk_first + E + 1;
+  if (P > 0)
+    QGG_HIP(launch_tile_plan(pp, E, 32 * pl.mb, variant == QGG_CHUNKED ? C : 0, pl.tiles,
+                             pl.chunk_first, stream));
+  const int mt = P > 0 ? (int)pl.cap : 0;
+
+  // the down adapter's share of dA (and its gradients) first: the SwiGLU
+  // derivative in the down GEMM's epilogue needs the whole dA
+  if (ldn) {
+    if (P > 0) QGG_HIP(launch_swiglu_act(h_saved, inter, p->offsets, E, P, abuf, stream));
+    QGG_HIP(launch_lora_bwd_gated(abuf, inter, d, E, p->perm, k, topk_gates, p->offsets,
+                                  pl.tiles, ntiles, mt, pl.mb, ldn->A, ldn->B, ldn->rank,
+                                  ldn->alpha, dy, u_down, bt, du, us, P > 0 ? da_share : nullptr,
+                                  dA_down, dB_down, P, stream));
+  }
+  GemmArgs dn = base_args(w_down, pl);
+  dn.a = dy;
+  dn.lda = d;
+  dn.a_rows = T;
+  dn.amode = kATokens;
+  dn.perm = p->perm;
+  dn.topk = k;
+  dn.y = dh;
+  dn.ldy = 2 * inter;
+  dn.epi = kEpiSwiGLUBwd;
+  dn.inter = inter;
+  dn.h = const_cast<uint16_t*>(h_saved);
+  dn.gates = topk_gates;
+  dn.lora_da = ldn ? da_share : nullptr;
+  GemmArgs gu = base_args(w_gate_up, pl);
+  gu.a = dh;
+  gu.lda = 2 * inter;
+  gu.a_rows = P;
+  gu.amode = kASorted;
+  gu.perm = p->perm;
+  gu.topk = k;
+  gu.y = dxp;
+  gu.ldy = d;
+  gu.epi = kEpiStore;
+  // the gate_up adapter: du = dH . B_gu, its share of dXp, dA, dB
+  auto gate_up_adapter = [&]() {
+    return launch_lora_bwd(x, d, 2 * inter, E, p->perm, k, kATokens, p->offsets, pl.tiles,
+                           ntiles, mt, pl.mb, lgu->A, lgu->B, lgu->rank, lgu->alpha, dh,
+                           u_gate_up, bt, du, dx ? dx_share : nullptr, dA_gate_up, dB_gate_up,
+                           stream);
+  };
+  if (P > 0 && variant == QGG_FUSED) {
+    QGG_HIP(launch_gemm_tn(dn, pl.mb, stream));
+    if (lgu) QGG_HIP(gate_up_adapter());
+    if (dx) QGG_HIP(launch_gemm_tn(gu, pl.mb, stream));
+  } else if (P > 0) {
+    // every chunk's down projection, then the gate_up adapter (it needs all
+    // of dH), then every chunk's gate_up projection; one chunk of scratch
+    const int nch = chunk_iterations(E, P, C);
+    dn.src = gu.src = kSrcBF16;
+    dn.wbf16 = gu.wbf16 = sbuf;
+    dn.max_tiles = gu.max_tiles = (int)pl.cap;
+    for (int c = 0; c < nch; ++c) {
+      dn.range = pl.chunk_first + c;
+      dn.bf16_slot_base = c * C;
+      QGG_HIP(launch_dequant(w_down->fmt, w_down->packed, w_down->scales, w_down->layout, d,
+                             inter, p->active, p->n_active, c * C, C, true, sbuf, stream));
+      QGG_HIP(launch_gemm_tn(dn, pl.mb, stream));
+    }
+    if (lgu) QGG_HIP(gate_up_adapter());
+    for (int c = 0; dx && c < nch; ++c) {
+      gu.range = pl.chunk_first + c;
+      gu.bf16_slot_base = c * C;
+      QGG_HIP(launch_dequant(w_gate_up->fmt, w_gate_up->packed, w_gate_up->scales,
+                             w_gate_up->layout, 2 * inter, d, p->active, p->n_active, c * C, C,
+                             true, sbuf, stream));
+      QGG_HIP(launch_gemm_tn(gu, pl.mb, stream));
+    }
+  } else if (lgu) {
+    QGG_HIP(gate_up_adapter());   // no routed rows: zero adapter gradients
+  }
+  if (dx) QGG_HIP(launch_combine(dxp, d, p->inv_perm, nullptr, T, k, dx, stream,
+                                 lgu ? dx_share : nullptr));
+  return QGG_OK;
 }
 
 }  // extern "C"

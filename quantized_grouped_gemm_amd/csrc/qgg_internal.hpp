@@ -55,6 +55,9 @@ struct GemmArgs {
   int lora_rank;
   const uint16_t* lora_u;
   const uint16_t* lora_b;
+  const uint16_t* lora_da;       // bwd SwiGLU epilogue, optional: [P][inter] BF16 sorted,
+                                 // added to g * (dY . W_down) before the SwiGLU
+                                 // derivative (a down adapter's share of dA)
   float* gpart;                  // bwd SwiGLU epilogue, optional: per sorted row and
                                  // 256-column item, sum over the item of
                                  // (dY . W_down)[c] * silu(gate)[c] * up[c]; [P][inter/256]
@@ -121,9 +124,28 @@ hipError_t launch_repack(int fmt, const uint8_t* packed, const void* scales, int
                          uint8_t* packed_out, void* scales_out, hipStream_t s);
 
 // out[t] = sum_j w_j * rows[inv_perm[t*k+j]] (w_j = gates[t*k+j], or 1 when
-// gates is null), fp32 in ascending j, BF16 out.
+// gates is null), fp32 in ascending j, BF16 out; rows2 (nullable) is added to
+// rows term by term.
 hipError_t launch_combine(const uint16_t* rows, int d, const int32_t* inv_perm,
-                          const float* gates, int T, int k, uint16_t* out, hipStream_t s);
+                          const float* gates, int T, int k, uint16_t* out, hipStream_t s,
+                          const uint16_t* rows2 = nullptr);
+// a [P][inter] = silu(h_gate) * h_up from h [P][2 inter] (sorted rows below
+// offsets[E]).
+hipError_t launch_swiglu_act(const uint16_t* h, int inter, const int32_t* offsets, int E,
+                             int64_t P, uint16_t* a, hipStream_t s);
+// Backward of a down-projection adapter inside the FFN: the upstream gradient
+// of sorted row i is gates[perm[i]] * dy[perm[i] / topk] (token-ordered dy);
+// the adapter's input is a [P][K] (sorted).  du [P][rank] and us [P][rank]
+// fp32 and bt [E][rank][N] BF16 are scratch.  dx [P][K] BF16 (the adapter's
+// share of the input gradient), dA [E][rank][K], dB [E][N][rank] fp32, each
+// nullable.
+hipError_t launch_lora_bwd_gated(const uint16_t* a, int K, int N, int E, const int32_t* perm,
+                                 int topk, const float* gates, const int32_t* offsets,
+                                 const int4* tiles, const int32_t* ntiles, int max_tiles, int MB,
+                                 const uint16_t* A, const uint16_t* B, int rank, float alpha,
+                                 const uint16_t* dy, const uint16_t* u, uint16_t* bt, float* du,
+                                 float* us, uint16_t* dx, float* dA, float* dB, int64_t P,
+                                 hipStream_t s);
 
 int num_cus();
 

@@ -113,3 +113,55 @@ def test_adapter_calls_graph_replays_match_eager():
             t.zero_()
         step()
         sync()
+
+
+def test_ffn_adapter_forward_and_backward_graph_replays_match_eager():
+    cfg = scaled(CONFIGS["int4_ffn_decode_zipf"], T=48, d=256, E=40, k=4, N=512, inter=256,
+                 chunks=(4,), name="int4_zipf_lora_graph")
+    rank = 16
+    print(f"case {cfg.name} rank {rank}", flush=True)
+    logits = torch.from_numpy(synth.configs.router_logits(cfg)).to(DEV)
+    x = dev_bf16(synth.configs.activations(cfg))
+    dy = dev_bf16(synth.configs.grad_output(cfg))
+    wg = dev_weights(cfg.fmt, *synth.configs.first_weights(cfg), layout=qgg.LAYOUT_MFMA)
+    wd = dev_weights(cfg.fmt, *synth.configs.down_weights(cfg), layout=qgg.LAYOUT_MFMA)
+    I = cfg.inter
+    lg = (dev_bf16(synth.normal_bf16(cfg.seed, 7, (cfg.E, rank, cfg.d), std=0.05)),
+          dev_bf16(synth.normal_bf16(cfg.seed, 8, (cfg.E, 2 * I, rank), std=0.05)), 0.5)
+    ld = (dev_bf16(synth.normal_bf16(cfg.seed, 9, (cfg.E, rank, I), std=0.05)),
+          dev_bf16(synth.normal_bf16(cfg.seed, 10, (cfg.E, cfg.d, rank), std=0.05)), 0.75)
+
+    def step():
+        r = qgg.moe_ffn_fwd_lora(wg, wd, lg, ld, x, logits, cfg.k, qgg.CHUNKED, 4, save_h=True)
+        g = qgg.moe_ffn_bwd_lora(wg, wd, lg, ld, x, dy, r["topk_gates"], r["perm"], r["h"],
+                                 r["u_gate_up"], r["u_down"], cfg.k, qgg.CHUNKED, 4)
+        f = qgg.moe_ffn_bwd_lora(wg, wd, lg, ld, x, dy, r["topk_gates"], r["perm"], r["h"],
+                                 r["u_gate_up"], r["u_down"], cfg.k, qgg.FUSED, 0)
+        return (r["y"], g["dx"], f["dx"], g["dA_gate_up"], g["dB_gate_up"], g["dA_down"],
+                g["dB_down"], f["dA_down"])
+
+    def host(outs):
+        return [host_u16(t) for t in outs[:3]] + [t.cpu().numpy() for t in outs[3:]]
+
+    ref = host(step())
+    sync()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    sync()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        outs = step()
+    names = ("y", "dx", "dx_fused", "dA_gate_up", "dB_gate_up", "dA_down", "dB_down",
+             "dA_down_fused")
+    for rep in range(3):
+        graph.replay()
+        sync()
+        for name, a, b in zip(names, host(outs), ref):
+            np.testing.assert_array_equal(a, b, err_msg=f"{name} replay {rep}")
+        for t in outs:
+            t.zero_()
+        step()
+        sync()

@@ -689,6 +689,111 @@ def test_moe_ffn_fwd_lora_parity(cfg, rank):
     np.testing.assert_array_equal(host_u16(r0["y"]), host_u16(rb["y"]))
 
 
+FFN_LORA_BWD_CASES = [
+    (DX_CASES[0], 16), (DX_CASES[1], 32), (DX_CASES[2], 48),
+    # 32 routed pairs over 40 experts: most experts have no rows
+    (scaled(CONFIGS["int4_ffn_decode_zipf"], T=16, d=256, E=40, k=2, N=512, inter=256,
+            chunks=(4,), kind="bwd", name="int4_lora_bwd_sparse"), 16),
+]
+
+
+GRAD_NORM_TOL = 1e-2   # per expert, ||got - ref||_F / ||ref||_F
+GRAD_MAX_TOL = 5e-2    # per element, floor = RMS of the expert's gradient matrix
+
+
+def _grad_close(got, ref, what):
+    """Adapter weight gradients [E][rows][cols] against the oracle.  Each
+    entry is a sum over the expert's routed rows of products whose factors
+    carry the BF16 rounding of the base weights (an INT4 q*s is rounded once)
+    and of the stored h, dH and du; its error therefore scales with the
+    expert's typical gradient entry, not with that entry (which can be small
+    by cancellation).  A CPU model of exactly those rounding points reproduces
+    the kernels' error to three digits and puts the worst test case at 0.47 %
+    normwise and 3.2 % elementwise under the expert-wide floor (1.6-2.0 % of it
+    from the weights' BF16 rounding alone), while a dropped term, a missing
+    gate or a wrong scale moves the normwise error to 23-980 %.  Experts
+    without rows must be exact zeros."""
+    got = np.asarray(got, np.float64)
+    assert np.all(np.isfinite(got)), f"{what}: non-finite"
+    zero = np.all(ref.reshape(ref.shape[0], -1) == 0, axis=1)
+    assert np.all(got[zero] == 0), f"{what}: nonzero gradient for an expert with no rows"
+    worst_n = worst_m = 0.0
+    for e in np.nonzero(~zero)[0]:
+        nrm = float(np.linalg.norm(got[e] - ref[e]) / np.linalg.norm(ref[e]))
+        floor = float(np.sqrt(np.mean(ref[e] ** 2)))
+        mx = float(np.max(np.abs(got[e] - ref[e]) / np.maximum(np.abs(ref[e]), floor)))
+        worst_n, worst_m = max(worst_n, nrm), max(worst_m, mx)
+    assert worst_n <= GRAD_NORM_TOL, f"{what}: normwise err {worst_n:.3e} > {GRAD_NORM_TOL}"
+    assert worst_m <= GRAD_MAX_TOL, f"{what}: max rel err {worst_m:.3e} > {GRAD_MAX_TOL}"
+    return worst_n, worst_m
+
+
+@pytest.mark.parametrize("cfg,rank", FFN_LORA_BWD_CASES,
+                         ids=lambda v: v.name if hasattr(v, "name") else str(v))
+def test_moe_ffn_bwd_lora_parity(cfg, rank):
+    """The FFN adapter backward against the oracle: dX through the frozen base
+    and both adapters, and both adapters' weight gradients; both adapters, each
+    alone, both variants (bit-identical), both weight layouts."""
+    print(f"case {cfg.name} rank {rank}", flush=True)
+    logits = synth.configs.router_logits(cfg)
+    x = synth.configs.activations(cfg)
+    dy = synth.configs.grad_output(cfg)
+    gu, dn = _ffn_weights(cfg)
+    I = cfg.inter
+    Agu = synth.normal_bf16(cfg.seed, STREAM["lora_a"], (cfg.E, rank, cfg.d), std=0.05)
+    Bgu = synth.normal_bf16(cfg.seed, STREAM["lora_b"], (cfg.E, 2 * I, rank), std=0.05)
+    Adn = synth.normal_bf16(cfg.seed + 1, STREAM["lora_a"], (cfg.E, rank, I), std=0.05)
+    Bdn = synth.normal_bf16(cfg.seed + 1, STREAM["lora_b"], (cfg.E, cfg.d, rank), std=0.05)
+    ids_ref, gates_ref = oracle.route(logits, cfg.k)
+    toks = np.arange(cfg.T, dtype=np.int32)
+    lt, xd, dyd = torch.from_numpy(logits).to(DEV), dev_bf16(x), dev_bf16(dy)
+    agu = (dev_bf16(Agu), dev_bf16(Bgu), 0.5)
+    adn = (dev_bf16(Adn), dev_bf16(Bdn), 0.75)
+    for which, (lg, ld) in {"both": (agu, adn), "gate_up": (agu, None),
+                            "down": (None, adn)}.items():
+        ref = oracle.ffn_lora_bwd(cfg.fmt, gu, dn, x, dy, ids_ref, gates_ref, toks,
+                                  (Agu, Bgu, 0.5) if lg else None,
+                                  (Adn, Bdn, 0.75) if ld else None)
+        outs = []
+        for layout in LAYOUTS:
+            wg = dev_weights(cfg.fmt, *gu, layout=layout)
+            wd = dev_weights(cfg.fmt, *dn, layout=layout)
+            fwd = qgg.moe_ffn_fwd_lora(wg, wd, lg, ld, xd, lt, cfg.k, qgg.FUSED, 0, save_h=True)
+            for variant, chunk in [(qgg.FUSED, 0), (qgg.CHUNKED, cfg.chunks[0])]:
+                g = qgg.moe_ffn_bwd_lora(wg, wd, lg, ld, xd, dyd, fwd["topk_gates"], fwd["perm"],
+                                         fwd["h"], fwd["u_gate_up"], fwd["u_down"], cfg.k,
+                                         variant, chunk)
+                sync()
+                what = f"{cfg.name} r{rank} {which} L{layout} v{variant}"
+                dxg = host_u16(g["dx"])
+                assert_close(bf16_to_f64(dxg), ref["dx"], what=what + " dx")
+                got = {"dx": dxg}
+                for name, rname in (("dA_gate_up", "dA_gu"), ("dB_gate_up", "dB_gu"),
+                                    ("dA_down", "dA_dn"), ("dB_down", "dB_dn")):
+                    if ref[rname] is None:
+                        assert g[name] is None
+                        continue
+                    got[name] = g[name].cpu().numpy()
+                    _grad_close(got[name], ref[rname], f"{what} {name}")
+                outs.append(got)
+        for o in outs[1:]:
+            for name in o:
+                np.testing.assert_array_equal(o[name], outs[0][name], err_msg=name)
+    # zero scales: dx is the frozen-base backward, bit for bit
+    wg = dev_weights(cfg.fmt, *gu, layout=qgg.LAYOUT_MFMA)
+    wd = dev_weights(cfg.fmt, *dn, layout=qgg.LAYOUT_MFMA)
+    z = ((agu[0], agu[1], 0.0), (adn[0], adn[1], 0.0))
+    fwd = qgg.moe_ffn_fwd_lora(wg, wd, z[0], z[1], xd, lt, cfg.k, qgg.FUSED, 0, save_h=True)
+    g = qgg.moe_ffn_bwd_lora(wg, wd, z[0], z[1], xd, dyd, fwd["topk_gates"], fwd["perm"],
+                             fwd["h"], fwd["u_gate_up"], fwd["u_down"], cfg.k, qgg.FUSED, 0)
+    base = qgg.moe_dx_bwd(wg, wd, dyd, fwd["topk_gates"], fwd["perm"], fwd["h"], cfg.k,
+                          qgg.FUSED, 0)
+    sync()
+    np.testing.assert_array_equal(host_u16(g["dx"]), host_u16(base))
+    for name in ("dA_gate_up", "dA_down", "dB_gate_up", "dB_down"):
+        assert torch.all(g[name] == 0), name
+
+
 def test_empty_batch_every_entry_point():
     """T = 0: every call succeeds; the adapter gradients come back as exact zeros."""
     print("case empty batch", flush=True)
