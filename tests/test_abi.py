@@ -164,6 +164,19 @@ def test_workspace_formulas_backward():
     assert lb >= 4096 * 8 * rank * 4 + 384 * rank * N * 2
 
 
+def test_workspace_formula_ffn_adapter_backward():
+    _lib_or_skip()
+    T, d, E, k, I = 64, 7168, 384, 8, 2048
+    P = T * k
+    base, _ = qgg.workspace_bytes(qgg.CALL_DX_BWD, T, d, E, k, I, qgg.FUSED, 0)
+    lb, _ = qgg.workspace_bytes(qgg.CALL_FFN_LORA_BWD, T, d, E, k, I, qgg.FUSED, 0)
+    # + a and the down share [P][I], the gate_up share [P][d], du and us
+    # [P][128] fp32, B transposed [E][128][max(d, 2I)] BF16
+    assert lb >= base + 2 * P * I * 2 + P * d * 2 + 2 * P * 128 * 4 + E * 128 * max(d, 2 * I) * 2
+    _, s8 = qgg.workspace_bytes(qgg.CALL_FFN_LORA_BWD, T, d, E, k, I, qgg.CHUNKED, 8)
+    assert s8 == 8 * 2 * I * d * 2
+
+
 def test_missing_library_raises(monkeypatch, tmp_path):
     monkeypatch.setattr(qgg, "LIB_PATH", str(tmp_path / "nope.so"))
     monkeypatch.setattr(qgg, "_lib", None)
