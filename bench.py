@@ -222,7 +222,9 @@ def run_ffn_fwd(cfg, args, cpu_budget=None):
     dn_ms = launch_means(per, nth("gemm", 1))
     kern = {}
     for kind in ("route", "permute", "combine"):
-        kern[kind + "_ms"] = round(launch_means(per, nth(kind, 0)), 4)
+        # decode-sized batches route and permute in one launch (kind "route")
+        if any(k == kind for k, _ in per[0]):
+            kern[kind + "_ms"] = round(launch_means(per, nth(kind, 0)), 4)
     kern.update(gate_up_ms=round(gu_ms, 4), down_ms=round(dn_ms, 4))
 
     F = acc.ffn_flops(P, d, I)
