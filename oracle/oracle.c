@@ -345,12 +345,15 @@ static int ffn_pairs(int mode, int fmt, const uint8_t* gu_p, const void* gu_s,
           break;
         }
         for (int64_t n = 0; n < d; ++n) dO[n] = g * (double)bf16_to_float(dy[t * d + n]);
-        /* dA = W_down^T dO */
+        /* dA = W_down^T dO: every dA[i] sums its terms over n ascending;
+           a thread takes 64 consecutive i at a time and runs n outside, so
+           that W_down is read along its rows */
 #pragma omp parallel for schedule(static)
-        for (int64_t i = 0; i < I; ++i) {
-          double acc = 0.0;
-          for (int64_t n = 0; n < d; ++n) acc += dO[n] * (double)wdn[n * I + i];
-          dA[i] = acc;
+        for (int64_t i0 = 0; i0 < I; i0 += 64) {
+          const int64_t i1 = i0 + 64 < I ? i0 + 64 : I;
+          for (int64_t i = i0; i < i1; ++i) dA[i] = 0.0;
+          for (int64_t n = 0; n < d; ++n)
+            for (int64_t i = i0; i < i1; ++i) dA[i] += dO[n] * (double)wdn[n * I + i];
         }
         if (da_out) memcpy(da_out + s * I, dA, sizeof(double) * (size_t)I);
         /* dH = [dA * up * silu'(gate) | dA * silu(gate)] */
@@ -358,12 +361,14 @@ static int ffn_pairs(int mode, int fmt, const uint8_t* gu_p, const void* gu_s,
           a[i] = dA[i] * h[I + i] * oracle_silu_grad(h[i]);
           a[I + i] = dA[i] * oracle_silu(h[i]);
         }
-        /* dXp = W_gu^T dH */
+        /* dXp = W_gu^T dH: every o[c] sums its terms over r ascending
+           (64 consecutive c per thread at a time, r outside, as above) */
 #pragma omp parallel for schedule(static)
-        for (int64_t c = 0; c < d; ++c) {
-          double acc = 0.0;
-          for (int64_t r = 0; r < N2; ++r) acc += a[r] * (double)wgu[r * d + c];
-          o[c] = acc;
+        for (int64_t c0 = 0; c0 < d; c0 += 64) {
+          const int64_t c1 = c0 + 64 < d ? c0 + 64 : d;
+          for (int64_t c = c0; c < c1; ++c) o[c] = 0.0;
+          for (int64_t r = 0; r < N2; ++r)
+            for (int64_t c = c0; c < c1; ++c) o[c] += a[r] * (double)wgu[r * d + c];
         }
         free(dO);
         free(dA);

@@ -62,6 +62,19 @@ def _covering_tokens(pref, T, k, seed, per_expert=8, min_rows=2048):
     return np.nonzero(chosen)[0].astype(np.int32)
 
 
+def _in_slices(fn, toks, what, per=1024):
+    """fn(toks) for slices of `per` tokens, concatenated along axis 0; a line
+    per slice, so that minutes of oracle time still show progress."""
+    outs = []
+    for i in range(0, toks.size, per):
+        outs.append(fn(toks[i:i + per]))
+        if toks.size > per:
+            print(f"  {what}: oracle tokens {i + min(per, toks.size - i)}/{toks.size}", flush=True)
+    if isinstance(outs[0], tuple):
+        return tuple(np.concatenate(parts, axis=0) for parts in zip(*outs))
+    return np.concatenate(outs, axis=0)
+
+
 def _rows_per_expert(pref, toks, k):
     slots = (toks[:, None] * k + np.arange(k)[None, :]).reshape(-1)
     rows = pref["inv_perm"][slots]
@@ -209,7 +222,8 @@ def test_moe_ffn_fwd_full(name):
     short, nrows = _rows_per_expert(pref, toks, cfg.k)
     assert short == 0, "the sample misses rows of an active expert"
     n_tok = toks.size
-    y_ref, h_ref = oracle.ffn(cfg.fmt, gu, dn, x, ids_ref, gates_ref, toks, want_h=True)
+    y_ref, h_ref = _in_slices(lambda t: oracle.ffn(cfg.fmt, gu, dn, x, ids_ref, gates_ref, t,
+                                                   want_h=True), toks, cfg.name)
     e = assert_close(bf16_to_f64(y0[toks]), y_ref, what=f"{cfg.name} y")
     slots = (toks[:, None] * cfg.k + np.arange(cfg.k)[None, :]).reshape(-1)
     assert_close(bf16_to_f64(h0[pref["inv_perm"][slots]]), h_ref, what=f"{cfg.name} h")
@@ -244,7 +258,8 @@ def test_moe_dx_bwd_full():
             else _covering_tokens(pref, cfg.T, cfg.k, seed=2))
     short, nrows = _rows_per_expert(pref, toks, cfg.k)
     assert short == 0, "the sample misses rows of an active expert"
-    dx_ref, _ = oracle.dx(cfg.fmt, gu, dn, x, dy, ids_ref, gates_ref, toks)
+    dx_ref = _in_slices(lambda t: oracle.dx(cfg.fmt, gu, dn, x, dy, ids_ref, gates_ref, t)[0],
+                        toks, "dx")
     e = assert_close(bf16_to_f64(dx0[toks]), dx_ref, what="dx")
     print(f"case dx: {toks.size} tokens ({nrows} routed rows, >= 8 per active expert) checked, "
           f"max rel err {e:.2e}", flush=True)
