@@ -8,11 +8,11 @@
 // here), not along the reduction.
 //
 // Work decomposition: as the forward kernel (persistent grid, XCD-contiguous
-// item ranges, 4 wavefronts x 64 output columns, v_mfma_f32_32x32x16_bf16),
+// item ranges, NW wavefronts x 64 output columns, v_mfma_f32_32x32x16_bf16),
 // with 32 reduction rows (W rows) per stage:
 //  - A (rows of the routed activations) is copied global -> LDS three stages
 //    ahead into a ring of four stage buffers, as in the forward kernel;
-//  - each stage's weight tile (32 W rows x 256 columns) is loaded once per
+//  - each stage's weight tile (32 W rows x 64 NW columns) is loaded once per
 //    workgroup, one 32-element scale group per thread (a single 16-byte load
 //    and one scale), decoded to BF16 and stored row-major in LDS one stage
 //    ahead of use;
@@ -33,19 +33,34 @@ namespace {
 constexpr int kKR = 32;                   // reduction rows per stage
 constexpr int kNBufA = 4;                 // stages in the LDS ring of A tiles
 constexpr int kARowB = kKR * 2;           // A bytes per tile row per stage
-// A stage buffer: MT rows, but at least the 4 KiB one round of 16-byte copies
-// by 256 threads fills
-template <int MB>
-constexpr int a_stage_bytes() { return 32 * MB * kARowB > 4096 ? 32 * MB * kARowB : 4096; }
-// B tile: 32 rows of 256 BF16 columns; the 16-byte piece P of row r is
+// Wavefronts per workgroup (each owns 64 output columns of an item) and
+// workgroups per CU: 128-row tiles of the plain-store form take 512-column
+// items on eight waves, so that every A stage copied into LDS feeds twice the
+// columns.  Shorter tiles, and the SwiGLU-backward form (whose epilogue needs
+// registers the eight-wave build would spill), keep 256-column items and two
+// workgroups per CU.
+template <int MB, int EPI>
+constexpr int tn_waves() { return MB == 4 && EPI == kEpiStore ? 8 : 4; }
+template <int MB, int EPI>
+constexpr int tn_occupancy() { return tn_waves<MB, EPI>() == 8 ? 1 : 2; }
+// A stage buffer: MT rows, but at least what one round of 16-byte copies by
+// the workgroup's threads fills
+template <int MB, int EPI>
+constexpr int a_stage_bytes() {
+  return 32 * MB * kARowB > 1024 * tn_waves<MB, EPI>() ? 32 * MB * kARowB
+                                                        : 1024 * tn_waves<MB, EPI>();
+}
+// B tile: 32 rows of 64 NW BF16 columns; the 16-byte piece P of row r is
 // stored at piece position P ^ swz_b(r).  swz_b takes the 16 values 0..15
 // on any 16 consecutive rows, with rows 4q..4q+3 differing in both bit pairs
 // [2:1] and [3:2]; this keeps the transposing reads (4 rows x 32 bytes per
 // 16 lanes, 4 rows x 64 bytes per 32 lanes) and the row stores (8 or 16 rows
 // x 16 bytes) free of bank conflicts whether a bank cycle serves 128 or 256
 // bytes.
-constexpr int kBRowB = 256 * 2;
-constexpr int kBStage = kKR * kBRowB;
+template <int NW>
+constexpr int b_row_bytes() { return 64 * NW * 2; }
+template <int NW>
+constexpr int b_stage_bytes() { return kKR * b_row_bytes<NW>(); }
 __device__ __forceinline__ int swz_b(int r) {
   return ((0xCA60 >> (4 * (r & 3))) & 15) ^ ((r >> 2) & 1) ^ (((r >> 3) & 1) << 1);
 }
@@ -164,17 +179,20 @@ __device__ __forceinline__ void store_bt(const BGroup<SRC>& b, uint8_t* base, co
 }
 
 
-// One work item: tile (rows [row0, row0 + nrows) of one expert) x 256 output
-// columns starting at c0, NMB live 32-row blocks.  Branch-free like the
-// forward kernel: out-of-range loads are clamped (or read zeros through the
-// buffer bounds) and only the stores are guarded.
+// One work item: tile (rows [row0, row0 + nrows) of one expert) x 64 NW
+// output columns starting at c0, NMB live 32-row blocks.  Branch-free like
+// the forward kernel: out-of-range loads are clamped (or read zeros through
+// the buffer bounds) and only the stores are guarded.
 template <int SRC, int MB, int EPI, int AMODE, int NMB>
 __device__ __forceinline__ void gemm_tn_item(const GemmArgs& g, const LdsRing4& As,
-                                             uint8_t (*Bs)[kBStage], float* Gl, int4 tile,
-                                             int c0) {
+                                             uint8_t (*Bs)[b_stage_bytes<tn_waves<MB, EPI>()>()],
+                                             float* Gl, int4 tile, int c0) {
+  constexpr int NW = tn_waves<MB, EPI>();
+  constexpr int NT = 64 * NW;                       // threads
+  constexpr int kBRowB = b_row_bytes<NW>();
   constexpr int kRing = tn_ring_depth<SRC>();
   constexpr int kBL = tn_b_loads<SRC>();
-  constexpr int kNCA = (128 * NMB + 255) / 256;   // A copies per thread per stage
+  constexpr int kNCA = (128 * NMB + NT - 1) / NT;   // A copies per thread per stage
   constexpr int kStageLoads = kNCA + kBL;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -185,14 +203,14 @@ __device__ __forceinline__ void gemm_tn_item(const GemmArgs& g, const LdsRing4& 
   const int row0 = tile.y, nrows = tile.z;
   const int64_t wsel = SRC == kSrcBF16 ? (int64_t)(tile.w - g.bf16_slot_base) : tile.x;
 
-  // A copies: chunk slot p = 256 i + tid of a stage holds K chunk
+  // A copies: chunk slot p = NT i + tid of a stage holds K chunk
   // (p & 3) ^ swz_a(r) of tile row r = p >> 2 (slots past the live blocks
   // copy clamped rows that no operand read touches)
   const __amdgpu_buffer_rsrc_t arsrc = raw_buffer(g.a, (uint32_t)(g.a_rows * g.lda * 2));
   uint32_t aoffs[kNCA];
 #pragma unroll
   for (int i = 0; i < kNCA; ++i) {
-    const int p = 256 * i + tid;
+    const int p = NT * i + tid;
     const int r = p >> 2;
     const int kc = (p & 3) ^ swz_a(r);
     const int rr = r < nrows ? r : 0;
@@ -206,7 +224,7 @@ __device__ __forceinline__ void gemm_tn_item(const GemmArgs& g, const LdsRing4& 
     const uint32_t soff = (uint32_t)((st < nstages ? st : nstages - 1) * kARowB);
 #pragma unroll
     for (int i = 0; i < kNCA; ++i)
-      copy16_to_lds(arsrc, aoffs[i], soff, As.b[BUF] + (256 * i + 64 * wave) * 16);
+      copy16_to_lds(arsrc, aoffs[i], soff, As.b[BUF] + (NT * i + 64 * wave) * 16);
   };
   // A operand offsets: row col of a block, chunk 2 s + half
   int aoff[2];
@@ -342,14 +360,14 @@ __device__ __forceinline__ void gemm_tn_item(const GemmArgs& g, const LdsRing4& 
 
   // Epilogue through LDS, 16 tile rows per round: the wavefronts write their
   // fp32 accumulators (C layout: lane = column, 16 rows per lane) into a
-  // 16 x 256 tile in Bs[0] (16-byte chunks XOR-permuted by row bit 2), then
+  // 16 x 64 NW tile in Bs[0] (16-byte chunks XOR-permuted by row bit 2), then
   // every thread finishes 16 consecutive columns of one row with 16-byte
   // loads of the saved activations and 16-byte stores.
   (void)active;
   float* tile_f = reinterpret_cast<float*>(Bs[0]);
-  auto tidx = [](int row, int c) { return row * 256 + (((c >> 2) ^ (((row >> 2) & 1) << 3)) << 2) + (c & 3); };
-  const int erow = tid >> 4;            // this thread's row in a round
-  const int eseg = tid & 15;            // its 16 columns: c0 + 16 eseg ..
+  auto tidx = [](int row, int c) { return row * NT + (((c >> 2) ^ (((row >> 2) & 1) << 3)) << 2) + (c & 3); };
+  const int erow = tid / (4 * NW);      // this thread's row in a round
+  const int eseg = tid % (4 * NW);      // its 16 columns: c0 + 16 eseg ..
   const int ecol = c0 + 16 * eseg;
 #pragma unroll
   for (int mb = 0; mb < NMB; ++mb) {
@@ -413,11 +431,12 @@ __device__ __forceinline__ void gemm_tn_item(const GemmArgs& g, const LdsRing4& 
             ou[e >> 1] = (uint32_t)bf16_hw_t(ru[0]) | ((uint32_t)bf16_hw_t(ru[1]) << 16);
           }
           if (g.gpart) {
-            // the 16 threads of a row are 16 consecutive lanes: a fixed
-            // butterfly gives every one the row's sum over the 256 columns
+            // the 16 threads of a row's 256-column part are 16 consecutive
+            // lanes: a fixed butterfly gives every one the part's sum, one
+            // partial per 256 columns
 #pragma unroll
             for (int m = 1; m < 16; m <<= 1) gp += __shfl_xor(gp, m, 16);
-            if (eseg == 0) g.gpart[orow * (g.inter / 256) + c0 / 256] = gp;
+            if ((eseg & 15) == 0) g.gpart[orow * (g.inter / 256) + ecol / 256] = gp;
           }
           u32x4_t* yg = reinterpret_cast<u32x4_t*>(g.y + orow * g.ldy + ecol);
           u32x4_t* yu = reinterpret_cast<u32x4_t*>(g.y + orow * g.ldy + g.inter + ecol);
@@ -441,18 +460,20 @@ __device__ __forceinline__ void gemm_tn_item(const GemmArgs& g, const LdsRing4& 
 }
 
 template <int SRC, int MB, int EPI, int AMODE>
-__global__ __launch_bounds__(256, 2) void k_gemm_tn(GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) uint8_t A0[a_stage_bytes<MB>()];
-  __shared__ __attribute__((aligned(16))) uint8_t A1[a_stage_bytes<MB>()];
-  __shared__ __attribute__((aligned(16))) uint8_t A2[a_stage_bytes<MB>()];
-  __shared__ __attribute__((aligned(16))) uint8_t A3[a_stage_bytes<MB>()];
+__global__ __launch_bounds__((64 * tn_waves<MB, EPI>()), (tn_occupancy<MB, EPI>())) void k_gemm_tn(
+    GemmArgs g) {
+  constexpr int NW = tn_waves<MB, EPI>();
+  __shared__ __attribute__((aligned(16))) uint8_t A0[a_stage_bytes<MB, EPI>()];
+  __shared__ __attribute__((aligned(16))) uint8_t A1[a_stage_bytes<MB, EPI>()];
+  __shared__ __attribute__((aligned(16))) uint8_t A2[a_stage_bytes<MB, EPI>()];
+  __shared__ __attribute__((aligned(16))) uint8_t A3[a_stage_bytes<MB, EPI>()];
   const LdsRing4 As{{A0, A1, A2, A3}};
   static_assert(kNBufA == 4, "four A stage buffers");
-  __shared__ __attribute__((aligned(16))) uint8_t Bs[2][kBStage];
+  __shared__ __attribute__((aligned(16))) uint8_t Bs[2][b_stage_bytes<NW>()];
   __shared__ float Gl[32 * MB];   // per-row gates for the SwiGLU-backward epilogue
   const int t_begin = g.range[0];
   const int t_end = g.range[1];
-  const int n_tiles_n = (g.K + 255) / 256;      // output columns = W's K index
+  const int n_tiles_n = (g.K + 64 * NW - 1) / (64 * NW);   // output columns = W's K index
   const int items = (t_end - t_begin) * n_tiles_n;
   const int per_xcd = gridDim.x >> 3;
   const int xcd = blockIdx.x & 7;
@@ -460,7 +481,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_tn(GemmArgs g) {
   const int q_end = min(items, (xcd + 1) * span);
   for (int q = xcd * span + (blockIdx.x >> 3); q < q_end; q += per_xcd) {
     const int4 tile = g.tiles[t_begin + q / n_tiles_n];
-    const int c0 = (q % n_tiles_n) * 256;
+    const int c0 = (q % n_tiles_n) * 64 * NW;
     const int nmb = (tile.z + 31) / 32;
     if (MB == 1 || nmb <= 1) {
       gemm_tn_item<SRC, MB, EPI, AMODE, 1>(g, As, Bs, Gl, tile, c0);
@@ -476,12 +497,14 @@ __global__ __launch_bounds__(256, 2) void k_gemm_tn(GemmArgs g) {
 
 template <int SRC, int MB, int EPI, int AMODE>
 hipError_t launch_tn_t(const GemmArgs& g, hipStream_t s) {
-  const int n_tiles_n = (g.K + 255) / 256;
+  constexpr int NW = tn_waves<MB, EPI>();
+  const int n_tiles_n = (g.K + 64 * NW - 1) / (64 * NW);
   const int64_t bound = (int64_t)g.max_tiles * n_tiles_n;
   if (bound <= 0) return hipSuccess;
-  int64_t grid = std::min<int64_t>(bound, (int64_t)num_cus() * 2);
+  int64_t grid = std::min<int64_t>(bound, (int64_t)num_cus() * tn_occupancy<MB, EPI>());
   grid = (grid + 7) / 8 * 8;
-  hipLaunchKernelGGL((k_gemm_tn<SRC, MB, EPI, AMODE>), dim3((unsigned)grid), dim3(256), 0, s, g);
+  hipLaunchKernelGGL((k_gemm_tn<SRC, MB, EPI, AMODE>), dim3((unsigned)grid), dim3(64 * NW), 0, s,
+                     g);
   return hipGetLastError();
 }
 
