@@ -9,9 +9,9 @@
 //
 // Work decomposition (gfx950, 64-wide wavefronts, v_mfma_f32_32x32x16_bf16):
 //  - a work item is (M-tile of up to 32*MB rows of one expert, 64*NW output
-//    columns); a persistent grid walks the items, split into 8 contiguous
-//    ranges so that each XCD (blocks are dealt round-robin to the 8 XCDs)
-//    works on neighbouring items that share A rows and weights in its L2;
+//    columns); a persistent grid takes the items in order from a counter, so
+//    the columns of one M-tile run side by side and a workgroup that drew
+//    small tiles takes more of them;
 //  - NW wavefronts per workgroup (8, or 4 for 32-row tiles), each owning 64
 //    output columns (two 32-column MFMA blocks) for all rows of the tile, so
 //    each weight element is loaded and decoded exactly once per tile;
@@ -177,7 +177,7 @@ __device__ __forceinline__ bf16x8_t b_operand(const BRegs<SRC>& r, const BScale<
 template <int SRC, int MB, int EPI, int AMODE, int NMB>
 __device__ __forceinline__ void gemm_nt_item(const GemmArgs& g,
                                              const LdsRing4& As, int4 tile,
-                                             int nt) {
+                                             int nt, int& next_q) {
   constexpr int kRing = ring_depth<SRC>();
   constexpr int kBL = b_loads_per_stage<SRC>();
   constexpr int NW = nt_waves<MB>();
@@ -344,6 +344,9 @@ __device__ __forceinline__ void gemm_nt_item(const GemmArgs& g,
   // drain the clamped copies past the last stage before the LDS ring is
   // reused by the next item
   __builtin_amdgcn_s_waitcnt(vm_lgkm0_imm(0));
+  // claim the workgroup's next item now, so the counter's round trip runs
+  // under this item's epilogue
+  if (threadIdx.x == 0) next_q = atomicAdd(g.work, 1);
 
   if (!active) return;
   {
@@ -409,29 +412,41 @@ __global__ __launch_bounds__(64 * nt_waves<MB>(), nt_occupancy<MB>()) void k_gem
   __shared__ __attribute__((aligned(16))) uint8_t A3[32 * MB * kStageRowB];
   const LdsRing4 As{{A0, A1, A2, A3}};
   static_assert(kNBuf == 4, "four A stage buffers");
+  __shared__ int s_next;
   const int t_begin = g.range[0];
   const int t_end = g.range[1];
   constexpr int NW = nt_waves<MB>();
   const int n_tiles_n = EPI == kEpiSwiGLU ? (g.inter + 32 * NW - 1) / (32 * NW)
                                           : (g.N + 64 * NW - 1) / (64 * NW);
-  const int items = (t_end - t_begin) * n_tiles_n;
-  const int per_xcd = gridDim.x >> 3;
-  const int xcd = blockIdx.x & 7;
-  const int span = (items + 7) >> 3;
-  const int q_end = min(items, (xcd + 1) * span);
-  for (int q = xcd * span + (blockIdx.x >> 3); q < q_end; q += per_xcd) {
-    const int4 tile = g.tiles[t_begin + q / n_tiles_n];
-    const int nt = q % n_tiles_n;
+  const unsigned items = (unsigned)((t_end - t_begin) * n_tiles_n);
+  // Items (M-tile q / n_tiles_n, column tile q % n_tiles_n) are handed out in
+  // order by one counter, so a workgroup that drew small tiles takes more of
+  // them; the plan puts the largest tiles first.
+  int next_q = 0;
+  if (threadIdx.x == 0) s_next = atomicAdd(g.work, 1);
+  stage_barrier<63>();
+  unsigned q = (unsigned)__builtin_amdgcn_readfirstlane(s_next);
+  while (q < items) {
+    const int4 tile = g.tiles[t_begin + (int)(q / n_tiles_n)];
+    const int nt = (int)(q % n_tiles_n);
     const int nmb = (tile.z + 31) / 32;
     if (MB == 1 || nmb <= 1) {
-      gemm_nt_item<SRC, MB, EPI, AMODE, 1>(g, As, tile, nt);
+      gemm_nt_item<SRC, MB, EPI, AMODE, 1>(g, As, tile, nt, next_q);
     } else if (MB == 2 || nmb == 2) {
-      gemm_nt_item<SRC, MB, EPI, AMODE, (MB >= 2 ? 2 : 1)>(g, As, tile, nt);
+      gemm_nt_item<SRC, MB, EPI, AMODE, (MB >= 2 ? 2 : 1)>(g, As, tile, nt, next_q);
     } else if (nmb == 3) {
-      gemm_nt_item<SRC, MB, EPI, AMODE, (MB >= 4 ? 3 : 1)>(g, As, tile, nt);
+      gemm_nt_item<SRC, MB, EPI, AMODE, (MB >= 4 ? 3 : 1)>(g, As, tile, nt, next_q);
     } else {
-      gemm_nt_item<SRC, MB, EPI, AMODE, (MB >= 4 ? 4 : 1)>(g, As, tile, nt);
+      gemm_nt_item<SRC, MB, EPI, AMODE, (MB >= 4 ? 4 : 1)>(g, As, tile, nt, next_q);
     }
+    if (threadIdx.x == 0) s_next = next_q;
+    stage_barrier<63>();
+    q = (unsigned)__builtin_amdgcn_readfirstlane(s_next);
+  }
+  // the last workgroup out clears the counters for the next launch
+  if (threadIdx.x == 0 && atomicAdd(g.work + 1, 1) == (int)gridDim.x - 1) {
+    atomicExch(g.work, 0);
+    atomicExch(g.work + 1, 0);
   }
 }
 

@@ -7,8 +7,9 @@
 // with the group-32 scales running along W's K index (the output columns
 // here), not along the reduction.
 //
-// Work decomposition: as the forward kernel (persistent grid, XCD-contiguous
-// item ranges, NW wavefronts x 64 output columns, v_mfma_f32_32x32x16_bf16),
+// Work decomposition: as the forward kernel (persistent grid taking items in
+// order from a counter, NW wavefronts x 64 output columns,
+// v_mfma_f32_32x32x16_bf16),
 // with 32 reduction rows (W rows) per stage:
 //  - A (rows of the routed activations) is copied global -> LDS three stages
 //    ahead into a ring of four stage buffers, as in the forward kernel;
@@ -186,7 +187,7 @@ __device__ __forceinline__ void store_bt(const BGroup<SRC>& b, uint8_t* base, co
 template <int SRC, int MB, int EPI, int AMODE, int NMB>
 __device__ __forceinline__ void gemm_tn_item(const GemmArgs& g, const LdsRing4& As,
                                              uint8_t (*Bs)[b_stage_bytes<tn_waves<MB, EPI>()>()],
-                                             float* Gl, int4 tile, int c0) {
+                                             float* Gl, int4 tile, int c0, int& next_q) {
   constexpr int NW = tn_waves<MB, EPI>();
   constexpr int NT = 64 * NW;                       // threads
   constexpr int kBRowB = b_row_bytes<NW>();
@@ -353,9 +354,12 @@ __device__ __forceinline__ void gemm_tn_item(const GemmArgs& g, const LdsRing4& 
     kstage(st + 1, I1{});
   }
   __builtin_amdgcn_s_waitcnt(vm_lgkm0_imm(0));
+  // claim the workgroup's next item now, so the counter's round trip runs
+  // under this item's epilogue
+  if (tid == 0) next_q = atomicAdd(g.work, 1);
   if constexpr (EPI == kEpiSwiGLUBwd) {
     if (tid < 32 * NMB) Gl[tid] = gval;
-    stage_barrier<0>();
+    stage_barrier<63>();
   }
 
   // Epilogue through LDS, 16 tile rows per round: the wavefronts write their
@@ -471,27 +475,37 @@ __global__ __launch_bounds__((64 * tn_waves<MB, EPI>()), (tn_occupancy<MB, EPI>(
   static_assert(kNBufA == 4, "four A stage buffers");
   __shared__ __attribute__((aligned(16))) uint8_t Bs[2][b_stage_bytes<NW>()];
   __shared__ float Gl[32 * MB];   // per-row gates for the SwiGLU-backward epilogue
+  __shared__ int s_next;
   const int t_begin = g.range[0];
   const int t_end = g.range[1];
   const int n_tiles_n = (g.K + 64 * NW - 1) / (64 * NW);   // output columns = W's K index
-  const int items = (t_end - t_begin) * n_tiles_n;
-  const int per_xcd = gridDim.x >> 3;
-  const int xcd = blockIdx.x & 7;
-  const int span = (items + 7) >> 3;
-  const int q_end = min(items, (xcd + 1) * span);
-  for (int q = xcd * span + (blockIdx.x >> 3); q < q_end; q += per_xcd) {
-    const int4 tile = g.tiles[t_begin + q / n_tiles_n];
-    const int c0 = (q % n_tiles_n) * 64 * NW;
+  const unsigned items = (unsigned)((t_end - t_begin) * n_tiles_n);
+  // items handed out in order by one counter, as in the forward kernel
+  int next_q = 0;
+  if (threadIdx.x == 0) s_next = atomicAdd(g.work, 1);
+  stage_barrier<63>();
+  unsigned q = (unsigned)__builtin_amdgcn_readfirstlane(s_next);
+  while (q < items) {
+    const int4 tile = g.tiles[t_begin + (int)(q / n_tiles_n)];
+    const int c0 = (int)(q % n_tiles_n) * 64 * NW;
     const int nmb = (tile.z + 31) / 32;
     if (MB == 1 || nmb <= 1) {
-      gemm_tn_item<SRC, MB, EPI, AMODE, 1>(g, As, Bs, Gl, tile, c0);
+      gemm_tn_item<SRC, MB, EPI, AMODE, 1>(g, As, Bs, Gl, tile, c0, next_q);
     } else if (MB == 2 || nmb == 2) {
-      gemm_tn_item<SRC, MB, EPI, AMODE, (MB >= 2 ? 2 : 1)>(g, As, Bs, Gl, tile, c0);
+      gemm_tn_item<SRC, MB, EPI, AMODE, (MB >= 2 ? 2 : 1)>(g, As, Bs, Gl, tile, c0, next_q);
     } else if (nmb == 3) {
-      gemm_tn_item<SRC, MB, EPI, AMODE, (MB >= 4 ? 3 : 1)>(g, As, Bs, Gl, tile, c0);
+      gemm_tn_item<SRC, MB, EPI, AMODE, (MB >= 4 ? 3 : 1)>(g, As, Bs, Gl, tile, c0, next_q);
     } else {
-      gemm_tn_item<SRC, MB, EPI, AMODE, (MB >= 4 ? 4 : 1)>(g, As, Bs, Gl, tile, c0);
+      gemm_tn_item<SRC, MB, EPI, AMODE, (MB >= 4 ? 4 : 1)>(g, As, Bs, Gl, tile, c0, next_q);
     }
+    if (threadIdx.x == 0) s_next = next_q;
+    stage_barrier<63>();
+    q = (unsigned)__builtin_amdgcn_readfirstlane(s_next);
+  }
+  // the last workgroup out clears the counters for the next launch
+  if (threadIdx.x == 0 && atomicAdd(g.work + 1, 1) == (int)gridDim.x - 1) {
+    atomicExch(g.work, 0);
+    atomicExch(g.work + 1, 0);
   }
 }
 

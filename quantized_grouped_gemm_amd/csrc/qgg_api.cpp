@@ -60,6 +60,7 @@ int64_t tile_capacity(int64_t P, int E, int MT) { return (P + MT - 1) / MT + E +
 struct Plan {
   int4* tiles = nullptr;
   int32_t* chunk_first = nullptr;
+  int32_t* work = nullptr;   // the GEMM launches' item and exit counters
   int mb = 1;
   int64_t cap = 0;
 };
@@ -68,7 +69,9 @@ void carve_plan(Carver& cv, int64_t P, int E, Plan& pl) {
   pl.mb = choose_mb(P, E);
   pl.cap = tile_capacity(P, E, 32 * pl.mb);
   pl.tiles = cv.take<int4>(sizeof(int4) * pl.cap);
-  pl.chunk_first = cv.take<int32_t>(sizeof(int32_t) * (E + 2));
+  // chunk bounds (E + 2 entries), then the GEMM launches' work counters (2)
+  pl.chunk_first = cv.take<int32_t>(sizeof(int32_t) * (E + 4));
+  pl.work = pl.chunk_first ? pl.chunk_first + E + 2 : nullptr;
 }
 
 bool valid_fmt(int f) { return f == QGG_FMT_MXFP4 || f == QGG_FMT_INT4; }
@@ -118,6 +121,7 @@ GemmArgs base_args(const qgg_qweight* w, const Plan& pl) {
   g.K = w->K;
   g.tiles = pl.tiles;
   g.range = pl.chunk_first;
+  g.work = pl.work;
   g.max_tiles = (int)pl.cap;
   g.mt_rows = 32 * pl.mb;
   return g;

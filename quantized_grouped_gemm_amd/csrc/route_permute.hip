@@ -294,38 +294,67 @@ __global__ __launch_bounds__(256) void k_gather_rows(const uint16_t* __restrict_
   for (int c = lane; c < d / 8; c += 64) dst[c] = src[c];
 }
 
-// M-tile plan: for the active experts in ascending order, tiles of up to MT
-// rows.  tiles[j] = {expert, first sorted row, rows, active index};
-// chunk_first[c] = first tile of chunk c (chunks of C active experts), and
-// chunk_first[nchunks] = number of tiles.
+// M-tile plan: the rows of the active experts cut into tiles of up to MT rows,
+// tiles[j] = {expert, first sorted row, rows, active index}, grouped into
+// chunks of C active experts: chunk_first[c] = first tile of chunk c and
+// chunk_first[nchunks] = number of tiles.  Inside a chunk the tiles are
+// ordered by their number of live 32-row blocks, most first (ascending
+// expert within a size), so that workgroups taking the items of a launch in
+// order from one counter finish on the smallest.  The GEMM launches' two
+// work counters (work[0], work[1]) are cleared here, before any launch of the
+// call uses them.
 __device__ __forceinline__ void tile_plan_body(const int32_t* __restrict__ counts,
                                                const int32_t* __restrict__ offsets,
                                                const int32_t* __restrict__ active,
                                                const int32_t* __restrict__ n_active, int MT,
                                                int C, int4* __restrict__ tiles,
                                                int32_t* __restrict__ chunk_first, int* scratch,
-                                               int E) {
+                                               int (*sk)[1025], int E, int32_t* work) {
   const int a = threadIdx.x;
   const int A = *n_active;
   const int e = a < A ? active[a] : -1;
   const int cnt = e >= 0 ? counts[e] : 0;
-  const int nt = (cnt + MT - 1) / MT;
-  int total;
-  const int first = block_excl_scan(nt, scratch, &total);
+  const int MB = MT / 32;
+  const int nfull = cnt / MT;
+  const int rem = cnt - nfull * MT;
+  const int rb = (rem + 31) / 32;        // live blocks of the last, partial tile
+  // sk[b - 1][i] = tiles with b live blocks of the active experts before i
+  // (i = 0 .. A; experts past the last active one add none)
+  int total = 0;
+  for (int b = 1; b <= MB; ++b) {
+    const int nb = (b == MB ? nfull : 0) + (rb == b ? 1 : 0);
+    int tb;
+    sk[b - 1][a] = block_excl_scan(nb, scratch, &tb);
+    if (a == 0) sk[b - 1][1024] = tb;
+    total += tb;
+  }
+  __syncthreads();
+  const int CC = C > 0 ? C : (A > 0 ? A : 1);
   if (e >= 0) {
+    const int c0 = a / CC * CC;                      // this chunk's experts [c0, c1)
+    const int c1 = min(c0 + CC, A);
+    int j = 0;                                        // tiles before the chunk
+    for (int b = 1; b <= MB; ++b) j += sk[b - 1][c0];
+    if (a == c0) chunk_first[a / CC] = j;
     const int r0 = offsets[e];
-    for (int i = 0; i < nt; ++i) {
-      const int rows = min(MT, cnt - i * MT);
-      tiles[first + i] = make_int4(e, r0 + i * MT, rows, a);
+    for (int b = MB; b >= 1; --b) {
+      const int lo = sk[b - 1][c0];
+      int t = j + sk[b - 1][a] - lo;
+      if (b == MB)
+        for (int i = 0; i < nfull; ++i) tiles[t++] = make_int4(e, r0 + i * MT, MT, a);
+      if (rb == b) tiles[t] = make_int4(e, r0 + nfull * MT, rem, a);
+      j += sk[b - 1][c1] - lo;
     }
   }
-  const int CC = C > 0 ? C : (A > 0 ? A : 1);
-  if (a < A && a % CC == 0) chunk_first[a / CC] = first;
   // chunks past the last live one (up to entry E + 1) are empty: their
   // bounds both read `total`, so a chunk loop of fixed length needs no host
   // read-back of the active count
   const int nch = (A + CC - 1) / CC;
   for (int c = nch + a; c <= E + 1; c += blockDim.x) chunk_first[c] = total;
+  if (a == 0) {
+    work[0] = 0;
+    work[1] = 0;
+  }
 }
 
 __global__ __launch_bounds__(1024) void k_tile_plan(const int32_t* __restrict__ counts,
@@ -333,9 +362,12 @@ __global__ __launch_bounds__(1024) void k_tile_plan(const int32_t* __restrict__ 
                                                     const int32_t* __restrict__ active,
                                                     const int32_t* __restrict__ n_active, int MT,
                                                     int C, int4* __restrict__ tiles,
-                                                    int32_t* __restrict__ chunk_first, int E) {
+                                                    int32_t* __restrict__ chunk_first, int E,
+                                                    int32_t* __restrict__ work) {
   __shared__ int scratch[16];
-  tile_plan_body(counts, offsets, active, n_active, MT, C, tiles, chunk_first, scratch, E);
+  __shared__ int sk[4][1025];
+  tile_plan_body(counts, offsets, active, n_active, MT, C, tiles, chunk_first, scratch, sk, E,
+                 work);
 }
 
 // Permutation of at most kTiny pairs in one workgroup without rank loops:
@@ -350,9 +382,11 @@ __global__ __launch_bounds__(1024) void k_perm_tiny(const int32_t* __restrict__ 
                                                     int E, int32_t* __restrict__ blk,
                                                     PermPtrs pp, int32_t* __restrict__ err,
                                                     int MT, int C, int4* __restrict__ tiles,
-                                                    int32_t* __restrict__ chunk_first) {
+                                                    int32_t* __restrict__ chunk_first,
+                                                    int32_t* __restrict__ work) {
   extern __shared__ int cnt[];       // [E]
   __shared__ int scratch[16];
+  __shared__ int sk[4][1025];
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int np = (int)P;
@@ -392,7 +426,7 @@ __global__ __launch_bounds__(1024) void k_perm_tiny(const int32_t* __restrict__ 
   if (MT > 0) {
     __syncthreads();
     tile_plan_body(pp.counts, pp.offsets, pp.active, pp.n_active, MT, C, tiles, chunk_first,
-                   scratch, E);
+                   scratch, sk, E, work);
   }
 }
 
@@ -428,7 +462,8 @@ hipError_t launch_permute_plan(const int32_t* ids, int64_t P, int E, const PermP
   TimedLaunch timed_(kLPermute, s);
   if (P <= kTiny) {
     hipLaunchKernelGGL(k_perm_tiny, dim3(1), dim3(1024), E * sizeof(int), s, ids, P, E,
-                       static_cast<int32_t*>(ws), pp, err, MT, C, tiles, chunk_first);
+                       static_cast<int32_t*>(ws), pp, err, MT, C, tiles, chunk_first,
+                       chunk_first ? chunk_first + E + 2 : nullptr);
     return hipGetLastError();
   }
   const int nblk = (int)((P + kSeg - 1) / kSeg);
@@ -462,7 +497,7 @@ hipError_t launch_tile_plan(const PermPtrs& pp, int E, int MT, int C, int4* tile
                             int32_t* chunk_first, hipStream_t s) {
   TimedLaunch timed_(kLPermute, s);
   hipLaunchKernelGGL(k_tile_plan, dim3(1), dim3(1024), 0, s, pp.counts, pp.offsets, pp.active,
-                     pp.n_active, MT, C, tiles, chunk_first, E);
+                     pp.n_active, MT, C, tiles, chunk_first, E, chunk_first + E + 2);
   return hipGetLastError();
 }
 
