@@ -19,7 +19,10 @@
  * Conventions for every call
  *  - Pointers are DEVICE memory owned by the caller unless marked "host".
  *    The library never allocates device memory: scratch and intermediates
- *    come from the caller's `workspace`, sized by qgg_workspace_bytes().
+ *    come from the caller's `workspace`, sized by qgg_workspace_bytes().  A
+ *    call uses its workspace until its last kernel ends (it also holds the
+ *    counters from which the grouped GEMM launches hand out their work), so
+ *    calls that may run at the same time need workspaces of their own.
  *  - BF16 tensors are passed as uint16_t bit patterns.  Row-major throughout.
  *  - Calls are asynchronous on `stream` (a hipStream_t; 0 = null stream) and
  *    never synchronize with the host, so a whole call can be captured into a
