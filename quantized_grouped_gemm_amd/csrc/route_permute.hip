@@ -319,12 +319,29 @@ __device__ __forceinline__ void tile_plan_body(const int32_t* __restrict__ count
   const int rem = cnt - nfull * MT;
   const int rb = (rem + 31) / 32;        // live blocks of the last, partial tile
   // sk[b - 1][i] = tiles with b live blocks of the active experts before i
-  // (i = 0 .. A; experts past the last active one add none)
+  // (i = 0 .. A; experts past the last active one add none): the MB
+  // exclusive scans of one pass, wavefront scans first, then wavefront b
+  // scans the wavefront totals of size b
+  const int lane = a & 63, wv = a >> 6, nwv = blockDim.x >> 6;
+  int incl[4];
+#pragma unroll
+  for (int b = 1; b <= 4; ++b) {
+    const int nb = b > MB ? 0 : (b == MB ? nfull : 0) + (rb == b ? 1 : 0);
+    incl[b - 1] = wave_incl_scan(nb);
+    if (lane == 63) scratch[16 * (b - 1) + wv] = incl[b - 1];
+    incl[b - 1] -= nb;
+  }
+  __syncthreads();
+  if (wv < MB) {
+    const int v = lane < nwv ? scratch[16 * wv + lane] : 0;
+    const int w = wave_incl_scan(v);
+    if (lane < nwv) scratch[16 * wv + lane] = w;
+  }
+  __syncthreads();
   int total = 0;
   for (int b = 1; b <= MB; ++b) {
-    const int nb = (b == MB ? nfull : 0) + (rb == b ? 1 : 0);
-    int tb;
-    sk[b - 1][a] = block_excl_scan(nb, scratch, &tb);
+    sk[b - 1][a] = (wv ? scratch[16 * (b - 1) + wv - 1] : 0) + incl[b - 1];
+    const int tb = scratch[16 * (b - 1) + nwv - 1];
     if (a == 0) sk[b - 1][1024] = tb;
     total += tb;
   }
@@ -364,7 +381,7 @@ __global__ __launch_bounds__(1024) void k_tile_plan(const int32_t* __restrict__ 
                                                     int C, int4* __restrict__ tiles,
                                                     int32_t* __restrict__ chunk_first, int E,
                                                     int32_t* __restrict__ work) {
-  __shared__ int scratch[16];
+  __shared__ int scratch[64];
   __shared__ int sk[4][1025];
   tile_plan_body(counts, offsets, active, n_active, MT, C, tiles, chunk_first, scratch, sk, E,
                  work);
@@ -385,7 +402,7 @@ __global__ __launch_bounds__(1024) void k_perm_tiny(const int32_t* __restrict__ 
                                                     int32_t* __restrict__ chunk_first,
                                                     int32_t* __restrict__ work) {
   extern __shared__ int cnt[];       // [E]
-  __shared__ int scratch[16];
+  __shared__ int scratch[64];
   __shared__ int sk[4][1025];
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
