@@ -9,9 +9,9 @@
 //
 // Work decomposition (gfx950, 64-wide wavefronts, v_mfma_f32_32x32x16_bf16):
 //  - a work item is (M-tile of up to 32*MB rows of one expert, 64*NW output
-//    columns); a persistent grid takes the items in order from a counter, so
-//    the columns of one M-tile run side by side and a workgroup that drew
-//    small tiles takes more of them;
+//    columns); a persistent grid starts on items 0 .. grid - 1 and takes the
+//    rest in order from a counter, so the columns of one M-tile run side by
+//    side and a workgroup that drew small tiles takes more of them;
 //  - NW wavefronts per workgroup (8, or 4 for 32-row tiles), each owning 64
 //    output columns (two 32-column MFMA blocks) for all rows of the tile, so
 //    each weight element is loaded and decoded exactly once per tile;
@@ -419,13 +419,12 @@ __global__ __launch_bounds__(64 * nt_waves<MB>(), nt_occupancy<MB>()) void k_gem
   const int n_tiles_n = EPI == kEpiSwiGLU ? (g.inter + 32 * NW - 1) / (32 * NW)
                                           : (g.N + 64 * NW - 1) / (64 * NW);
   const unsigned items = (unsigned)((t_end - t_begin) * n_tiles_n);
-  // Items (M-tile q / n_tiles_n, column tile q % n_tiles_n) are handed out in
-  // order by one counter, so a workgroup that drew small tiles takes more of
-  // them; the plan puts the largest tiles first.
+  // Items (M-tile q / n_tiles_n, column tile q % n_tiles_n): workgroup b
+  // starts with item b, and every further item comes in order from one
+  // counter, so a workgroup that drew small tiles takes more of them (the
+  // plan puts the largest tiles first); an empty launch touches no counter.
   int next_q = 0;
-  if (threadIdx.x == 0) s_next = atomicAdd(g.work, 1);
-  stage_barrier<63>();
-  unsigned q = (unsigned)__builtin_amdgcn_readfirstlane(s_next);
+  unsigned q = blockIdx.x;
   while (q < items) {
     const int4 tile = g.tiles[t_begin + (int)(q / n_tiles_n)];
     const int nt = (int)(q % n_tiles_n);
@@ -439,14 +438,16 @@ __global__ __launch_bounds__(64 * nt_waves<MB>(), nt_occupancy<MB>()) void k_gem
     } else {
       gemm_nt_item<SRC, MB, EPI, AMODE, (MB >= 4 ? 4 : 1)>(g, As, tile, nt, next_q);
     }
-    if (threadIdx.x == 0) s_next = next_q;
+    // draws return 0, 1, ... and a launch makes exactly `items` of them (one
+    // per item past the grid's first, one failing draw per workgroup that
+    // had an item), so the draw of items - 1 is the last: it clears the
+    // counter for the next launch
+    if (threadIdx.x == 0) {
+      s_next = next_q;
+      if ((unsigned)next_q == items - 1) atomicExch(g.work, 0);
+    }
     stage_barrier<63>();
-    q = (unsigned)__builtin_amdgcn_readfirstlane(s_next);
-  }
-  // the last workgroup out clears the counters for the next launch
-  if (threadIdx.x == 0 && atomicAdd(g.work + 1, 1) == (int)gridDim.x - 1) {
-    atomicExch(g.work, 0);
-    atomicExch(g.work + 1, 0);
+    q = gridDim.x + (unsigned)__builtin_amdgcn_readfirstlane(s_next);
   }
 }
 

@@ -7,8 +7,8 @@
 // with the group-32 scales running along W's K index (the output columns
 // here), not along the reduction.
 //
-// Work decomposition: as the forward kernel (persistent grid taking items in
-// order from a counter, NW wavefronts x 64 output columns,
+// Work decomposition: as the forward kernel (persistent grid taking items past
+// its first in order from a counter, NW wavefronts x 64 output columns,
 // v_mfma_f32_32x32x16_bf16),
 // with 32 reduction rows (W rows) per stage:
 //  - A (rows of the routed activations) is copied global -> LDS three stages
@@ -480,11 +480,10 @@ __global__ __launch_bounds__((64 * tn_waves<MB, EPI>()), (tn_occupancy<MB, EPI>(
   const int t_end = g.range[1];
   const int n_tiles_n = (g.K + 64 * NW - 1) / (64 * NW);   // output columns = W's K index
   const unsigned items = (unsigned)((t_end - t_begin) * n_tiles_n);
-  // items handed out in order by one counter, as in the forward kernel
+  // workgroup b starts with item b, the rest come in order from one counter,
+  // as in the forward kernel
   int next_q = 0;
-  if (threadIdx.x == 0) s_next = atomicAdd(g.work, 1);
-  stage_barrier<63>();
-  unsigned q = (unsigned)__builtin_amdgcn_readfirstlane(s_next);
+  unsigned q = blockIdx.x;
   while (q < items) {
     const int4 tile = g.tiles[t_begin + (int)(q / n_tiles_n)];
     const int c0 = (int)(q % n_tiles_n) * 64 * NW;
@@ -498,14 +497,16 @@ __global__ __launch_bounds__((64 * tn_waves<MB, EPI>()), (tn_occupancy<MB, EPI>(
     } else {
       gemm_tn_item<SRC, MB, EPI, AMODE, (MB >= 4 ? 4 : 1)>(g, As, Bs, Gl, tile, c0, next_q);
     }
-    if (threadIdx.x == 0) s_next = next_q;
+    // draws return 0, 1, ... and a launch makes exactly `items` of them (one
+    // per item past the grid's first, one failing draw per workgroup that
+    // had an item), so the draw of items - 1 is the last: it clears the
+    // counter for the next launch
+    if (threadIdx.x == 0) {
+      s_next = next_q;
+      if ((unsigned)next_q == items - 1) atomicExch(g.work, 0);
+    }
     stage_barrier<63>();
-    q = (unsigned)__builtin_amdgcn_readfirstlane(s_next);
-  }
-  // the last workgroup out clears the counters for the next launch
-  if (threadIdx.x == 0 && atomicAdd(g.work + 1, 1) == (int)gridDim.x - 1) {
-    atomicExch(g.work, 0);
-    atomicExch(g.work + 1, 0);
+    q = gridDim.x + (unsigned)__builtin_amdgcn_readfirstlane(s_next);
   }
 }
 

@@ -40,8 +40,8 @@ struct GemmArgs {
   // plan
   const int4* tiles;
   const int32_t* range;          // device: first and one-past-last tile
-  int32_t* work;                 // device: item counter, exit counter (zero
-                                 // before a launch; the launch leaves them zero)
+  int32_t* work;                 // device: item counter (zero before a launch;
+                                 // the launch leaves it zero)
   int max_tiles;                 // host bound on range[1] - range[0]
   int mt_rows;                   // rows per M-tile (32 * MB)
   // output
