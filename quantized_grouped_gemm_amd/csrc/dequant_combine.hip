@@ -134,15 +134,16 @@ __global__ __launch_bounds__(256) void k_repack(const uint8_t* __restrict__ pack
 
 // out[t][:] = sum over j ascending of w_j * rows[inv_perm[t*k+j]][:], fp32
 // accumulation, BF16 out; with rows2, each term is w_j * (rows + rows2) of
-// that sorted row (the two added in fp32 first).  Grid (T, d / 2048): each
-// thread owns 8 columns of one token and issues its k row loads together.
-__global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ rows,
+// that sorted row (the two added in fp32 first).  Grid (T, column blocks):
+// each thread owns 8 columns of one token and issues its k row loads
+// together; a block spans a whole row (up to 1024 threads).
+__global__ __launch_bounds__(1024) void k_combine(const uint16_t* __restrict__ rows,
                                                  const uint16_t* __restrict__ rows2, int d,
                                                  const int32_t* __restrict__ inv_perm,
                                                  const float* __restrict__ gates, int k,
                                                  uint16_t* __restrict__ out) {
   const int64_t t = blockIdx.x;
-  const int c = blockIdx.y * 256 + threadIdx.x;   // 8-column chunk
+  const int c = blockIdx.y * blockDim.x + threadIdx.x;   // 8-column chunk
   if (c >= d / 8) return;
   float acc[8];
 #pragma unroll
@@ -156,8 +157,10 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ ro
       const int j = j0 + b;
       const int src = j < k ? inv_perm[t * k + j] : -1;
       w[b] = src < 0 ? 0.f : (gates ? gates[t * k + j] : 1.0f);
+      // each routed row is read once: non-temporal loads keep it out of the caches
       v[b] = src < 0 ? u32x4_t{0u, 0u, 0u, 0u}
-                     : reinterpret_cast<const u32x4_t*>(rows + (int64_t)src * d)[c];
+                     : __builtin_nontemporal_load(
+                           reinterpret_cast<const u32x4_t*>(rows + (int64_t)src * d) + c);
     }
     if (rows2) {
       u32x4_t v2[kB];
@@ -193,7 +196,7 @@ __global__ __launch_bounds__(256) void k_combine(const uint16_t* __restrict__ ro
   }
   u32x4_t o = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
                pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])};
-  reinterpret_cast<u32x4_t*>(out + t * d)[c] = o;
+  __builtin_nontemporal_store(o, reinterpret_cast<u32x4_t*>(out + t * d) + c);
 }
 
 // Scale validation for the fused decoder: an INT4 group whose BF16 scale is
@@ -261,8 +264,11 @@ hipError_t launch_combine(const uint16_t* rows, int d, const int32_t* inv_perm,
                           const uint16_t* rows2) {
   TimedLaunch timed_(kLCombine, s);
   if (T == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_combine, dim3(T, (d / 8 + 255) / 256), dim3(256), 0, s, rows, rows2, d,
-                     inv_perm, gates, k, out);
+  const int chunks = d / 8;
+  const int ny = (chunks + 1023) / 1024;
+  const int threads = ((chunks + ny - 1) / ny + 63) / 64 * 64;
+  hipLaunchKernelGGL(k_combine, dim3(T, ny), dim3(threads), 0, s, rows, rows2, d, inv_perm, gates,
+                     k, out);
   return hipGetLastError();
 }
 
