@@ -45,9 +45,12 @@ __device__ __forceinline__ uint32_t order_key(float v) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// One wavefront per token.  Each lane holds up to 16 logits (E <= 1024); k
-// rounds of a wavefront arg-max under the key (logit desc, id asc) pick the
-// experts; gates are the softmax over the kept logits.
+// One wavefront per token.  Each lane holds NV logits (experts lane, lane +
+// 64, ...; NV * 64 >= E); k rounds of a wavefront arg-max under the key
+// (logit desc, id asc) pick the experts, each lane offering its best
+// untaken entry (recomputed only by the lane whose entry was just taken);
+// gates are the softmax over the kept logits.
+template <int NV>
 __global__ __launch_bounds__(256) void k_route(const float* __restrict__ logits, int T, int E,
                                                int k, int32_t* __restrict__ ids,
                                                float* __restrict__ gates,
@@ -56,10 +59,10 @@ __global__ __launch_bounds__(256) void k_route(const float* __restrict__ logits,
   const int t = blockIdx.x * 4 + threadIdx.x / 64;
   if (t >= T) return;
   const float* row = logits + (int64_t)t * E;
-  float v[16];
+  float v[NV];
   bool bad = false;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
+  for (int i = 0; i < NV; ++i) {
     const int e = lane + 64 * i;
     float x = -INFINITY;
     if (e < E) {
@@ -76,21 +79,28 @@ __global__ __launch_bounds__(256) void k_route(const float* __restrict__ logits,
   float m = 0.f, sum = 0.f;
   int my_id = 0;       // lane j keeps pick j (k <= 32)
   float my_w = 0.f;
-  for (int j = 0; j < k; ++j) {
-    // this lane's best untaken entry; key 0 = none (a valid entry, even
-    // -inf, has a nonzero key)
+  // this lane's best untaken entry; key 0 = none (a valid entry, even -inf,
+  // has a nonzero key)
+  auto lane_best = [&]() {
     uint64_t key = 0;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < NV; ++i) {
       const int e = lane + 64 * i;
       const uint64_t ki = ((uint64_t)order_key(v[i]) << 32) | (uint32_t)~e;
       if (e < E && !((taken >> i) & 1u) && ki > key) key = ki;
     }
-    key = wave_max_u64(key);
+    return key;
+  };
+  uint64_t mine = lane_best();
+  for (int j = 0; j < k; ++j) {
+    const uint64_t key = wave_max_u64(mine);
     const int bi = (int)~(uint32_t)key;
     const uint32_t ok = (uint32_t)(key >> 32);
     const float best = __uint_as_float((ok & 0x80000000u) ? (ok & 0x7FFFFFFFu) : ~ok);
-    if ((bi & 63) == lane) taken |= 1u << (bi >> 6);
+    if ((bi & 63) == lane) {
+      taken |= 1u << (bi >> 6);
+      mine = lane_best();
+    }
     if (j == 0) m = best;
     const float w = expf(best - m);
     sum += w;
@@ -453,8 +463,12 @@ hipError_t launch_route(const float* logits, int T, int E, int k, int32_t* ids, 
                         int32_t* err, hipStream_t s) {
   TimedLaunch timed_(kLRoute, s);
   if (T == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_route, dim3((T + 3) / 4), dim3(256), 0, s, logits, T, E, k, ids, gates,
-                     err);
+  const dim3 grid((T + 3) / 4);
+  if (E <= 64) hipLaunchKernelGGL(k_route<1>, grid, dim3(256), 0, s, logits, T, E, k, ids, gates, err);
+  else if (E <= 128) hipLaunchKernelGGL(k_route<2>, grid, dim3(256), 0, s, logits, T, E, k, ids, gates, err);
+  else if (E <= 256) hipLaunchKernelGGL(k_route<4>, grid, dim3(256), 0, s, logits, T, E, k, ids, gates, err);
+  else if (E <= 512) hipLaunchKernelGGL(k_route<8>, grid, dim3(256), 0, s, logits, T, E, k, ids, gates, err);
+  else hipLaunchKernelGGL(k_route<16>, grid, dim3(256), 0, s, logits, T, E, k, ids, gates, err);
   return hipGetLastError();
 }
 
