@@ -53,18 +53,23 @@ def kernel_hash(kernel: str) -> str:
 
 
 def measured_traffic(kernel: str, workload: str):
-    """HBM bytes per launch of `kernel` on `workload` from the committed
-    counter summary (FETCH_SIZE and WRITE_SIZE scaled by a copy kernel), if it
-    was taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_counters.json")
+    """(HBM bytes per launch, where the figure comes from) for `kernel` on
+    `workload`: the committed counter summary (FETCH_SIZE and WRITE_SIZE of a
+    separate rocprofv3 run, scaled by a copy kernel of known size) if it was
+    taken on the current kernel source; else (None, why not)."""
+    rel = os.path.join("profiles", f"{kernel}_{workload}_counters.json")
     try:
-        with open(path) as f:
+        with open(os.path.join(ROOT, rel)) as f:
             c = json.load(f)
     except (OSError, ValueError):
-        return None
-    if c.get("kernel_hash") != kernel_hash(kernel):
-        return None
-    return c.get("hbm_bytes_per_launch")
+        return None, f"no counter summary {rel}"
+    h = kernel_hash(kernel)
+    if c.get("kernel_hash") != h:
+        return None, f"{rel} was taken on another kernel source (hash {c.get('kernel_hash')})"
+    return c.get("hbm_bytes_per_launch"), (
+        f"{rel}: rocprofv3 FETCH_SIZE x {c.get('fetch_scale', 0):.3f} + WRITE_SIZE x "
+        f"{c.get('write_scale', 0):.3f} per launch, counters of a separate profiled run on "
+        f"this kernel source (hash {h})")
 
 
 # ------------------------------------------------------------------ timing
@@ -129,7 +134,9 @@ def nth(kind, n):
 
 def roofline(alg_flops, alg_bytes, kernel_ms, traffic, kernel_name):
     """Roofline object of a kernel: bound by whichever of the MFMA and HBM
-    times at the published peaks is larger."""
+    times at the published peaks is larger.  `traffic` is None or
+    (bytes or None, source) from measured_traffic."""
+    traffic, traffic_src = traffic if isinstance(traffic, tuple) else (traffic, None)
     from quantized_grouped_gemm_amd import accounting as acc
     t_mfma = alg_flops / (acc.BF16_DENSE_PEAK_TFLOPS * 1e12)
     t_hbm = alg_bytes / (acc.HBM_PEAK_GBPS * 1e9)
@@ -140,7 +147,8 @@ def roofline(alg_flops, alg_bytes, kernel_ms, traffic, kernel_name):
         bound, achieved, peak, unit = ("mfma", alg_flops / s / 1e12, acc.BF16_DENSE_PEAK_TFLOPS,
                                        "TFLOP/s")
     return {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
-            "frac": round(achieved / peak, 4), "traffic": traffic, "kernel": kernel_name,
+            "frac": round(achieved / peak, 4), "traffic": traffic,
+            **({"traffic_source": traffic_src} if traffic_src else {}), "kernel": kernel_name,
             "kernel_ms": round(kernel_ms, 4), "alg_flops": alg_flops, "alg_bytes": alg_bytes,
             "mfma_frac": round(alg_flops / s / 1e12 / acc.BF16_DENSE_PEAK_TFLOPS, 4),
             "hbm_frac": round(alg_bytes / s / 1e9 / acc.HBM_PEAK_GBPS, 4)}
