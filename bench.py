@@ -16,7 +16,10 @@ peak dequant scratch, the scratch checked against the caching allocator).
 
 Per-kernel durations come from HIP events the library records around each of
 its kernel launches on the call's stream (qgg_set_timing_events), over the
-same number of steps as the timed region.
+same number of steps as the timed region; each roofline takes the mean launch
+duration and also reports the median and the minimum.  No cache flush runs
+between steps: every workload's per-step stream of packed weights (1.1-6.7 GB)
+exceeds the 256 MB MALL four times over or more.
 
 Prints ONE JSON line.
 """
@@ -125,6 +128,12 @@ def launch_means(per_step, pick):
     return float(np.mean([s[pick(s)][1] for s in per_step]))
 
 
+def launch_spread(per_step, pick):
+    """(median, min) duration (ms) of the same launches."""
+    v = [s[pick(s)][1] for s in per_step]
+    return float(np.median(v)), float(np.min(v))
+
+
 def nth(kind, n):
     def pick(s):
         idx = [i for i, (k, _) in enumerate(s) if k == kind]
@@ -132,10 +141,11 @@ def nth(kind, n):
     return pick
 
 
-def roofline(alg_flops, alg_bytes, kernel_ms, traffic, kernel_name):
+def roofline(alg_flops, alg_bytes, kernel_ms, traffic, kernel_name, spread=None):
     """Roofline object of a kernel: bound by whichever of the MFMA and HBM
-    times at the published peaks is larger.  `traffic` is None or
-    (bytes or None, source) from measured_traffic."""
+    times at the published peaks is larger (achieved from the mean launch
+    duration `kernel_ms`; `spread` adds the median and minimum).  `traffic`
+    is None or (bytes or None, source) from measured_traffic."""
     traffic, traffic_src = traffic if isinstance(traffic, tuple) else (traffic, None)
     from quantized_grouped_gemm_amd import accounting as acc
     t_mfma = alg_flops / (acc.BF16_DENSE_PEAK_TFLOPS * 1e12)
@@ -149,7 +159,10 @@ def roofline(alg_flops, alg_bytes, kernel_ms, traffic, kernel_name):
     return {"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
             "frac": round(achieved / peak, 4), "traffic": traffic,
             **({"traffic_source": traffic_src} if traffic_src else {}), "kernel": kernel_name,
-            "kernel_ms": round(kernel_ms, 4), "alg_flops": alg_flops, "alg_bytes": alg_bytes,
+            "kernel_ms": round(kernel_ms, 4),
+            **({"kernel_ms_median": round(spread[0], 4), "kernel_ms_min": round(spread[1], 4)}
+               if spread else {}),
+            "alg_flops": alg_flops, "alg_bytes": alg_bytes,
             "mfma_frac": round(alg_flops / s / 1e12 / acc.BF16_DENSE_PEAK_TFLOPS, 4),
             "hbm_frac": round(alg_bytes / s / 1e9 / acc.HBM_PEAK_GBPS, 4)}
 
@@ -244,7 +257,7 @@ def run_ffn_fwd(cfg, args, cpu_budget=None):
     gu_bytes = w_gu + cfg.T * d * 2.0 + P * I * 2.0
     dom = "k_gemm_nt"
     rl = roofline(gu_flops, gu_bytes, gu_ms, measured_traffic(dom, cfg.name),
-                  "k_gemm_nt (gate_up, SwiGLU epilogue)")
+                  "k_gemm_nt (gate_up, SwiGLU epilogue)", launch_spread(per, nth("gemm", 0)))
     out = {
         "ms_per_step": round(ms, 4),
         "step_TFLOPs": round(F / (ms / 1e3) / 1e12, 3),
@@ -258,7 +271,7 @@ def run_ffn_fwd(cfg, args, cpu_budget=None):
     # down kernel roofline too (the step's second GEMM)
     dn_bytes = w_dn + P * I * 2.0 + P * d * 2.0
     out["roofline_down"] = roofline(2.0 * P * d * I, dn_bytes, dn_ms, None,
-                                    "k_gemm_nt (down)")
+                                    "k_gemm_nt (down)", launch_spread(per, nth("gemm", 1)))
 
     def ws_query(variant, chunk):
         return qgg.workspace_bytes(qgg.CALL_FFN_FWD, cfg.T, d, cfg.E, cfg.k, I, variant, chunk)
@@ -350,7 +363,8 @@ def run_proj(cfg, args):
            "gemm_ms": round(g_ms, 4), "weight_GBps": round(wbytes / (g_ms / 1e3) / 1e9, 1),
            "n_active": A,
            "roofline": roofline(F, alg, g_ms, measured_traffic("k_gemm_nt", cfg.name),
-                                "k_gemm_nt (INT4 gate_up projection)")}
+                                "k_gemm_nt (INT4 gate_up projection)",
+                                launch_spread(per, nth("gemm", 0)))}
     C = cfg.chunks[0]
     if args.sweep:
         cms = time_steps(lambda: call(qgg.CHUNKED, C), max(2, args.steps // 4), 1)
@@ -400,10 +414,12 @@ def run_bwd(cfg, args):
                        "combine_ms": round(launch_means(per, nth("combine", 0)), 4)},
            "roofline": roofline(2.0 * P * 2 * I * d, gu_bytes, gu_ms,
                                 measured_traffic("k_gemm_tn", cfg.name),
-                                "k_gemm_tn (dXp = dH . W_gate_up)"),
+                                "k_gemm_tn (dXp = dH . W_gate_up)",
+                                launch_spread(per, nth("gemm_t", 1))),
            "roofline_down": roofline(2.0 * P * d * I, w_dn + cfg.T * d * 2.0 + P * I * 2 * 2.0
                                      + P * 2 * I * 2.0, dn_ms, None,
-                                     "k_gemm_tn (dA = g dY . W_down, SwiGLU backward)")}
+                                     "k_gemm_tn (dA = g dY . W_down, SwiGLU backward)",
+                                     launch_spread(per, nth("gemm_t", 0)))}
 
     def ws_query(variant, chunk):
         return qgg.workspace_bytes(qgg.CALL_DX_BWD, cfg.T, d, cfg.E, cfg.k, I, variant, chunk)
