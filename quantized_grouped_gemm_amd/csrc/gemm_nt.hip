@@ -35,15 +35,16 @@ constexpr int kKL = 64;                  // K elements per stage (one K step)
 constexpr int kStageRowB = kKL * 2;      // A bytes per tile row per stage
 constexpr int kNBuf = 4;                 // stages in the LDS ring of A tiles
 // Wavefronts per workgroup (each owns 64 output columns of an item) and
-// workgroups per CU.  Tiles of 64 or 128 rows take 512-column items on eight
-// waves: every A stage copied into LDS then feeds twice the columns, which
-// halves the L2 -> LDS traffic of A.  Short tiles (decode-sized expert groups)
-// need fewer registers, and a third 4-wave workgroup keeps more weight loads
-// in flight.
+// workgroups per CU.  128-row tiles take 512-column items on eight waves:
+// every A stage copied into LDS then feeds twice the columns, which halves
+// the L2 -> LDS traffic of A.  Shorter tiles (decode-sized and mid-sized
+// expert groups) need fewer registers and take 256-column items on four
+// waves, three workgroups per CU for 32-row tiles and two for 64-row tiles,
+// which keeps more weight loads in flight.
 template <int MB>
-constexpr int nt_waves() { return MB == 1 ? 4 : 8; }
+constexpr int nt_waves() { return MB == 4 ? 8 : 4; }
 template <int MB>
-constexpr int nt_occupancy() { return MB == 1 ? 3 : 1; }
+constexpr int nt_occupancy() { return MB == 1 ? 3 : (MB == 2 ? 2 : 1); }
 // weight steps in flight per wavefront (BF16 steps are 4x larger)
 template <int SRC>
 constexpr int ring_depth() { return SRC == kSrcBF16 ? 2 : 4; }

@@ -47,7 +47,12 @@ struct Carver {
 
 // Rows per M-tile, from the mean rows per expert (P / E) rounded up to a
 // power-of-two number of 32-row MFMA blocks, at most 4.
-int choose_mb(int64_t P, int E) {
+// Tile height in 32-row blocks.  Top-k routing gives an expert at most one
+// row per token, so a batch of T <= 64 tokens fits every expert in one tile of
+// ceil(T / 32) blocks and each expert streams its weights once; larger batches
+// take the height from the mean rows per expert.
+int choose_mb(int64_t P, int E, int64_t T) {
+  if (T <= 64) return T <= 32 ? 1 : 2;
   const int64_t mean = E > 0 ? (P + E - 1) / E : P;
   const int64_t blocks = (mean + 31) / 32;
   if (blocks <= 1) return 1;
@@ -65,8 +70,8 @@ struct Plan {
   int64_t cap = 0;
 };
 
-void carve_plan(Carver& cv, int64_t P, int E, Plan& pl) {
-  pl.mb = choose_mb(P, E);
+void carve_plan(Carver& cv, int64_t P, int E, int64_t T, Plan& pl) {
+  pl.mb = choose_mb(P, E, T);
   pl.cap = tile_capacity(P, E, 32 * pl.mb);
   pl.tiles = cv.take<int4>(sizeof(int4) * pl.cap);
   // chunk bounds (E + 2 entries), then the GEMM launches' work counters (2)
@@ -233,14 +238,14 @@ size_t qgg_workspace_bytes(int call, int T, int d, int E, int k, int N_or_inter,
       cv.take<char>(permute_ws_bytes(P, E));
       break;
     case QGG_CALL_GEMM:
-      carve_plan(cv, P, E, pl);
+      carve_plan(cv, P, E, T, pl);
       if (variant == QGG_CHUNKED) scratch = (size_t)C * N_or_inter * d * 2;
       cv.take<char>(scratch);
       break;
     case QGG_CALL_FFN_FWD: {
       const int64_t I = N_or_inter;
       cv.take<char>(permute_ws_bytes(P, E));
-      carve_plan(cv, P, E, pl);
+      carve_plan(cv, P, E, T, pl);
       cv.take<char>((size_t)P * I * 2);
       cv.take<char>((size_t)P * d * 2);
       if (variant == QGG_CHUNKED) scratch = (size_t)C * 2 * I * d * 2;
@@ -248,14 +253,14 @@ size_t qgg_workspace_bytes(int call, int T, int d, int E, int k, int N_or_inter,
       break;
     }
     case QGG_CALL_LORA_BWD:   // d = N (dY width), N_or_inter = adapter rank
-      carve_plan(cv, P, E, pl);
+      carve_plan(cv, P, E, T, pl);
       cv.take<char>((size_t)P * N_or_inter * 4);
       cv.take<char>((size_t)E * N_or_inter * d * 2);
       break;
     case QGG_CALL_DX_BWD:
     case QGG_CALL_FFN_LORA_BWD: {
       const int64_t I = N_or_inter;
-      carve_plan(cv, P, E, pl);
+      carve_plan(cv, P, E, T, pl);
       cv.take<char>((size_t)P * 2 * I * 2);
       cv.take<char>((size_t)P * d * 2);
       if (variant == QGG_CHUNKED) scratch = (size_t)C * 2 * I * d * 2;
@@ -327,7 +332,7 @@ static qgg_status grouped_gemm(const qgg_qweight* w, const qgg_lora* lora, const
   const int C = chunk > 0 ? std::min(chunk, E) : (int)std::min<int64_t>(E, std::max<int64_t>(P, 1));
   Carver cv(workspace);
   Plan pl;
-  carve_plan(cv, P, E, pl);
+  carve_plan(cv, P, E, T, pl);
   uint16_t* sbuf = cv.take<uint16_t>(scratch);
 
   if (dq_only) {
@@ -415,7 +420,7 @@ qgg_status lora_grouped_gemm_bwd(const qgg_lora* lora, int E, int N, int K, cons
   if (!workspace || ws_bytes < need) return QGG_ERR_WORKSPACE_TOO_SMALL;
   Carver cv(workspace);
   Plan pl;
-  carve_plan(cv, P, E, pl);
+  carve_plan(cv, P, E, T, pl);
   float* du = cv.take<float>((size_t)P * lora->rank * 4);
   uint16_t* bt = cv.take<uint16_t>((size_t)E * lora->rank * N * 2);
   const PermPtrs pp = to_ptrs(p);
@@ -456,7 +461,7 @@ static qgg_status ffn_forward(const qgg_qweight* w_gate_up, const qgg_qweight* w
   Carver cv(workspace);
   void* pws = cv.take<char>(permute_ws_bytes(P, E));
   Plan pl;
-  carve_plan(cv, P, E, pl);
+  carve_plan(cv, P, E, T, pl);
   uint16_t* abuf = cv.take<uint16_t>((size_t)P * inter * 2);
   uint16_t* obuf = cv.take<uint16_t>((size_t)P * d * 2);
   uint16_t* sbuf = cv.take<uint16_t>(scratch);
@@ -644,7 +649,7 @@ static qgg_status backward(const qgg_qweight* w_gate_up, const qgg_qweight* w_do
   const int C = chunk > 0 ? std::min(chunk, E) : (int)std::min<int64_t>(E, std::max<int64_t>(P, 1));
   Carver cv(workspace);
   Plan pl;
-  carve_plan(cv, P, E, pl);
+  carve_plan(cv, P, E, T, pl);
   uint16_t* dh = cv.take<uint16_t>((size_t)P * 2 * inter * 2);
   uint16_t* dxp = cv.take<uint16_t>((size_t)P * d * 2);
   uint16_t* sbuf = cv.take<uint16_t>(scratch);
@@ -766,7 +771,7 @@ qgg_status moe_ffn_bwd_lora(const qgg_qweight* w_gate_up, const qgg_qweight* w_d
   const int C = chunk > 0 ? std::min(chunk, E) : (int)std::min<int64_t>(E, std::max<int64_t>(P, 1));
   Carver cv(workspace);
   Plan pl;
-  carve_plan(cv, P, E, pl);
+  carve_plan(cv, P, E, T, pl);
   uint16_t* dh = cv.take<uint16_t>((size_t)P * 2 * inter * 2);
   uint16_t* dxp = cv.take<uint16_t>((size_t)P * d * 2);
   uint16_t* sbuf = cv.take<uint16_t>(scratch);
