@@ -12,7 +12,7 @@
 //    columns); a persistent grid starts on items 0 .. grid - 1 and takes the
 //    rest in order from a counter, so the columns of one M-tile run side by
 //    side and a workgroup that drew small tiles takes more of them;
-//  - NW wavefronts per workgroup (8, or 4 for 32-row tiles), each owning 64
+//  - NW wavefronts per workgroup (8 for 128-row tiles, else 4), each owning 64
 //    output columns (two 32-column MFMA blocks) for all rows of the tile, so
 //    each weight element is loaded and decoded exactly once per tile;
 //  - weights go from HBM straight into MFMA B-operand registers: lane (c, h)
