@@ -182,6 +182,12 @@ PROJ_CASES = [
            name="int4_512col_ragged"),
     scaled(CONFIGS["tiny_mxfp4_proj"], T=600, d=128, E=2, k=1, N=64, chunks=(1,),
            name="mxfp4_n64_tall"),
+    # decode-sized batches (33..64 tokens): one 64-row tile per expert, with
+    # one and two live 32-row blocks, on four-wave workgroups
+    scaled(CONFIGS["tiny_mxfp4_proj"], T=64, d=256, E=3, k=2, N=320, chunks=(2,),
+           name="mxfp4_decode_tile64"),
+    scaled(CONFIGS["kimi_int4_gate_up"], T=48, d=256, E=5, k=3, N=256, chunks=(2,),
+           name="int4_decode_tile64"),
 ]
 
 
